@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the ResidualQuant KV path on one MI355X.
+
+A step is one pass of the whole hot path over a synthetic Ouro-1.4B-like
+cache (24 layers x 4 loops, 16 heads x 128, 8192 tokens, batch 4): for every
+loop and layer, fused decode attention of one query token per (batch row,
+head) over the packed INT4-anchor / INT2-residual cache, then the quantize-
+append of the new token's K/V for all loops and layers.  Inputs are resident
+in HBM before timing starts.
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--no-bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "decode_attention_int4_amd", "csrc", "rq_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_sha(path=DECODE_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(config: str):
+    """HBM bytes per dominant-kernel launch from committed rocprofv3 counter
+    runs, or None when missing or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"decode_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != src_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_steps(step, steps: int, torch):
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def dominant_kernel_ms(run, steps: int, torch):
+    """Average duration of the residual-loop decode-attention launch, bracketed
+    by events on the stream the kernel runs on, over `steps` full steps."""
+    stream = torch.cuda.current_stream()
+    w = run.w
+    P = w.loops_per_group
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        for loop in range(w.loops):
+            for layer in range(w.layers):
+                dominant = (w.mode == 0 and loop % P != P - 1)
+                if dominant:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    run.attend(loop, layer)
+                    b.record(stream)
+                    pairs.append((a, b))
+                else:
+                    run.attend(loop, layer)
+        run.append_new()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in pairs]
+    return sum(ms) / len(ms), len(ms)
+
+
+def read_peak_gbps(torch, rq, nbytes=8 << 30, reps=5):
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(7)
+    sink = torch.zeros(rq.read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    rq.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        rq.read_probe(buf, sink)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(run, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same step:
+    attention calls of sampled (batch row, layer, head) slices for every loop,
+    plus encoding of sampled new-token loop groups; extrapolated to one full
+    step (every loop x layer x batch row x head, and the whole append)."""
+    import numpy as np
+
+    import oracle as O
+    from decode_attention_int4_amd.synth import rotation_signs
+
+    w = run.w
+    cores = min(16, os.cpu_count() or 1)
+    p = O.Params(d=w.head_dim, P=w.loops_per_group, anchor_bits=w.anchor_bits,
+                 residual_bits=w.residual_bits, mode=w.mode, alpha_mode=w.alpha_mode,
+                 rotate=1 if (w.rotation == 1 and w.mode == 0) else 0)
+    signs = rotation_signs(w).numpy()
+
+    def bits(t):
+        return t.contiguous().cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+
+    encs = []
+    for key, kept in run.kept.items():
+        b, layer, head = key
+        HK = O.rotation_matrix(w.head_dim, signs[0, layer])
+        HV = O.rotation_matrix(w.head_dim, signs[1, layer])
+        encs.append((key, O.encode_slice(p, bits(kept[0]), HK), O.encode_slice(p, bits(kept[1]), HV),
+                     HK, HV))
+    jobs = [(e, loop) for e in encs for loop in range(w.loops)]
+
+    def attn(job):
+        (key, ek, ev, HK, HV), loop = job
+        b, layer, head = key
+        return O.attention_slice(p, ek, ev, HK, HV, bits(run.q[loop, layer, b, head]), loop,
+                                 run.N, w.softmax_scale)
+
+    n_calls = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        while time.perf_counter() - t0 < budget_s * 0.8:
+            list(ex.map(attn, jobs * max(1, cores // len(jobs))))
+            n_calls += len(jobs) * max(1, cores // len(jobs))
+    t_attn = time.perf_counter() - t0
+    calls_per_s = n_calls / t_attn
+
+    # append: encode new-token loop groups (one per kv, batch row, layer, head, group)
+    new = run.new_kv  # [2, B, loops, layers, H, 1, d]
+    groups = [(kv, b, layer, head, k) for kv in range(2) for b in range(w.batch)
+              for layer in range(w.layers) for head in range(w.kv_heads)
+              for k in range(w.loops // w.loops_per_group)]
+    rng = np.random.default_rng(0)
+    sample = [groups[i] for i in rng.choice(len(groups), size=min(256, len(groups)), replace=False)]
+    Hs = {}
+    t1 = time.perf_counter()
+    for kv, b, layer, head, k in sample:
+        if (kv, layer) not in Hs:
+            Hs[(kv, layer)] = O.rotation_matrix(w.head_dim, signs[kv, layer])
+        P = w.loops_per_group
+        x = O.bf16_decode(bits(new[kv, b, k * P:(k + 1) * P, layer, head, 0]))
+        O.encode_group(p, x, Hs[(kv, layer)])
+    t_enc = (time.perf_counter() - t1) / len(sample)
+
+    step_calls = w.loops * w.layers * w.batch * w.q_heads
+    step_s = step_calls / calls_per_s + t_enc * len(groups)
+    return {
+        "value": w.batch / step_s,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{n_calls} fp64 attention calls (n={run.N}) on {len(encs)} sampled "
+                   f"(batch,layer,head) slices x {w.loops} loops with {cores} threads "
+                   f"({calls_per_s:.1f} calls/s) + {len(sample)} new-token loop-group encodes "
+                   f"({t_enc * 1e3:.2f} ms each, 1 thread); extrapolated to {step_calls} calls "
+                   f"and {len(groups)} encodes per step = {step_s:.1f} s/step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="ouro8k_b4")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) pair is independent; see the design notes on sharding).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_int4_amd import rq
+    from decode_attention_int4_amd.synth import WORKLOADS
+    from decode_attention_int4_amd.workload import BF16Decode, RQDecode
+
+    w = WORKLOADS[args.config]
+    log(f"[bench] {w}")
+    t = time.perf_counter()
+    keep = [(0, 0, 0), (w.batch - 1, w.layers - 1, w.kv_heads - 1)]
+    run = RQDecode(w, keep=keep)
+    torch.cuda.synchronize()
+    log(f"[bench] packed cache {rq.cache_bytes(run.desc) / 1e9:.2f} GB filled in "
+        f"{time.perf_counter() - t:.1f} s")
+
+    for _ in range(args.warmup):
+        run.step()
+    ms, wall = time_steps(run.step, args.steps, torch)
+    tok_s = w.batch / (ms * 1e-3)
+    step_bytes = run.step_bytes()
+    log(f"[bench] {ms:.3f} ms/step, {tok_s:.1f} tokens/s, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+
+    dom_ms, n_launch = dominant_kernel_ms(run, args.steps, torch)
+    P = w.loops_per_group
+    dom_loop = 0 if w.mode == 0 else P - 1
+    dom_bytes = run.call_bytes(dom_loop)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    log(f"[bench] residual-loop attention: {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
+        f"{achieved:.0f} GB/s")
+
+    extra = {}
+    if not args.no_probe:
+        peak = read_peak_gbps(torch, rq)
+        extra["measured_read_peak_gbps"] = round(peak, 1)
+        extra["frac_of_measured_read_peak"] = round(achieved / peak, 4)
+        log(f"[bench] streaming-read probe: {peak:.0f} GB/s")
+
+    if not args.no_bf16:
+        base = BF16Decode(w)
+        for _ in range(args.warmup):
+            base.step()
+        bms, _ = time_steps(base.step, args.steps, torch)
+        extra["bf16_baseline"] = {
+            "ms_per_step": round(bms, 4), "tokens_per_s": round(w.batch / (bms * 1e-3), 2),
+            "hbm_gbps": round(base.step_bytes() / (bms * 1e-3) / 1e9, 1),
+            "speedup_of_residual": round(bms / ms, 3)}
+        log(f"[bench] bf16 baseline: {bms:.3f} ms/step, {w.batch / (bms * 1e-3):.1f} tokens/s")
+        del base
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(run)
+        log(f"[bench] oracle: {cpu['value']:.4f} tokens/s ({cpu['sample']})")
+
+    traffic = traffic_from_profile(args.config)
+    line = {
+        "metric": "decode-attn tokens/s + achieved HBM GB/s on INT4/INT2 residual KV, 8k/16k",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "loops": w.loops, "layers": w.layers,
+                   "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
+                   "context_tokens": w.n_tokens, "anchor_bits": w.anchor_bits,
+                   "residual_bits": w.residual_bits, "group": 16,
+                   "mode": "residual" if w.mode == 0 else "direct"},
+        "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel<128,4,2> (residual loop)",
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

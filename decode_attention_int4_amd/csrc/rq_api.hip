@@ -1,0 +1,277 @@
+// rq_api.hip -- host side of the C ABI declared in include/rq.h: argument
+// validation, cache geometry, split-K planning and kernel launches.  No
+// allocation, no synchronization.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/rq.h"
+#include "rq_kernels.h"
+#include "rq_layout.h"
+
+namespace rq {
+int decode_tile_tokens(int d);
+int bf16_tile_tokens();
+
+// Split-K planning.  The decode kernels run 4 waves per workgroup; a launch
+// needs well over 256 workgroups to occupy the 256 CUs, so small batch*heads
+// products are split along the tokens.  Splits never shrink below two tiles.
+// The result is non-decreasing in n_tokens, so a workspace sized for n serves
+// any smaller n.
+static constexpr int32_t kTargetBlocks = 1024;
+
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile) {
+  SplitPlan p{1, tile};
+  if (n_tokens <= 0 || bh <= 0) return p;
+  const int32_t n_tiles = (n_tokens + tile - 1) / tile;
+  int32_t splits = (kTargetBlocks + bh - 1) / bh;
+  const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+  if (splits > max_splits) splits = max_splits;
+  const int32_t tiles_per = (n_tiles + splits - 1) / splits;
+  p.tokens_per_split = tiles_per * tile;
+  p.splits = (n_tokens + p.tokens_per_split - 1) / p.tokens_per_split;
+  return p;
+}
+
+static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile) {
+  if (n_tokens <= 0 || bh <= 0) return 1;
+  const int32_t n_tiles = (n_tokens + tile - 1) / tile;
+  int32_t splits = (kTargetBlocks + bh - 1) / bh;
+  const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+  return splits < max_splits ? splits : max_splits;
+}
+
+}  // namespace rq
+
+using rq::Geometry;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rq_status check_desc(const rq_cache_desc* d) {
+  if (!d) return RQ_ERR_INVALID_ARG;
+  if (d->batch <= 0 || d->loops <= 0 || d->layers <= 0 || d->kv_heads <= 0 || d->max_tokens <= 0 ||
+      d->head_dim <= 0 || d->loops_per_group <= 0 || d->group_size <= 0)
+    return RQ_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128) return RQ_ERR_UNSUPPORTED;
+  if (d->group_size != 16) return RQ_ERR_UNSUPPORTED;
+  if (d->loops % d->loops_per_group != 0 || d->loops > 64) return RQ_ERR_UNSUPPORTED;
+  if ((d->anchor_bits != 2 && d->anchor_bits != 4) || (d->residual_bits != 2 && d->residual_bits != 4))
+    return RQ_ERR_UNSUPPORTED;
+  if (d->mode != RQ_MODE_RESIDUAL && d->mode != RQ_MODE_DIRECT) return RQ_ERR_UNSUPPORTED;
+  if (d->alpha_mode != RQ_ALPHA_LS && d->alpha_mode != RQ_ALPHA_NORM_RATIO && d->alpha_mode != RQ_ALPHA_ONE)
+    return RQ_ERR_UNSUPPORTED;
+  if (d->rotation != RQ_ROT_NONE && d->rotation != RQ_ROT_HADAMARD) return RQ_ERR_UNSUPPORTED;
+  // every 64-bit offset must stay far from overflow
+  const double total = 2.0 * d->batch * d->loops * (double)d->layers * d->kv_heads *
+                       (double)d->max_tokens * (d->head_dim * 0.5 + 2 * d->head_dim / 16.0 + 2.0);
+  if (total > 9.0e18) return RQ_ERR_UNSUPPORTED;
+  return RQ_OK;
+}
+
+bool needs_signs(const rq_cache_desc* d) {
+  return d->mode == RQ_MODE_RESIDUAL && d->rotation == RQ_ROT_HADAMARD;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rq_status_string(rq_status s) {
+  switch (s) {
+    case RQ_OK: return "ok";
+    case RQ_ERR_INVALID_ARG: return "invalid argument";
+    case RQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RQ_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case RQ_ERR_WORKSPACE: return "workspace too small";
+    case RQ_ERR_ALIGNMENT: return "misaligned device pointer";
+    case RQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+rq_status rq_validate_desc(const rq_cache_desc* desc) { return check_desc(desc); }
+
+rq_status rq_cache_bytes(const rq_cache_desc* desc, uint64_t* total_bytes) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (!total_bytes) return RQ_ERR_INVALID_ARG;
+  *total_bytes = rq::make_geometry(*desc).total;
+  return RQ_OK;
+}
+
+rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, int32_t layer,
+                        int32_t loop, int32_t kv_head, rq_slot* out) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (!out || kv < 0 || kv > 1 || batch < 0 || batch >= desc->batch || layer < 0 ||
+      layer >= desc->layers || loop < 0 || loop >= desc->loops || kv_head < 0 ||
+      kv_head >= desc->kv_heads)
+    return RQ_ERR_INVALID_ARG;
+  const Geometry g = rq::make_geometry(*desc);
+  const uint64_t off = g.slot_offset(kv, batch, layer, loop, kv_head);
+  out->codes_offset = off;
+  out->sz_offset = off + g.sz_rel(loop);
+  out->alpha_offset = g.has_alpha(loop) ? off + g.alpha_rel(loop) : UINT64_MAX;
+  out->slot_bytes = g.slot_bytes[g.is_anchor(loop) ? 0 : 1];
+  out->bits = g.bits_of(loop);
+  out->code_bytes = desc->head_dim * out->bits / 8;
+  return RQ_OK;
+}
+
+rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
+                             int32_t n_tokens, int32_t t_new, const int8_t* signs, void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (n_tokens < 0 || t_new < 0) return RQ_ERR_INVALID_ARG;
+  if ((int64_t)n_tokens + t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
+  if (t_new == 0) return RQ_OK;
+  if (!cache || !kv_bf16 || (needs_signs(desc) && !signs)) return RQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 256) || !aligned(kv_bf16, 4)) return RQ_ERR_ALIGNMENT;
+  rq::QuantArgs a{};
+  a.g = rq::make_geometry(*desc);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.kv = kv_bf16;
+  a.signs = signs;
+  a.n_tokens = n_tokens;
+  a.t_new = t_new;
+  a.items = 2ull * desc->batch * desc->layers * desc->kv_heads *
+            (uint64_t)(desc->loops / desc->loops_per_group) * (uint64_t)t_new;
+  return rq::launch_quant_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK
+                                                                                      : RQ_ERR_LAUNCH;
+}
+
+rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
+                         int32_t tok_begin, int32_t tok_end, int32_t out_dtype, void* out,
+                         void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (tok_begin < 0 || tok_end < tok_begin) return RQ_ERR_INVALID_ARG;
+  if (tok_end > desc->max_tokens) return RQ_ERR_CAPACITY;
+  if (out_dtype != RQ_OUT_F32 && out_dtype != RQ_OUT_BF16) return RQ_ERR_INVALID_ARG;
+  if (tok_end == tok_begin) return RQ_OK;
+  if (!cache || !out || (needs_signs(desc) && !signs)) return RQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 256) || !aligned(out, 4)) return RQ_ERR_ALIGNMENT;
+  rq::ReconArgs a{};
+  a.g = rq::make_geometry(*desc);
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.signs = signs;
+  a.tok_begin = tok_begin;
+  a.n_out = tok_end - tok_begin;
+  a.out_bf16 = out_dtype == RQ_OUT_BF16;
+  a.out = out;
+  a.vectors = 2ull * desc->batch * desc->loops * desc->layers * desc->kv_heads * (uint64_t)a.n_out;
+  return rq::launch_reconstruct(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK
+                                                                                    : RQ_ERR_LAUNCH;
+}
+
+uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
+  if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
+  const int32_t bh = desc->batch * q_heads;
+  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim));
+  return rq::align_up(4ull * bh, 256) + (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull;
+}
+
+rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
+                              int32_t loop, int32_t layer, const uint16_t* q_bf16, int32_t q_heads,
+                              int32_t n_tokens, float softmax_scale, void* workspace,
+                              uint64_t workspace_bytes, float* out, void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (loop < 0 || loop >= desc->loops || layer < 0 || layer >= desc->layers || q_heads <= 0 ||
+      n_tokens < 0)
+    return RQ_ERR_INVALID_ARG;
+  if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
+  if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
+  if (!cache || !q_bf16 || !workspace || !out || (needs_signs(desc) && !signs))
+    return RQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q_bf16, 4) || !aligned(out, 4))
+    return RQ_ERR_ALIGNMENT;
+  if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
+  if (workspace_bytes < rq_decode_workspace_bytes(desc, q_heads, n_tokens)) return RQ_ERR_WORKSPACE;
+  const int32_t bh = desc->batch * q_heads;
+  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim));
+  rq::DecodeArgs a{};
+  a.g = rq::make_geometry(*desc);
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.signs = signs;
+  a.q = q_bf16;
+  a.out = out;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rq::align_up(4ull * bh, 256));
+  a.loop = loop;
+  a.layer = layer;
+  a.q_heads = q_heads;
+  a.group_ratio = q_heads / desc->kv_heads;
+  a.n_tokens = n_tokens;
+  a.splits = plan.splits;
+  a.tokens_per_split = plan.tokens_per_split;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  return rq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
+}
+
+uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
+                                        int32_t max_n_tokens) {
+  if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
+  const int32_t bh = desc->batch * q_heads;
+  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::bf16_tile_tokens());
+  return rq::align_up(4ull * bh, 256) + (uint64_t)bh * s * (2 + desc->head_dim) * 4ull;
+}
+
+rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, int32_t loop, int32_t layer,
+                                   const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                                   float softmax_scale, void* workspace, uint64_t workspace_bytes,
+                                   float* out, void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (loop < 0 || loop >= desc->loops || layer < 0 || layer >= desc->layers || q_heads <= 0 ||
+      n_tokens < 0)
+    return RQ_ERR_INVALID_ARG;
+  if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
+  if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
+  if (!k_cache || !v_cache || !q_bf16 || !workspace || !out) return RQ_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 256) ||
+      !aligned(q_bf16, 4) || !aligned(out, 4))
+    return RQ_ERR_ALIGNMENT;
+  if (workspace_bytes < rq_bf16_decode_workspace_bytes(desc, q_heads, n_tokens)) return RQ_ERR_WORKSPACE;
+  const int32_t bh = desc->batch * q_heads;
+  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens());
+  rq::Bf16DecodeArgs a{};
+  a.batch = desc->batch;
+  a.loops = desc->loops;
+  a.layers = desc->layers;
+  a.kv_heads = desc->kv_heads;
+  a.max_tokens = desc->max_tokens;
+  a.d = desc->head_dim;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.q = q_bf16;
+  a.out = out;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rq::align_up(4ull * bh, 256));
+  a.loop = loop;
+  a.layer = layer;
+  a.q_heads = q_heads;
+  a.group_ratio = q_heads / desc->kv_heads;
+  a.n_tokens = n_tokens;
+  a.splits = plan.splits;
+  a.tokens_per_split = plan.tokens_per_split;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  return rq::launch_bf16_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK
+                                                                                   : RQ_ERR_LAUNCH;
+}
+
+uint32_t rq_read_probe_sink_words(void) { return rq::kProbeBlocks; }
+
+rq_status rq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16) return RQ_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return RQ_ERR_ALIGNMENT;
+  return rq::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? RQ_OK
+             : RQ_ERR_LAUNCH;
+}
+
+}  // extern "C"

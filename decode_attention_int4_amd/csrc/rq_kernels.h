@@ -1,0 +1,71 @@
+// rq_kernels.h -- argument blocks and launchers of the library's kernels
+// (internal; the public interface is include/rq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq_layout.h"
+
+namespace rq {
+
+struct QuantArgs {
+  Geometry g;
+  uint8_t* cache;
+  const uint16_t* kv;     // [2][B][L][layers][H][t_new][d] BF16
+  const int8_t* signs;    // [2][layers][d]
+  int32_t n_tokens, t_new;
+  uint64_t items;         // 2*B*layers*H*(L/P)*t_new
+};
+hipError_t launch_quant_append(const QuantArgs& a, hipStream_t s);
+
+struct ReconArgs {
+  Geometry g;
+  const uint8_t* cache;
+  const int8_t* signs;
+  int32_t tok_begin, n_out;
+  int32_t out_bf16;
+  void* out;              // [2][B][L][layers][H][n_out][d]
+  uint64_t vectors;       // 2*B*L*layers*H*n_out
+};
+hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
+
+// Split-K decode: partial states live in the workspace after the counters.
+struct DecodeArgs {
+  Geometry g;
+  const uint8_t* cache;
+  const int8_t* signs;
+  const uint16_t* q;      // [B][Hq][d]
+  float* out;             // [B][Hq][d]
+  uint32_t* counters;     // [B*Hq]
+  float* partials;        // [B*Hq][splits][2 + 2d]
+  int32_t loop, layer, q_heads, group_ratio, n_tokens;
+  int32_t splits, tokens_per_split;
+  float qscale;           // softmax scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct Bf16DecodeArgs {
+  int32_t batch, loops, layers, kv_heads, max_tokens, d;
+  const uint16_t* k;      // [B][L][layers][H][max_tokens][d]
+  const uint16_t* v;
+  const uint16_t* q;
+  float* out;
+  uint32_t* counters;
+  float* partials;        // [B*Hq][splits][2 + d]
+  int32_t loop, layer, q_heads, group_ratio, n_tokens;
+  int32_t splits, tokens_per_split;
+  float qscale;
+};
+hipError_t launch_bf16_decode(const Bf16DecodeArgs& a, hipStream_t s);
+
+constexpr uint32_t kProbeBlocks = 2048;
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
+
+// Split-K partition shared by workspace sizing and the launch.
+struct SplitPlan {
+  int32_t splits;
+  int32_t tokens_per_split;
+};
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile_tokens);
+
+}  // namespace rq

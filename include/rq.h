@@ -1,0 +1,215 @@
+/*
+ * rq.h -- C ABI of librq, an MI355X (gfx950) implementation of the
+ * ResidualQuant KV cache for looped Transformers: per-loop-group
+ * quantize-and-append, reconstruction, and fused decode attention that reads
+ * the packed cache directly.
+ *
+ * The method (web pages about "ResidualQuant: KV Cache Quantization for Looped
+ * Transformers with 2-Bit Residuals"; arXiv abstract, ai4snews summary
+ * paragraphs 1-4, agihunt "Confirmed" list):
+ *   - each loop of a looped Transformer keeps its own K/V per layer, so the KV
+ *     cache grows with the loop count (abstract);
+ *   - within a loop group, the final loop's state is the anchor, stored at
+ *     INT4; every other loop stores only its INT2 residual against the
+ *     dequantized anchor (ai4snews para. 1; agihunt);
+ *   - the residual is rotated by a fixed orthogonal matrix before
+ *     quantization (the anchor is not rotated) and carries a BF16
+ *     least-squares scale alpha; every group of 16 head_dim values has an FP8
+ *     scale and offset (ai4snews paras. 1-2);
+ *   - any loop is reconstructed from two reads, the anchor and its own
+ *     residual (ai4snews para. 3).
+ * The rotation is a randomized Walsh-Hadamard transform
+ * H = (1/sqrt(d)) WHT_d diag(signs) (d = 96: block diagonal 64 + 32).
+ *
+ * Conventions for every call:
+ *   - All buffers except `desc` and `out` structs are DEVICE pointers owned by
+ *     the caller.  The library never allocates, frees or synchronizes; work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns before it completes.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-RQ_OK status means nothing was enqueued, except RQ_ERR_LAUNCH, which
+ *     reports a failed kernel launch (later kernels of the same call are not
+ *     enqueued).  Statuses are never thrown across the ABI.
+ *   - The library is stateless: the caller tracks how many tokens are cached.
+ *
+ * Cache descriptor and supported values:
+ *   head_dim 64, 96 or 128; group_size 16; loops % loops_per_group == 0;
+ *   anchor_bits and residual_bits each 2 or 4; mode RESIDUAL or DIRECT;
+ *   alpha_mode LS, NORM_RATIO or ONE; rotation HADAMARD or NONE;
+ *   1 <= batch, layers, kv_heads; 1 <= loops <= 64; 1 <= max_tokens.
+ *
+ * Byte layout of a cache buffer (little endian).  A "slot" holds one
+ * (kv, batch row, layer, loop, kv head) stream of max_tokens tokens, where
+ * kv = 0 is K and kv = 1 is V.  Slot order, outermost first:
+ *     kv, batch, layer, loop, kv_head
+ * Loop j of loop group k (j = loop % P, P = loops_per_group) is the group's
+ * anchor when j == P-1.  Its bit width is anchor_bits for the anchor and
+ * residual_bits otherwise (direct mode: the anchor-position loop is stored at
+ * anchor_bits, the others at residual_bits, all as plain quantized states).
+ * A slot is three sub-planes, each starting on a 256-byte boundary:
+ *     codes [max_tokens][d*bits/8]  element i of a token is in byte i*bits/8,
+ *                                   at bit (i*bits) % 8 (low bits first)
+ *     sz    [max_tokens][2*d/16]    byte 2g = FP8 e4m3fn scale of group g,
+ *                                   byte 2g+1 = FP8 e4m3fn offset of group g
+ *     alpha [max_tokens] uint16     BF16 coefficient (residual loops of
+ *                                   RESIDUAL mode only; absent otherwise)
+ * A dequantized group value is scale * code + offset.  Slot sizes and
+ * offsets are given by rq_cache_slot(); the total by rq_cache_bytes().
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RQ_OK = 0,
+  RQ_ERR_INVALID_ARG = 1, /* null pointer, bad index or negative size */
+  RQ_ERR_UNSUPPORTED = 2, /* well-formed descriptor outside the supported set */
+  RQ_ERR_CAPACITY = 3,    /* token range exceeds max_tokens */
+  RQ_ERR_WORKSPACE = 4,   /* workspace smaller than rq_*_workspace_bytes() */
+  RQ_ERR_ALIGNMENT = 5,   /* a device pointer is not aligned as required */
+  RQ_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch */
+} rq_status;
+
+enum { RQ_MODE_RESIDUAL = 0, RQ_MODE_DIRECT = 1 };
+enum { RQ_ALPHA_LS = 0, RQ_ALPHA_NORM_RATIO = 1, RQ_ALPHA_ONE = 2 };
+enum { RQ_ROT_NONE = 0, RQ_ROT_HADAMARD = 1 };
+enum { RQ_OUT_F32 = 0, RQ_OUT_BF16 = 1 };
+
+typedef struct rq_cache_desc {
+  int32_t batch;
+  int32_t loops;           /* total loops L */
+  int32_t layers;
+  int32_t kv_heads;
+  int32_t max_tokens;      /* capacity per slot */
+  int32_t head_dim;        /* d */
+  int32_t loops_per_group; /* P; the anchor is loop P-1 of each group */
+  int32_t anchor_bits;
+  int32_t residual_bits;
+  int32_t group_size;      /* must be 16 */
+  int32_t mode;            /* RQ_MODE_* */
+  int32_t alpha_mode;      /* RQ_ALPHA_* (RESIDUAL mode) */
+  int32_t rotation;        /* RQ_ROT_* (RESIDUAL mode) */
+} rq_cache_desc;
+
+typedef struct rq_slot {
+  uint64_t codes_offset; /* bytes from the start of the cache buffer */
+  uint64_t sz_offset;
+  uint64_t alpha_offset; /* UINT64_MAX when the slot has no alpha plane */
+  uint64_t slot_bytes;   /* bytes from codes_offset to the next slot */
+  int32_t bits;          /* code width of this slot */
+  int32_t code_bytes;    /* bytes per token in the codes sub-plane */
+} rq_slot;
+
+/* Human-readable name of a status; never NULL. */
+const char* rq_status_string(rq_status s);
+
+/* Checks a descriptor against the supported set (host only). */
+rq_status rq_validate_desc(const rq_cache_desc* desc);
+
+/* Total size in bytes of a cache buffer for `desc` (host only).  The buffer
+ * must be 256-byte aligned. */
+rq_status rq_cache_bytes(const rq_cache_desc* desc, uint64_t* total_bytes);
+
+/* Location of one slot inside the cache buffer (host only). */
+rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, int32_t layer,
+                        int32_t loop, int32_t kv_head, rq_slot* out);
+
+/*
+ * Quantize-and-append (ai4snews paras. 1-2; agihunt "Confirmed").  For every
+ * (kv, batch row, layer, kv head, token, loop group), quantizes the anchor
+ * loop (group 16, asymmetric, FP8 e4m3fn scale = fp8((max-min)/Q), offset =
+ * fp8(min), codes rounded to nearest-even against the stored FP8 values and
+ * clamped to [0, Q]), then for each other loop forms r = x - deq(anchor),
+ * y = H r (signs of (kv, layer)), quantizes y at residual_bits and stores
+ * alpha = bf16(<y,yhat>/<yhat,yhat>) (0 when yhat = 0).  All arithmetic that
+ * decides a stored value is done in IEEE double precision.
+ *   cache    device, rq_cache_bytes() bytes, 256-byte aligned; written at
+ *            token positions [n_tokens, n_tokens + t_new) of every slot.
+ *   kv_bf16  device BF16 [2][batch][loops][layers][kv_heads][t_new][d],
+ *            contiguous, 4-byte aligned.
+ *   signs    device int8 [2][layers][d] of +-1 (may be NULL when rotation is
+ *            NONE or mode is DIRECT).
+ * Errors: RQ_ERR_CAPACITY when n_tokens + t_new > max_tokens; t_new == 0 is a
+ * no-op returning RQ_OK.
+ */
+rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
+                             int32_t n_tokens, int32_t t_new, const int8_t* signs,
+                             void* stream);
+
+/*
+ * Reconstruction from two reads (ai4snews para. 3): xhat = deq(anchor) +
+ * alpha * H^T deq(residual) for residual loops, deq(anchor) for the anchor,
+ * deq(own codes) in DIRECT mode.  Computed in fp32.
+ *   out  device [2][batch][loops][layers][kv_heads][tok_end - tok_begin][d],
+ *        fp32 (out_dtype RQ_OUT_F32) or BF16 round-to-nearest-even
+ *        (RQ_OUT_BF16).
+ */
+rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
+                         int32_t tok_begin, int32_t tok_end, int32_t out_dtype, void* out,
+                         void* stream);
+
+/* Bytes of workspace rq_decode_attention needs for `q_heads` query heads and
+ * any n_tokens <= max_n_tokens. */
+uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
+                                   int32_t max_n_tokens);
+
+/*
+ * Fused decode attention over the packed cache (abstract: reduced KV memory
+ * traffic; ai4snews para. 4: reconstruction must not offset the saved
+ * traffic).  One query token per (batch row, query head) attends to tokens
+ * [0, n_tokens) of loop `loop`, layer `layer`:
+ *     out = softmax_t(scale * q . xhat^K_t) . xhat^V_t
+ * computed without materializing xhat: q . deq(anchor) + alpha (H q) .
+ * deq(residual) per token, and H^T applied once to the accumulated residual-V
+ * term.  Query head h reads kv head h / (q_heads / kv_heads).
+ *   q_bf16     device BF16 [batch][q_heads][d], contiguous, 4-byte aligned
+ *   workspace  device, >= rq_decode_workspace_bytes(desc, q_heads, n_tokens),
+ *              256-byte aligned.  Its first 4*batch*q_heads bytes are
+ *              counters that must be ZERO before the first call (e.g. a
+ *              zero-filled allocation); every completed call leaves them zero.
+ *              Calls that share a workspace must not run concurrently.
+ *   out        device fp32 [batch][q_heads][d]; n_tokens == 0 writes zeros.
+ * Errors: RQ_ERR_UNSUPPORTED when q_heads is not a multiple of kv_heads;
+ * RQ_ERR_CAPACITY when n_tokens > max_tokens; RQ_ERR_WORKSPACE.
+ */
+rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache,
+                              const int8_t* signs, int32_t loop, int32_t layer,
+                              const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                              float softmax_scale, void* workspace, uint64_t workspace_bytes,
+                              float* out, void* stream);
+
+/*
+ * Baseline: split-K flash decode over an uncompressed BF16 cache of the same
+ * logical shape (the comparison the pages make against BF16 attention,
+ * ai4snews para. 4).  k_cache and v_cache are device BF16
+ * [batch][loops][layers][kv_heads][max_tokens][d]; everything else as in
+ * rq_decode_attention (same workspace rules, sized by
+ * rq_bf16_decode_workspace_bytes).
+ */
+uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
+                                        int32_t max_n_tokens);
+rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, int32_t loop, int32_t layer,
+                                   const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                                   float softmax_scale, void* workspace,
+                                   uint64_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Streaming-read probe: reads `bytes` bytes (a multiple of 16, 16-byte
+ * aligned) once with 16-byte loads and writes an XOR of all of them per
+ * workgroup into `sink` (device, rq_read_probe_sink_words() uint32 words).
+ * Used to measure attainable HBM read bandwidth.
+ */
+uint32_t rq_read_probe_sink_words(void);
+rq_status rq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RQ_H */

@@ -1,0 +1,87 @@
+"""Shared pieces of the GPU parity tests: oracle runs on kept BF16 slices,
+plane comparison through the documented layout, and the error metrics."""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from decode_attention_int4_amd.synth import Workload, rotation_signs
+from tests.layout_decode import Geom, decode_slice
+
+# Attention outputs must be within 1e-3 relative L2 and 2e-3 max-abs of the
+# fp64 oracle computed on the same BF16 inputs.
+REL_L2 = 1e-3
+MAX_ABS = 2e-3
+
+POOL = cf.ThreadPoolExecutor(max_workers=8)   # ctypes calls release the GIL
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def params(w: Workload) -> O.Params:
+    return O.Params(d=w.head_dim, g=16, P=w.loops_per_group, anchor_bits=w.anchor_bits,
+                    residual_bits=w.residual_bits, mode=w.mode, alpha_mode=w.alpha_mode,
+                    rotate=1 if (w.rotation == 1 and w.mode == 0) else 0)
+
+
+def rotations(w: Workload, layer: int):
+    s = rotation_signs(w).numpy()
+    return (O.rotation_matrix(w.head_dim, s[0, layer]), O.rotation_matrix(w.head_dim, s[1, layer]))
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def encode_kept(w: Workload, kept: torch.Tensor, layer: int):
+    """kept: BF16 [2, loops, N, d] -> (enc K, enc V, HK, HV) from the oracle."""
+    p = params(w)
+    HK, HV = rotations(w, layer)
+    fk = POOL.submit(O.encode_slice, p, bits16(kept[0]), HK)
+    fv = POOL.submit(O.encode_slice, p, bits16(kept[1]), HV)
+    return fk.result(), fv.result(), HK, HV
+
+
+def assert_planes_equal(gpu: "Planes", enc: O.Encoded, what: str, loops=None):
+    loops = range(enc.codes.shape[0]) if loops is None else loops
+    for l in loops:
+        for name in ("codes", "s8", "z8", "alpha"):
+            a, b = getattr(gpu, name)[l], getattr(enc, name)[l]
+            if not np.array_equal(a, b):
+                bad = np.argwhere(a != b)
+                raise AssertionError(f"{what} loop {l} {name}: {len(bad)} mismatches, first at "
+                                     f"{bad[0].tolist()}: gpu {a[tuple(bad[0])]} oracle "
+                                     f"{b[tuple(bad[0])]}")
+
+
+def check_slice_planes(w, run, key, t0=0, n=None):
+    b, layer, head = key
+    geom = Geom.of(run.desc)
+    n = run.N if n is None else n
+    ek, ev, HK, HV = encode_kept(w, run.kept[key], layer)
+    for kv, enc in ((0, ek), (1, ev)):
+        gpu = decode_slice(run.cache, geom, kv, b, layer, head, n, t0)
+        assert_planes_equal(gpu, enc, f"{w.name} kv={kv} slice={key}")
+    return ek, ev, HK, HV
+
+
+def attention_errors(gpu: np.ndarray, ref: np.ndarray):
+    rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300)
+    return rel, np.abs(gpu - ref).max()
+
+
+def assert_close_attention(gpu, ref, what):
+    rel, mx = attention_errors(np.asarray(gpu, np.float64), ref)
+    assert rel <= REL_L2 and mx <= MAX_ABS, f"{what}: rel-L2 {rel:.3e}, max-abs {mx:.3e}"
+    return rel, mx
+
+
+def oracle_attention(w, ek, ev, HK, HV, q_bits, loop, n):
+    return O.attention_slice(params(w), ek, ev, HK, HV, q_bits, loop, n, w.softmax_scale)

@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed): every declared symbol is
+exported, the cache geometry matches the documented layout and the storage
+accounting, and invalid arguments are rejected before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_int4_amd.rq as rq
+import oracle as O
+from tests.layout_decode import Geom
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+FAKE = ctypes.c_void_p(1 << 20)        # 256-aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(rq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rq.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+DESCS = [
+    rq.make_desc(1, 4, 1, 2, 256, 64),
+    rq.make_desc(4, 4, 24, 16, 8192 + 256, 128),
+    rq.make_desc(2, 32, 4, 55, 8192 + 256, 96),
+    rq.make_desc(2, 4, 3, 5, 300, 128, mode=rq.MODE_DIRECT),
+    rq.make_desc(3, 8, 2, 3, 77, 96, anchor_bits=2, residual_bits=4),
+    rq.make_desc(1, 4, 2, 2, 100, 64, anchor_bits=4, residual_bits=4, rotation=rq.ROT_NONE),
+]
+
+
+@pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.head_dim}-{d.max_tokens}-{d.mode}")
+def test_geometry_matches_documented_layout(desc):
+    g = Geom.of(desc)
+    assert rq.cache_bytes(desc) == g.total()
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        kv = int(rng.integers(0, 2))
+        b = int(rng.integers(0, desc.batch))
+        layer = int(rng.integers(0, desc.layers))
+        loop = int(rng.integers(0, desc.loops))
+        head = int(rng.integers(0, desc.kv_heads))
+        s = rq.cache_slot(desc, kv, b, layer, loop, head)
+        off = g.slot_offset(kv, b, layer, loop, head)
+        c, z, a = g.sub_sizes(loop)
+        assert s.codes_offset == off and s.codes_offset % 256 == 0
+        assert s.sz_offset == off + c
+        assert s.alpha_offset == (off + c + z if g.has_alpha(loop) else 2 ** 64 - 1)
+        assert s.bits == g.bits(loop)
+        assert s.code_bytes == desc.head_dim * s.bits // 8
+        assert s.slot_bytes == g.slot_bytes(loop)
+
+
+@pytest.mark.parametrize("mode,ab,rb", [(0, 4, 2), (1, 4, 2), (0, 4, 4), (0, 2, 2)])
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_cache_bytes_equal_accounting(mode, ab, rb, d):
+    """With max_tokens a multiple of 256 nothing is padded, so the buffer holds
+    exactly bits_per_element * elements / 8 bytes."""
+    desc = rq.make_desc(2, 8, 3, 5, 512, d, anchor_bits=ab, residual_bits=rb, mode=mode)
+    elements = 2 * 2 * 8 * 3 * 5 * 512 * d
+    bits = O.bits_per_element(ab, rb, 16, d, 4, with_alpha=(mode == 0))
+    assert rq.cache_bytes(desc) * 8 == bits * elements
+
+
+def test_unsupported_descriptors():
+    base = dict(batch=1, loops=4, layers=1, kv_heads=2, max_tokens=16, head_dim=64)
+    assert rq.validate_desc(rq.make_desc(**base)) == 0
+    bad = [dict(head_dim=80), dict(head_dim=256), dict(group_size=32), dict(loops=6),
+           dict(anchor_bits=3), dict(residual_bits=8), dict(mode=2), dict(alpha_mode=5),
+           dict(rotation=2), dict(loops=128, loops_per_group=4)]
+    for kw in bad:
+        args = {**base}
+        extra = {k: v for k, v in kw.items() if k not in base}
+        args.update({k: v for k, v in kw.items() if k in base})
+        assert rq.validate_desc(rq.make_desc(**args, **extra)) == 2, kw
+    for kw in [dict(batch=0), dict(max_tokens=0), dict(kv_heads=-1)]:
+        args = {**base, **kw}
+        assert rq.validate_desc(rq.make_desc(**args)) == 1, kw
+    assert rq.lib().rq_validate_desc(None) == 1
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    L = rq.lib()
+    d = rq.make_desc(1, 4, 1, 2, 256, 64)
+    D = ctypes.byref(d)
+    ws = rq.decode_workspace_bytes(d, 2, 256)
+    # quantize_append
+    assert L.rq_quantize_append(D, FAKE, FAKE, 200, 100, FAKE, None) == 3
+    assert L.rq_quantize_append(D, FAKE, FAKE, -1, 1, FAKE, None) == 1
+    assert L.rq_quantize_append(D, None, FAKE, 0, 1, FAKE, None) == 1
+    assert L.rq_quantize_append(D, FAKE, FAKE, 0, 1, None, None) == 1       # signs needed
+    assert L.rq_quantize_append(D, MISALIGNED, FAKE, 0, 1, FAKE, None) == 5
+    assert L.rq_quantize_append(D, FAKE, FAKE, 256, 0, FAKE, None) == 0      # empty append
+    # reconstruct
+    assert L.rq_reconstruct(D, FAKE, FAKE, 10, 300, 0, FAKE, None) == 3
+    assert L.rq_reconstruct(D, FAKE, FAKE, 10, 5, 0, FAKE, None) == 1
+    assert L.rq_reconstruct(D, FAKE, FAKE, 0, 4, 7, FAKE, None) == 1
+    assert L.rq_reconstruct(D, FAKE, FAKE, 3, 3, 0, FAKE, None) == 0
+    # decode attention
+    f = ctypes.c_float(0.125)
+    assert L.rq_decode_attention(D, FAKE, FAKE, 4, 0, FAKE, 2, 10, f, FAKE, ws, FAKE, None) == 1
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 1, FAKE, 2, 10, f, FAKE, ws, FAKE, None) == 1
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 3, 10, f, FAKE, ws, FAKE, None) == 2
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 257, f, FAKE, ws, FAKE, None) == 3
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, FAKE, 16, FAKE, None) == 4
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, MISALIGNED, ws, FAKE,
+                                 None) == 5
+    assert L.rq_decode_attention(D, FAKE, None, 0, 0, FAKE, 2, 256, f, FAKE, ws, FAKE, None) == 1
+    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, ctypes.c_float(float("nan")),
+                                 FAKE, ws, FAKE, None) == 1
+    # BF16 baseline
+    wb = rq.bf16_decode_workspace_bytes(d, 2, 256)
+    assert L.rq_bf16_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 300, f, FAKE, wb, FAKE,
+                                      None) == 3
+    assert L.rq_bf16_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, FAKE, 8, FAKE,
+                                      None) == 4
+    # probe
+    assert L.rq_read_probe(FAKE, 12, FAKE, None) == 1
+    assert L.rq_read_probe(MISALIGNED, 16, FAKE, None) == 5
+
+
+def test_workspace_bound_is_monotone():
+    for d in DESCS:
+        for hq in (d.kv_heads, 2 * d.kv_heads):
+            prev = 0
+            for n in [0, 1, 63, 64, 65, 500, 4096, 8192, 16384]:
+                w = rq.decode_workspace_bytes(d, hq, n)
+                assert w >= prev and w >= 256
+                prev = w
+
+
+def test_status_strings():
+    for s in range(7):
+        assert rq._status_string(s)
+    assert rq._status_string(99) == "unknown status"

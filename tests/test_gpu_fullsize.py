@@ -1,0 +1,67 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times (chunked fill, then one decode step: every loop x layer
+attention call and the new token's quantize-append).  The oracle checks
+sampled (batch row, layer, kv head) slices one by one: all their codes, FP8
+bytes and alphas bit for bit, and their attention outputs for every loop."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_int4_amd.synth import WORKLOADS
+from decode_attention_int4_amd.workload import RQDecode
+from tests.gpu_common import (assert_close_attention, bits16, check_slice_planes,
+                              oracle_attention, POOL, say)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "ouro8k_b4": ([(0, 0, 0), (3, 23, 15), (1, 11, 7)], None),
+    "ouro16k_b2": ([(1, 17, 3), (0, 6, 12)], None),
+    "ouro16k_b4": ([(3, 2, 14)], None),
+    "ouro16k_b4_direct": ([(2, 20, 5)], None),
+    "huginn8k_b2": ([(1, 3, 54), (0, 1, 20)], [0, 3, 5, 14, 15, 22, 30, 31]),
+}
+
+
+def _run_case(name, keep, loops=None, w=None):
+    w = w or WORKLOADS[name]
+    say(f"[fullsize] {name}: fill {w.n_tokens} tokens, batch {w.batch}")
+    run = RQDecode(w, keep=keep)
+    run.out.fill_(float("nan"))
+    run.step()
+    torch.cuda.synchronize()
+    out = run.out.cpu().numpy()
+    assert np.isfinite(out).all()
+    loops = range(w.loops) if loops is None else loops
+    for key in keep:
+        b, layer, head = key
+        say(f"[fullsize] {name}: oracle on slice {key}")
+        ek, ev, HK, HV = check_slice_planes(w, run, key)
+        futs = {loop: POOL.submit(oracle_attention, w, ek, ev, HK, HV,
+                                  bits16(run.q[loop, layer, b, head]), loop, run.N)
+                for loop in loops}
+        for loop, f in futs.items():
+            rel, mx = assert_close_attention(out[loop, layer, b, head], f.result(),
+                                             f"{name} slice {key} loop {loop}")
+        say(f"[fullsize] {name}: slice {key} ok (last rel-L2 {rel:.2e}, max-abs {mx:.2e})")
+    del run
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fullsize(name):
+    keep, loops = CASES[name]
+    _run_case(name, keep, loops)
+
+
+def test_capacity_batch128():
+    """Largest batch of the capacity sweep (8k context): 185 GB of packed cache."""
+    w = WORKLOADS["ouro8k_b4"].with_(name="ouro8k_b128", batch=128)
+    free, _ = torch.cuda.mem_get_info()
+    need = 1.47e9 * 128 + 8e9
+    if free < need:
+        pytest.skip(f"needs {need / 1e9:.0f} GB free, have {free / 1e9:.0f} GB")
+    _run_case("ouro8k_b128", [(127, 13, 9), (64, 0, 0)], loops=[0, 3], w=w)

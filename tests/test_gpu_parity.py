@@ -1,0 +1,155 @@
+"""GPU parity at oracle-friendly sizes: the tiny configuration in full, and
+every precision / scaling / rotation / mode variant at small ragged shapes
+with grouped-query heads, through the C ABI.  Codes, FP8 bytes and alphas
+must equal the oracle's bit for bit; attention outputs must be within 1e-3
+relative L2 and 2e-3 max-abs of the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_int4_amd import rq
+from decode_attention_int4_amd.synth import WORKLOADS, Workload, kv_chunk
+from decode_attention_int4_amd.workload import BF16Decode, RQDecode
+from tests.gpu_common import (assert_close_attention, bits16, check_slice_planes, encode_kept,
+                              oracle_attention, params, say)
+from tests.layout_decode import Geom, decode_slice
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = WORKLOADS["tiny"]
+    say(f"[tiny] building cache {w}")
+    keep = [(0, 0, 0), (0, 0, 1)]
+    run = RQDecode(w, keep=keep, chunk_tokens=100)  # appends of 100, 100, 56 tokens
+    torch.cuda.synchronize()
+    enc = {k: encode_kept(w, run.kept[k], k[1]) for k in keep}
+    return w, run, enc
+
+
+def test_tiny_planes_bit_exact(tiny):
+    w, run, enc = tiny
+    for key in run.kept:
+        check_slice_planes(w, run, key)
+
+
+def test_tiny_reconstruct(tiny):
+    w, run, enc = tiny
+    out32 = rq.reconstruct(run.desc, run.cache, run.signs, 0, run.N).cpu().numpy()
+    out16 = rq.reconstruct(run.desc, run.cache, run.signs, 0, run.N,
+                           out_dtype=torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+    p = params(w)
+    for (b, layer, head), (ek, ev, HK, HV) in enc.items():
+        for kv, e, H in ((0, ek, HK), (1, ev, HV)):
+            for loop in range(w.loops):
+                ref = O.reconstruct_slice(p, e, H, loop)
+                got = out32[kv, b, loop, layer, head].astype(np.float64)
+                tol = 4e-6 * max(1.0, np.abs(ref).max())
+                assert np.abs(got - ref).max() <= tol, (kv, loop)
+                got16 = O.bf16_decode(out16[kv, b, loop, layer, head])
+                ulp = np.abs(O.bf16_decode(O.bf16_encode(ref)) - ref) * 2 + 1e-30
+                assert np.all(np.abs(got16 - ref) <= np.maximum(ulp, 2 ** -7 * np.abs(ref)) + tol)
+
+
+@pytest.mark.parametrize("n", [1, 17, 64, 100, 129, 255, 256])
+def test_tiny_decode_every_length(tiny, n):
+    w, run, enc = tiny
+    for loop in range(w.loops):
+        out = rq.decode_attention(run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], n,
+                                  w.softmax_scale, run.ws).cpu().numpy()
+        for (b, layer, head), (ek, ev, HK, HV) in enc.items():
+            ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, 0, b, head]), loop, n)
+            assert_close_attention(out[b, head], ref, f"tiny loop {loop} n {n} head {head}")
+
+
+def test_tiny_empty_context_gives_zeros(tiny):
+    w, run, _ = tiny
+    out = torch.full((1, 2, 64), float("nan"), device="cuda")
+    rq.decode_attention(run.desc, run.cache, run.signs, 1, 0, run.q[1, 0], 0, w.softmax_scale,
+                        run.ws, out=out)
+    assert torch.all(out == 0)
+
+
+def test_tiny_step_and_append(tiny):
+    w, run, enc = tiny
+    run.out.fill_(float("nan"))
+    run.step()
+    torch.cuda.synchronize()
+    for (b, layer, head), (ek, ev, HK, HV) in enc.items():
+        for loop in range(w.loops):
+            ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, layer, b, head]), loop,
+                                   run.N)
+            assert_close_attention(run.out[loop, layer, b, head].cpu().numpy(), ref,
+                                   f"tiny step loop {loop}")
+        # the appended token at position N
+        new = run.new_kv[:, b, :, layer, head]           # [2, loops, 1, d]
+        nk, nv, _, _ = encode_kept(w, new, layer)
+        geom = Geom.of(run.desc)
+        for kv, e in ((0, nk), (1, nv)):
+            g = decode_slice(run.cache, geom, kv, b, layer, head, 1, run.N)
+            for name in ("codes", "s8", "z8", "alpha"):
+                assert np.array_equal(getattr(g, name), getattr(e, name)), name
+
+
+def test_workspace_counters_return_to_zero(tiny):
+    w, run, _ = tiny
+    torch.cuda.synchronize()
+    nbh = w.batch * w.q_heads
+    assert torch.all(run.ws[:4 * nbh] == 0)
+
+
+def test_bf16_baseline_tiny():
+    w = WORKLOADS["tiny"]
+    base = BF16Decode(w)
+    for loop in range(w.loops):
+        out = base.attend(loop, 0).cpu().numpy()
+        for head in range(w.kv_heads):
+            K = O.bf16_decode(bits16(base.k[0, loop, 0, head, :base.N]))
+            V = O.bf16_decode(bits16(base.v[0, loop, 0, head, :base.N]))
+            q = O.bf16_decode(bits16(base.q[loop, 0, 0, head]))
+            ref = O.attention_dense(q, K, V, w.softmax_scale)
+            assert_close_attention(out[0, head], ref, f"bf16 loop {loop}")
+
+
+def test_read_probe_xor():
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
+    sink = torch.zeros(rq.read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    rq.read_probe(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+
+
+VARIANTS = {
+    "residual": {},
+    "direct": dict(mode=1),
+    "uniform_int4": dict(anchor_bits=4, residual_bits=4),
+    "uniform_int2": dict(anchor_bits=2, residual_bits=2),
+    "int4_residual_int2_anchor": dict(anchor_bits=2, residual_bits=4),
+    "norm_ratio": dict(alpha_mode=1),
+    "alpha_one": dict(alpha_mode=2),
+    "no_rotation": dict(rotation=0),
+}
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_variants_small(d, variant):
+    w = Workload(f"small_{variant}_{d}", batch=2, loops=8, layers=2, kv_heads=2, q_heads=4,
+                 head_dim=d, n_tokens=333, seed=d + len(variant), **VARIANTS[variant])
+    keep = [(1, 1, 0), (0, 0, 1)]
+    say(f"[variant] {w.name}")
+    run = RQDecode(w, keep=keep, chunk_tokens=128)
+    run.step()
+    torch.cuda.synchronize()
+    out = run.out.cpu().numpy()
+    for key in keep:
+        b, layer, head = key
+        ek, ev, HK, HV = check_slice_planes(w, run, key)
+        for loop in range(w.loops):
+            for hq in (2 * head, 2 * head + 1):          # grouped-query heads of this kv head
+                ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, layer, b, hq]),
+                                       loop, run.N)
+                assert_close_attention(out[loop, layer, b, hq], ref,
+                                       f"{w.name} loop {loop} hq {hq}")
