@@ -133,8 +133,7 @@ def cpu_baseline(run, budget_s: float = 12.0):
     encs = []
     for key, kept in run.kept.items():
         b, layer, head = key
-        HK = O.rotation_matrix(w.head_dim, signs[0, layer])
-        HV = O.rotation_matrix(w.head_dim, signs[1, layer])
+        HK, HV = signs[0, layer].copy(), signs[1, layer].copy()
         encs.append((key, O.encode_slice(p, bits(kept[0]), HK), O.encode_slice(p, bits(kept[1]), HV),
                      HK, HV))
     jobs = [(e, loop) for e in encs for loop in range(w.loops)]
@@ -165,7 +164,7 @@ def cpu_baseline(run, budget_s: float = 12.0):
     t1 = time.perf_counter()
     for kv, b, layer, head, k in sample:
         if (kv, layer) not in Hs:
-            Hs[(kv, layer)] = O.rotation_matrix(w.head_dim, signs[kv, layer])
+            Hs[(kv, layer)] = signs[kv, layer].copy()
         P = w.loops_per_group
         x = O.bf16_decode(bits(new[kv, b, k * P:(k + 1) * P, layer, head, 0]))
         O.encode_group(p, x, Hs[(kv, layer)])

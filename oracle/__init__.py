@@ -94,24 +94,28 @@ def _declare(L):
     L.rqo_bf16_encode_n.argtypes = [_f64, ctypes.c_long, _u16]
     L.rqo_rotation_matrix.argtypes = [ctypes.c_int, _i8, _f64]
     L.rqo_rotation_matrix.restype = ctypes.c_int
+    L.rqo_rotate.argtypes = [ctypes.c_int, _i8, _f64, _f64]
+    L.rqo_rotate.restype = ctypes.c_int
+    L.rqo_rotate_t.argtypes = [ctypes.c_int, _i8, _f64, _f64]
+    L.rqo_rotate_t.restype = ctypes.c_int
     L.rqo_quant_group.argtypes = [_f64, ctypes.c_int, ctypes.c_int, _u8, _u8, _u8]
     L.rqo_quant_vector.argtypes = [_f64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8, _u8, _u8]
     L.rqo_dequant_vector.argtypes = [_u8, _u8, _u8, ctypes.c_int, ctypes.c_int, _f64]
-    L.rqo_encode_group.argtypes = [_P(_Params), _f64, _f64, _u8, _u8, _u8, _u16]
+    L.rqo_encode_group.argtypes = [_P(_Params), _f64, _i8, _u8, _u8, _u8, _u16]
     L.rqo_encode_group.restype = ctypes.c_int
-    L.rqo_reconstruct_group.argtypes = [_P(_Params), _u8, _u8, _u8, _u16, _f64, ctypes.c_int, _f64]
+    L.rqo_reconstruct_group.argtypes = [_P(_Params), _u8, _u8, _u8, _u16, _i8, ctypes.c_int, _f64]
     L.rqo_reconstruct_group.restype = ctypes.c_int
-    L.rqo_encode_slice.argtypes = [_P(_Params), ctypes.c_int, ctypes.c_int, _u16, _f64,
+    L.rqo_encode_slice.argtypes = [_P(_Params), ctypes.c_int, ctypes.c_int, _u16, _i8,
                                    _u8, _u8, _u8, _u16]
     L.rqo_encode_slice.restype = ctypes.c_int
     L.rqo_reconstruct_slice.argtypes = [_P(_Params), ctypes.c_int, ctypes.c_int, _u8, _u8, _u8,
-                                        _u16, _f64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64]
+                                        _u16, _i8, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64]
     L.rqo_reconstruct_slice.restype = ctypes.c_int
     L.rqo_attention_dense.argtypes = [ctypes.c_int, ctypes.c_int, _f64, _f64, _f64,
                                       ctypes.c_double, _f64]
     L.rqo_attention_dense.restype = ctypes.c_int
     L.rqo_attention_slice.argtypes = [_P(_Params), ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, _u16, _f64, _f64,
+                                      ctypes.c_int, _u16, _i8, _i8,
                                       _u8, _u8, _u8, _u16, _u8, _u8, _u8, _u16,
                                       ctypes.c_double, ctypes.c_int, _f64]
     L.rqo_attention_slice.restype = ctypes.c_int
@@ -159,6 +163,15 @@ def bf16_encode(x) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- rotation
+def _signs_ptr(signs, d):
+    """(array kept alive, pointer) for an optional int8 [d] sign vector."""
+    if signs is None:
+        return None, None
+    a = np.ascontiguousarray(signs, dtype=np.int8)
+    assert a.shape == (d,), f"signs must have shape ({d},)"
+    return a, _ptr(a, ctypes.c_int8)
+
+
 def rotation_matrix(d: int, signs) -> np.ndarray:
     s = np.ascontiguousarray(signs, dtype=np.int8)
     assert s.shape == (d,)
@@ -166,6 +179,25 @@ def rotation_matrix(d: int, signs) -> np.ndarray:
     _check(lib().rqo_rotation_matrix(d, _ptr(s, ctypes.c_int8), _ptr(H, ctypes.c_double)),
            "rotation_matrix")
     return H
+
+
+def rotate(d: int, signs, r) -> np.ndarray:
+    """y = H r, as exact +-1 sums followed by the 1/sqrt(n) scale."""
+    s, sp = _signs_ptr(signs, d)
+    v = np.ascontiguousarray(r, np.float64)
+    out = np.empty(d, np.float64)
+    _check(lib().rqo_rotate(d, sp, _ptr(v, ctypes.c_double), _ptr(out, ctypes.c_double)), "rotate")
+    return out
+
+
+def rotate_t(d: int, signs, y) -> np.ndarray:
+    """r = H^T y."""
+    s, sp = _signs_ptr(signs, d)
+    v = np.ascontiguousarray(y, np.float64)
+    out = np.empty(d, np.float64)
+    _check(lib().rqo_rotate_t(d, sp, _ptr(v, ctypes.c_double), _ptr(out, ctypes.c_double)),
+           "rotate_t")
+    return out
 
 
 # ---------------------------------------------------------------- quantizer
@@ -189,37 +221,33 @@ def dequant_vector(codes, s8, z8, g: int) -> np.ndarray:
     return out
 
 
-def encode_group(p: Params, x, H=None):
+def encode_group(p: Params, x, signs=None):
     """x: float64 [P, d] -> (codes [P,d], s8 [P,ng], z8 [P,ng], alpha [P])."""
     a = np.ascontiguousarray(x, dtype=np.float64)
     assert a.shape == (p.P, p.d)
-    if H is None:
-        H = np.eye(p.d)
-    Hc = np.ascontiguousarray(H, dtype=np.float64)
+    s, sp = _signs_ptr(signs, p.d)
     codes = np.zeros((p.P, p.d), np.uint8)
     s8 = np.zeros((p.P, p.ng), np.uint8)
     z8 = np.zeros((p.P, p.ng), np.uint8)
     alpha = np.zeros(p.P, np.uint16)
     cp = p.c()
-    _check(lib().rqo_encode_group(ctypes.byref(cp), _ptr(a, ctypes.c_double),
-                                  _ptr(Hc, ctypes.c_double), _ptr(codes, ctypes.c_uint8),
-                                  _ptr(s8, ctypes.c_uint8), _ptr(z8, ctypes.c_uint8),
-                                  _ptr(alpha, ctypes.c_uint16)), "encode_group")
+    _check(lib().rqo_encode_group(ctypes.byref(cp), _ptr(a, ctypes.c_double), sp,
+                                  _ptr(codes, ctypes.c_uint8), _ptr(s8, ctypes.c_uint8),
+                                  _ptr(z8, ctypes.c_uint8), _ptr(alpha, ctypes.c_uint16)),
+           "encode_group")
     return codes, s8, z8, alpha
 
 
-def reconstruct_group(p: Params, codes, s8, z8, alpha, H, j: int) -> np.ndarray:
-    if H is None:
-        H = np.eye(p.d)
+def reconstruct_group(p: Params, codes, s8, z8, alpha, signs, j: int) -> np.ndarray:
     args = [np.ascontiguousarray(codes, np.uint8), np.ascontiguousarray(s8, np.uint8),
-            np.ascontiguousarray(z8, np.uint8), np.ascontiguousarray(alpha, np.uint16),
-            np.ascontiguousarray(H, np.float64)]
+            np.ascontiguousarray(z8, np.uint8), np.ascontiguousarray(alpha, np.uint16)]
+    s, sp = _signs_ptr(signs, p.d)
     out = np.empty(p.d, np.float64)
     cp = p.c()
     _check(lib().rqo_reconstruct_group(
         ctypes.byref(cp), _ptr(args[0], ctypes.c_uint8), _ptr(args[1], ctypes.c_uint8),
-        _ptr(args[2], ctypes.c_uint8), _ptr(args[3], ctypes.c_uint16),
-        _ptr(args[4], ctypes.c_double), j, _ptr(out, ctypes.c_double)), "reconstruct_group")
+        _ptr(args[2], ctypes.c_uint8), _ptr(args[3], ctypes.c_uint16), sp, j,
+        _ptr(out, ctypes.c_double)), "reconstruct_group")
     return out
 
 
@@ -232,34 +260,30 @@ class Encoded:
     alpha: np.ndarray   # uint16 [L, N]
 
 
-def encode_slice(p: Params, x_bf16, H=None) -> Encoded:
+def encode_slice(p: Params, x_bf16, signs=None) -> Encoded:
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     L, N, d = x.shape
     assert d == p.d
-    if H is None:
-        H = np.eye(d)
-    Hc = np.ascontiguousarray(H, dtype=np.float64)
+    s, sp = _signs_ptr(signs, d)
     e = Encoded(np.zeros((L, N, d), np.uint8), np.zeros((L, N, p.ng), np.uint8),
                 np.zeros((L, N, p.ng), np.uint8), np.zeros((L, N), np.uint16))
     cp = p.c()
-    _check(lib().rqo_encode_slice(ctypes.byref(cp), L, N, _ptr(x, ctypes.c_uint16),
-                                  _ptr(Hc, ctypes.c_double), _ptr(e.codes, ctypes.c_uint8),
-                                  _ptr(e.s8, ctypes.c_uint8), _ptr(e.z8, ctypes.c_uint8),
-                                  _ptr(e.alpha, ctypes.c_uint16)), "encode_slice")
+    _check(lib().rqo_encode_slice(ctypes.byref(cp), L, N, _ptr(x, ctypes.c_uint16), sp,
+                                  _ptr(e.codes, ctypes.c_uint8), _ptr(e.s8, ctypes.c_uint8),
+                                  _ptr(e.z8, ctypes.c_uint8), _ptr(e.alpha, ctypes.c_uint16)),
+           "encode_slice")
     return e
 
 
-def reconstruct_slice(p: Params, e: Encoded, H, loop: int, t0: int = 0, t1=None) -> np.ndarray:
+def reconstruct_slice(p: Params, e: Encoded, signs, loop: int, t0: int = 0, t1=None) -> np.ndarray:
     L, N, d = e.codes.shape
     t1 = N if t1 is None else t1
-    if H is None:
-        H = np.eye(d)
-    Hc = np.ascontiguousarray(H, dtype=np.float64)
+    s, sp = _signs_ptr(signs, d)
     out = np.empty((t1 - t0, d), np.float64)
     cp = p.c()
     _check(lib().rqo_reconstruct_slice(
         ctypes.byref(cp), L, N, _ptr(e.codes, ctypes.c_uint8), _ptr(e.s8, ctypes.c_uint8),
-        _ptr(e.z8, ctypes.c_uint8), _ptr(e.alpha, ctypes.c_uint16), _ptr(Hc, ctypes.c_double),
+        _ptr(e.z8, ctypes.c_uint8), _ptr(e.alpha, ctypes.c_uint16), sp,
         loop, t0, t1, _ptr(out, ctypes.c_double)), "reconstruct_slice")
     return out
 
@@ -276,18 +300,17 @@ def attention_dense(q, K, V, scale: float) -> np.ndarray:
     return out
 
 
-def attention_slice(p: Params, ek: Encoded, ev: Encoded, HK, HV, q_bf16, loop: int, n: int,
-                    scale: float, fused: bool = False) -> np.ndarray:
+def attention_slice(p: Params, ek: Encoded, ev: Encoded, signs_k, signs_v, q_bf16, loop: int,
+                    n: int, scale: float, fused: bool = False) -> np.ndarray:
     L, N, d = ek.codes.shape
     q = np.ascontiguousarray(q_bf16, np.uint16)
     assert q.shape == (d,)
-    HKc = np.ascontiguousarray(np.eye(d) if HK is None else HK, np.float64)
-    HVc = np.ascontiguousarray(np.eye(d) if HV is None else HV, np.float64)
+    sk, skp = _signs_ptr(signs_k, d)
+    sv, svp = _signs_ptr(signs_v, d)
     out = np.empty(d, np.float64)
     cp = p.c()
     _check(lib().rqo_attention_slice(
-        ctypes.byref(cp), L, N, n, loop, _ptr(q, ctypes.c_uint16), _ptr(HKc, ctypes.c_double),
-        _ptr(HVc, ctypes.c_double),
+        ctypes.byref(cp), L, N, n, loop, _ptr(q, ctypes.c_uint16), skp, svp,
         _ptr(ek.codes, ctypes.c_uint8), _ptr(ek.s8, ctypes.c_uint8), _ptr(ek.z8, ctypes.c_uint8),
         _ptr(ek.alpha, ctypes.c_uint16),
         _ptr(ev.codes, ctypes.c_uint8), _ptr(ev.s8, ctypes.c_uint8), _ptr(ev.z8, ctypes.c_uint8),

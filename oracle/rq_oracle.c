@@ -160,20 +160,87 @@ int rqo_rotation_matrix(int d, const int8_t* signs, double* H) {
   return 0;
 }
 
-static void matvec(int d, const double* H, const double* v, double* out) {
-  for (int i = 0; i < d; ++i) {
-    double acc = 0.0;
-    for (int j = 0; j < d; ++j) acc += H[(size_t)i * d + j] * v[j];
-    out[i] = acc;
+/* A rotation of dimension d as its definition factors it: per block of the
+ * binary decomposition of d, the Sylvester matrix S_n (entries +-1) and the
+ * scale 1/sqrt(n); the signs multiply the input.  Applying it as the +-1 sum
+ * followed by one multiplication by 1/sqrt(n) keeps the sum exact, so an exact
+ * zero stays an exact zero and a rounding tie downstream is decided on the
+ * exact value. */
+typedef struct {
+  int d, nblk;
+  int off[32], n[32];
+  double inv[32];
+  double* S[32];
+  const int8_t* signs;
+} rot_t;
+
+static void rot_free(rot_t* R) {
+  for (int b = 0; b < R->nblk; ++b) free(R->S[b]);
+  R->nblk = 0;
+}
+
+static int rot_init(rot_t* R, int d, const int8_t* signs) {
+  memset(R, 0, sizeof *R);
+  R->d = d;
+  R->signs = signs;
+  int off = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    int n = 1 << bit;
+    if (!(d & n)) continue;
+    double* S = (double*)malloc(sizeof(double) * (size_t)n * (size_t)n);
+    if (!S) {
+      rot_free(R);
+      return -2;
+    }
+    sylvester(n, S);
+    R->off[R->nblk] = off;
+    R->n[R->nblk] = n;
+    R->inv[R->nblk] = 1.0 / sqrt((double)n);
+    R->S[R->nblk] = S;
+    R->nblk++;
+    off += n;
+  }
+  return 0;
+}
+
+/* y = B diag(signs) r */
+static void rot_apply(const rot_t* R, const double* r, double* y) {
+  for (int b = 0; b < R->nblk; ++b) {
+    const int n = R->n[b], o = R->off[b];
+    for (int i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < n; ++j) acc += R->S[b][(size_t)i * n + j] * (R->signs[o + j] * r[o + j]);
+      y[o + i] = acc * R->inv[b];
+    }
   }
 }
 
-static void matvec_t(int d, const double* H, const double* v, double* out) {
-  for (int j = 0; j < d; ++j) {
-    double acc = 0.0;
-    for (int i = 0; i < d; ++i) acc += H[(size_t)i * d + j] * v[i];
-    out[j] = acc;
+/* r = diag(signs) B^T y */
+static void rot_apply_t(const rot_t* R, const double* y, double* r) {
+  for (int b = 0; b < R->nblk; ++b) {
+    const int n = R->n[b], o = R->off[b];
+    for (int j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < n; ++i) acc += R->S[b][(size_t)i * n + j] * y[o + i];
+      r[o + j] = R->signs[o + j] * (acc * R->inv[b]);
+    }
   }
+}
+
+int rqo_rotate(int d, const int8_t* signs, const double* r, double* y) {
+  rot_t R;
+  if (d <= 0 || rot_init(&R, d, signs)) return -1;
+  rot_apply(&R, r, y);
+  rot_free(&R);
+  return 0;
+}
+
+int rqo_rotate_t(int d, const int8_t* signs, const double* y, double* r) {
+  rot_t R;
+  if (d <= 0 || rot_init(&R, d, signs)) return -1;
+  rot_apply_t(&R, y, r);
+  rot_free(&R);
+  return 0;
 }
 
 /* ------------------------------------------------------------------------- */
@@ -231,6 +298,18 @@ static int params_ok(const rqo_params* p) {
   return 1;
 }
 
+static int uses_rotation(const rqo_params* p) {
+  return p->mode == RQO_MODE_RESIDUAL && p->rotate;
+}
+
+/* Rotation of a parameter set: initialized only when residuals are rotated. */
+static int rot_for(const rqo_params* p, const int8_t* signs, rot_t* R) {
+  memset(R, 0, sizeof *R);
+  if (!uses_rotation(p)) return 0;
+  if (!signs) return -1;
+  return rot_init(R, p->d, signs);
+}
+
 /* Anchor = last loop of the group ([abstract]: "uses the final-loop KV states
  * as a reference"; [ai4s p1]: "final-loop KV as a shared anchor").  Residual
  * mode: the anchor is stored at anchor_bits without rotation; every other
@@ -239,9 +318,8 @@ static int params_ok(const rqo_params* p) {
  * Direct mode: every loop is quantized on its own, the anchor-position loop at
  * anchor_bits and the others at residual_bits ([ai4s p2]: "direct
  * quantization"). */
-int rqo_encode_group(const rqo_params* p, const double* x, const double* H,
-                     uint8_t* codes, uint8_t* s8, uint8_t* z8, uint16_t* alpha) {
-  if (!params_ok(p)) return -1;
+static int encode_group_r(const rqo_params* p, const double* x, const rot_t* R,
+                          uint8_t* codes, uint8_t* s8, uint8_t* z8, uint16_t* alpha) {
   const int d = p->d, g = p->g, P = p->P, ng = d / g, a = P - 1;
   double* A = (double*)malloc(sizeof(double) * d * 4);
   if (!A) return -2;
@@ -261,7 +339,7 @@ int rqo_encode_group(const rqo_params* p, const double* x, const double* H,
     }
     for (int i = 0; i < d; ++i) r[i] = x[l * d + i] - A[i];
     if (p->rotate)
-      matvec(d, H, r, y);
+      rot_apply(R, r, y);
     else
       memcpy(y, r, sizeof(double) * d);
     rqo_quant_vector(y, d, g, p->residual_bits, codes + l * d, s8 + l * ng, z8 + l * ng);
@@ -287,14 +365,23 @@ int rqo_encode_group(const rqo_params* p, const double* x, const double* H,
   return 0;
 }
 
+int rqo_encode_group(const rqo_params* p, const double* x, const int8_t* signs,
+                     uint8_t* codes, uint8_t* s8, uint8_t* z8, uint16_t* alpha) {
+  if (!params_ok(p)) return -1;
+  rot_t R;
+  if (rot_for(p, signs, &R)) return -1;
+  int rc = encode_group_r(p, x, &R, codes, s8, z8, alpha);
+  rot_free(&R);
+  return rc;
+}
+
 /* Shared-anchor reconstruction from exactly two stored pieces, the anchor and
  * the loop's own residual ([ai4s p3]: "shared-anchor reconstruction ... needs
  * only two KV cache reads"; [agihunt]: "reads back the anchor plus the
  * residuals"): xhat_l = deq(anchor) + alpha_l * H^T deq(residual_l). */
-int rqo_reconstruct_group(const rqo_params* p, const uint8_t* codes, const uint8_t* s8,
-                          const uint8_t* z8, const uint16_t* alpha, const double* H,
-                          int j, double* out) {
-  if (!params_ok(p) || j < 0 || j >= p->P) return -1;
+static int reconstruct_group_r(const rqo_params* p, const uint8_t* codes, const uint8_t* s8,
+                               const uint8_t* z8, const uint16_t* alpha, const rot_t* R, int j,
+                               double* out) {
   const int d = p->d, g = p->g, ng = d / g, a = p->P - 1;
   if (p->mode == RQO_MODE_DIRECT || j == a) {
     rqo_dequant_vector(codes + j * d, s8 + j * ng, z8 + j * ng, d, g, out);
@@ -307,7 +394,7 @@ int rqo_reconstruct_group(const rqo_params* p, const uint8_t* codes, const uint8
   rqo_dequant_vector(codes + a * d, s8 + a * ng, z8 + a * ng, d, g, A);
   rqo_dequant_vector(codes + j * d, s8 + j * ng, z8 + j * ng, d, g, yh);
   if (p->rotate)
-    matvec_t(d, H, yh, rh);
+    rot_apply_t(R, yh, rh);
   else
     memcpy(rh, yh, sizeof(double) * d);
   double al = rqo_bf16_decode(alpha[j]);
@@ -316,31 +403,40 @@ int rqo_reconstruct_group(const rqo_params* p, const uint8_t* codes, const uint8
   return 0;
 }
 
+int rqo_reconstruct_group(const rqo_params* p, const uint8_t* codes, const uint8_t* s8,
+                          const uint8_t* z8, const uint16_t* alpha, const int8_t* signs,
+                          int j, double* out) {
+  if (!params_ok(p) || j < 0 || j >= p->P) return -1;
+  rot_t R;
+  if (rot_for(p, signs, &R)) return -1;
+  int rc = reconstruct_group_r(p, codes, s8, z8, alpha, &R, j, out);
+  rot_free(&R);
+  return rc;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Slices                                                                    */
 /* ------------------------------------------------------------------------- */
 
-int rqo_encode_slice(const rqo_params* p, int L, int N, const uint16_t* x, const double* H,
+int rqo_encode_slice(const rqo_params* p, int L, int N, const uint16_t* x, const int8_t* signs,
                      uint8_t* codes, uint8_t* s8, uint8_t* z8, uint16_t* alpha) {
   if (!params_ok(p) || L <= 0 || L % p->P || N < 0) return -1;
   const int d = p->d, P = p->P, ng = d / p->g;
+  rot_t R;
+  if (rot_for(p, signs, &R)) return -1;
   double* xg = (double*)malloc(sizeof(double) * P * d);
   uint8_t* cg = (uint8_t*)malloc((size_t)P * d);
   uint8_t* sg = (uint8_t*)malloc((size_t)P * ng);
   uint8_t* zg = (uint8_t*)malloc((size_t)P * ng);
   uint16_t* ag = (uint16_t*)malloc(sizeof(uint16_t) * P);
-  if (!xg || !cg || !sg || !zg || !ag) {
-    free(xg); free(cg); free(sg); free(zg); free(ag);
-    return -2;
-  }
-  int rc = 0;
+  int rc = (!xg || !cg || !sg || !zg || !ag) ? -2 : 0;
   for (int k = 0; k < L / P && rc == 0; ++k) {
     for (int t = 0; t < N && rc == 0; ++t) {
       for (int j = 0; j < P; ++j) {
         const uint16_t* src = x + ((size_t)(k * P + j) * N + t) * d;
         for (int i = 0; i < d; ++i) xg[j * d + i] = rqo_bf16_decode(src[i]);
       }
-      rc = rqo_encode_group(p, xg, H, cg, sg, zg, ag);
+      rc = encode_group_r(p, xg, &R, cg, sg, zg, ag);
       for (int j = 0; j < P; ++j) {
         size_t v = (size_t)(k * P + j) * N + t;
         memcpy(codes + v * d, cg + j * d, (size_t)d);
@@ -351,6 +447,7 @@ int rqo_encode_slice(const rqo_params* p, int L, int N, const uint16_t* x, const
     }
   }
   free(xg); free(cg); free(sg); free(zg); free(ag);
+  rot_free(&R);
   return rc;
 }
 
@@ -368,27 +465,33 @@ static void gather_group(const rqo_params* p, int N, int loop, int t, const uint
   }
 }
 
-int rqo_reconstruct_slice(const rqo_params* p, int L, int N, const uint8_t* codes,
-                          const uint8_t* s8, const uint8_t* z8, const uint16_t* alpha,
-                          const double* H, int loop, int t0, int t1, double* out) {
-  if (!params_ok(p) || L <= 0 || L % p->P || loop < 0 || loop >= L || t0 < 0 || t1 > N ||
-      t0 > t1)
-    return -1;
+static int reconstruct_slice_r(const rqo_params* p, int N, const uint8_t* codes,
+                               const uint8_t* s8, const uint8_t* z8, const uint16_t* alpha,
+                               const rot_t* R, int loop, int t0, int t1, double* out) {
   const int d = p->d, P = p->P, ng = d / p->g;
   uint8_t* cg = (uint8_t*)malloc((size_t)P * d);
   uint8_t* sg = (uint8_t*)malloc((size_t)P * ng);
   uint8_t* zg = (uint8_t*)malloc((size_t)P * ng);
   uint16_t* ag = (uint16_t*)malloc(sizeof(uint16_t) * P);
-  if (!cg || !sg || !zg || !ag) {
-    free(cg); free(sg); free(zg); free(ag);
-    return -2;
-  }
-  int rc = 0;
+  int rc = (!cg || !sg || !zg || !ag) ? -2 : 0;
   for (int t = t0; t < t1 && rc == 0; ++t) {
     gather_group(p, N, loop, t, codes, s8, z8, alpha, cg, sg, zg, ag);
-    rc = rqo_reconstruct_group(p, cg, sg, zg, ag, H, loop % P, out + (size_t)(t - t0) * d);
+    rc = reconstruct_group_r(p, cg, sg, zg, ag, R, loop % P, out + (size_t)(t - t0) * d);
   }
   free(cg); free(sg); free(zg); free(ag);
+  return rc;
+}
+
+int rqo_reconstruct_slice(const rqo_params* p, int L, int N, const uint8_t* codes,
+                          const uint8_t* s8, const uint8_t* z8, const uint16_t* alpha,
+                          const int8_t* signs, int loop, int t0, int t1, double* out) {
+  if (!params_ok(p) || L <= 0 || L % p->P || loop < 0 || loop >= L || t0 < 0 || t1 > N ||
+      t0 > t1)
+    return -1;
+  rot_t R;
+  if (rot_for(p, signs, &R)) return -1;
+  int rc = reconstruct_slice_r(p, N, codes, s8, z8, alpha, &R, loop, t0, t1, out);
+  rot_free(&R);
   return rc;
 }
 
@@ -429,7 +532,7 @@ int rqo_attention_dense(int n, int d, const double* q, const double* Khat, const
  * s*sum(q*c) + z*sum(q), and H^T applied once to sum_t p_t alpha_t deq(R_t).
  * Both must agree to rounding. */
 int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
-                        const uint16_t* q_bf16, const double* HK, const double* HV,
+                        const uint16_t* q_bf16, const int8_t* signs_k, const int8_t* signs_v,
                         const uint8_t* kc, const uint8_t* ks, const uint8_t* kz,
                         const uint16_t* ka, const uint8_t* vc, const uint8_t* vs,
                         const uint8_t* vz, const uint16_t* va, double scale, int fused,
@@ -437,93 +540,94 @@ int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
   if (!params_ok(p) || L <= 0 || L % p->P || loop < 0 || loop >= L || n < 0 || n > N)
     return -1;
   const int d = p->d, g = p->g, ng = d / g, P = p->P;
-  double* q = (double*)malloc(sizeof(double) * d);
-  if (!q) return -2;
-  for (int i = 0; i < d; ++i) q[i] = rqo_bf16_decode(q_bf16[i]);
-  int rc = 0;
-
-  if (!fused) {
-    double* Kh = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
-    double* Vh = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
-    if (!Kh || !Vh) {
-      free(Kh); free(Vh); free(q);
-      return -2;
-    }
-    rc = rqo_reconstruct_slice(p, L, N, kc, ks, kz, ka, HK, loop, 0, n, Kh);
-    if (!rc) rc = rqo_reconstruct_slice(p, L, N, vc, vs, vz, va, HV, loop, 0, n, Vh);
-    if (!rc) rc = rqo_attention_dense(n, d, q, Kh, Vh, scale, out);
-    free(Kh); free(Vh); free(q);
-    return rc;
+  rot_t RK, RV;
+  if (rot_for(p, signs_k, &RK)) return -1;
+  if (rot_for(p, signs_v, &RV)) {
+    rot_free(&RK);
+    return -1;
   }
-
-  const int j = loop % P, a = P - 1;
-  const int two = (p->mode == RQO_MODE_RESIDUAL && j != a);
-  const int own = (p->mode == RQO_MODE_DIRECT) ? loop : (loop - j + a); /* first plane */
+  double* q = (double*)malloc(sizeof(double) * d);
+  double* Kh = NULL;
+  double* Vh = NULL;
   double* u = (double*)malloc(sizeof(double) * d);
   double* lg = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
   double* accA = (double*)calloc((size_t)d, sizeof(double));
   double* accR = (double*)calloc((size_t)d, sizeof(double));
   double* tmp = (double*)malloc(sizeof(double) * d);
-  if (!u || !lg || !accA || !accR || !tmp) {
-    free(q); free(u); free(lg); free(accA); free(accR); free(tmp);
-    return -2;
-  }
-  if (two && p->rotate)
-    matvec(d, HK, q, u);
-  else
-    memcpy(u, q, sizeof(double) * d);
+  int rc = (!q || !u || !lg || !accA || !accR || !tmp) ? -2 : 0;
+  if (rc == 0)
+    for (int i = 0; i < d; ++i) q[i] = rqo_bf16_decode(q_bf16[i]);
 
-  double m = -INFINITY;
-  for (int t = 0; t < n; ++t) {
-    size_t vA = (size_t)own * N + t;
-    double la = 0.0;
-    for (int gi = 0; gi < ng; ++gi) {
-      double sq = 0.0, sqc = 0.0;
-      for (int i = gi * g; i < (gi + 1) * g; ++i) {
-        sq += q[i];
-        sqc += q[i] * kc[vA * d + i];
-      }
-      la += rqo_fp8_decode(ks[vA * ng + gi]) * sqc + rqo_fp8_decode(kz[vA * ng + gi]) * sq;
-    }
-    double lr = 0.0;
-    if (two) {
-      size_t vR = (size_t)loop * N + t;
+  if (rc == 0 && !fused) {
+    Kh = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+    Vh = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+    rc = (!Kh || !Vh) ? -2 : 0;
+    if (!rc) rc = reconstruct_slice_r(p, N, kc, ks, kz, ka, &RK, loop, 0, n, Kh);
+    if (!rc) rc = reconstruct_slice_r(p, N, vc, vs, vz, va, &RV, loop, 0, n, Vh);
+    if (!rc) rc = rqo_attention_dense(n, d, q, Kh, Vh, scale, out);
+  } else if (rc == 0) {
+    const int j = loop % P, a = P - 1;
+    const int two = (p->mode == RQO_MODE_RESIDUAL && j != a);
+    const int own = (p->mode == RQO_MODE_DIRECT) ? loop : (loop - j + a); /* first plane */
+    if (two && p->rotate)
+      rot_apply(&RK, q, u);
+    else
+      memcpy(u, q, sizeof(double) * d);
+
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+      size_t vA = (size_t)own * N + t;
+      double la = 0.0;
       for (int gi = 0; gi < ng; ++gi) {
-        double su = 0.0, suc = 0.0;
+        double sq = 0.0, sqc = 0.0;
         for (int i = gi * g; i < (gi + 1) * g; ++i) {
-          su += u[i];
-          suc += u[i] * kc[vR * d + i];
+          sq += q[i];
+          sqc += q[i] * kc[vA * d + i];
         }
-        lr += rqo_fp8_decode(ks[vR * ng + gi]) * suc + rqo_fp8_decode(kz[vR * ng + gi]) * su;
+        la += rqo_fp8_decode(ks[vA * ng + gi]) * sqc + rqo_fp8_decode(kz[vA * ng + gi]) * sq;
       }
-      lr *= rqo_bf16_decode(ka[vR]);
+      double lr = 0.0;
+      if (two) {
+        size_t vR = (size_t)loop * N + t;
+        for (int gi = 0; gi < ng; ++gi) {
+          double su = 0.0, suc = 0.0;
+          for (int i = gi * g; i < (gi + 1) * g; ++i) {
+            su += u[i];
+            suc += u[i] * kc[vR * d + i];
+          }
+          lr += rqo_fp8_decode(ks[vR * ng + gi]) * suc + rqo_fp8_decode(kz[vR * ng + gi]) * su;
+        }
+        lr *= rqo_bf16_decode(ka[vR]);
+      }
+      lg[t] = scale * (la + lr);
+      if (lg[t] > m) m = lg[t];
     }
-    lg[t] = scale * (la + lr);
-    if (lg[t] > m) m = lg[t];
-  }
-  double l = 0.0;
-  for (int t = 0; t < n; ++t) {
-    double w = exp(lg[t] - m);
-    l += w;
-    size_t vA = (size_t)own * N + t;
-    for (int i = 0; i < d; ++i)
-      accA[i] += w * (rqo_fp8_decode(vs[vA * ng + i / g]) * vc[vA * d + i] +
-                      rqo_fp8_decode(vz[vA * ng + i / g]));
-    if (two) {
-      size_t vR = (size_t)loop * N + t;
-      double al = rqo_bf16_decode(va[vR]);
+    double l = 0.0;
+    for (int t = 0; t < n; ++t) {
+      double w = exp(lg[t] - m);
+      l += w;
+      size_t vA = (size_t)own * N + t;
       for (int i = 0; i < d; ++i)
-        accR[i] += w * al *
-                   (rqo_fp8_decode(vs[vR * ng + i / g]) * vc[vR * d + i] +
-                    rqo_fp8_decode(vz[vR * ng + i / g]));
+        accA[i] += w * (rqo_fp8_decode(vs[vA * ng + i / g]) * vc[vA * d + i] +
+                        rqo_fp8_decode(vz[vA * ng + i / g]));
+      if (two) {
+        size_t vR = (size_t)loop * N + t;
+        double al = rqo_bf16_decode(va[vR]);
+        for (int i = 0; i < d; ++i)
+          accR[i] += w * al *
+                     (rqo_fp8_decode(vs[vR * ng + i / g]) * vc[vR * d + i] +
+                      rqo_fp8_decode(vz[vR * ng + i / g]));
+      }
     }
+    if (two && p->rotate)
+      rot_apply_t(&RV, accR, tmp);
+    else
+      memcpy(tmp, accR, sizeof(double) * d);
+    for (int i = 0; i < d; ++i) out[i] = (n > 0) ? (accA[i] + tmp[i]) / l : 0.0;
   }
-  if (two && p->rotate)
-    matvec_t(d, HV, accR, tmp);
-  else
-    memcpy(tmp, accR, sizeof(double) * d);
-  for (int i = 0; i < d; ++i) out[i] = (n > 0) ? (accA[i] + tmp[i]) / l : 0.0;
-  free(q); free(u); free(lg); free(accA); free(accR); free(tmp);
+  free(q); free(u); free(lg); free(accA); free(accR); free(tmp); free(Kh); free(Vh);
+  rot_free(&RK);
+  rot_free(&RV);
   return rc;
 }
 

@@ -58,8 +58,15 @@ void rqo_fp8_encode_n(const double* in, long n, uint8_t* out);
 void rqo_bf16_decode_n(const uint16_t* in, long n, double* out);
 void rqo_bf16_encode_n(const double* in, long n, uint16_t* out);
 
-/* ---- rotation H = B * diag(signs), row-major d*d; returns 0 on success ---- */
+/* ---- rotation H = B * diag(signs) ----
+ * B is block diagonal over the binary decomposition of d (largest block first),
+ * each block the n x n Sylvester Walsh-Hadamard matrix times 1/sqrt(n).
+ * rqo_rotation_matrix writes H row-major (d*d); rqo_rotate computes y = H r and
+ * rqo_rotate_t computes r = H^T y as the exact +-1 sums followed by the scale.
+ * Functions below that take `signs` ignore it when residuals are not rotated. */
 int rqo_rotation_matrix(int d, const int8_t* signs, double* H);
+int rqo_rotate(int d, const int8_t* signs, const double* r, double* y);
+int rqo_rotate_t(int d, const int8_t* signs, const double* y, double* r);
 
 /* ---- group quantizer and its inverse ---- */
 void rqo_quant_group(const double* x, int g, int bits,
@@ -71,28 +78,29 @@ void rqo_dequant_vector(const uint8_t* codes, const uint8_t* s8, const uint8_t* 
 
 /* ---- one loop group of one token vector ---- */
 int rqo_encode_group(const rqo_params* p, const double* x /* [P][d] */,
-                     const double* H,
+                     const int8_t* signs /* [d] */,
                      uint8_t* codes /* [P][d] */, uint8_t* s8 /* [P][ng] */,
                      uint8_t* z8 /* [P][ng] */, uint16_t* alpha /* [P] */);
 int rqo_reconstruct_group(const rqo_params* p, const uint8_t* codes,
                           const uint8_t* s8, const uint8_t* z8,
-                          const uint16_t* alpha, const double* H, int j,
+                          const uint16_t* alpha, const int8_t* signs, int j,
                           double* out /* [d] */);
 
 /* ---- whole slices (see header comment for array layouts) ---- */
 int rqo_encode_slice(const rqo_params* p, int L, int N, const uint16_t* x,
-                     const double* H, uint8_t* codes, uint8_t* s8, uint8_t* z8,
+                     const int8_t* signs, uint8_t* codes, uint8_t* s8, uint8_t* z8,
                      uint16_t* alpha);
 int rqo_reconstruct_slice(const rqo_params* p, int L, int N,
                           const uint8_t* codes, const uint8_t* s8, const uint8_t* z8,
-                          const uint16_t* alpha, const double* H, int loop,
+                          const uint16_t* alpha, const int8_t* signs, int loop,
                           int t0, int t1, double* out /* [t1-t0][d] */);
 
 /* ---- attention of one query over tokens [0, n) ---- */
 int rqo_attention_dense(int n, int d, const double* q, const double* Khat,
                         const double* Vhat, double scale, double* out);
 int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
-                        const uint16_t* q_bf16, const double* HK, const double* HV,
+                        const uint16_t* q_bf16, const int8_t* signs_k,
+                        const int8_t* signs_v,
                         const uint8_t* kc, const uint8_t* ks, const uint8_t* kz,
                         const uint16_t* ka,
                         const uint8_t* vc, const uint8_t* vs, const uint8_t* vz,

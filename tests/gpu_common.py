@@ -3,6 +3,7 @@ plane comparison through the documented layout, and the error metrics."""
 from __future__ import annotations
 
 import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
@@ -32,8 +33,9 @@ def params(w: Workload) -> O.Params:
 
 
 def rotations(w: Workload, layer: int):
+    """Sign vectors of K and V at `layer` (the oracle builds H from them)."""
     s = rotation_signs(w).numpy()
-    return (O.rotation_matrix(w.head_dim, s[0, layer]), O.rotation_matrix(w.head_dim, s[1, layer]))
+    return s[0, layer].copy(), s[1, layer].copy()
 
 
 def bits16(t: torch.Tensor) -> np.ndarray:
@@ -49,16 +51,21 @@ def encode_kept(w: Workload, kept: torch.Tensor, layer: int):
     return fk.result(), fv.result(), HK, HV
 
 
-def assert_planes_equal(gpu: "Planes", enc: O.Encoded, what: str, loops=None):
+def assert_planes_equal(gpu: "Planes", enc: O.Encoded, what: str, loops=None, dump=None):
     loops = range(enc.codes.shape[0]) if loops is None else loops
+    msgs = []
     for l in loops:
         for name in ("codes", "s8", "z8", "alpha"):
             a, b = getattr(gpu, name)[l], getattr(enc, name)[l]
             if not np.array_equal(a, b):
                 bad = np.argwhere(a != b)
-                raise AssertionError(f"{what} loop {l} {name}: {len(bad)} mismatches, first at "
-                                     f"{bad[0].tolist()}: gpu {a[tuple(bad[0])]} oracle "
-                                     f"{b[tuple(bad[0])]}")
+                msgs.append(f"{what} loop {l} {name}: {len(bad)} mismatches, first at "
+                            f"{bad[0].tolist()}: gpu {a[tuple(bad[0])]} oracle "
+                            f"{b[tuple(bad[0])]}")
+    if msgs:
+        if dump is not None:
+            dump(gpu, enc)
+        raise AssertionError("; ".join(msgs))
 
 
 def check_slice_planes(w, run, key, t0=0, n=None):
@@ -66,9 +73,18 @@ def check_slice_planes(w, run, key, t0=0, n=None):
     geom = Geom.of(run.desc)
     n = run.N if n is None else n
     ek, ev, HK, HV = encode_kept(w, run.kept[key], layer)
-    for kv, enc in ((0, ek), (1, ev)):
+    for kv, enc, H in ((0, ek, HK), (1, ev, HV)):
         gpu = decode_slice(run.cache, geom, kv, b, layer, head, n, t0)
-        assert_planes_equal(gpu, enc, f"{w.name} kv={kv} slice={key}")
+
+        def dump(g, e, kv=kv, H=H):
+            os.makedirs("gpurun_out", exist_ok=True)
+            path = f"gpurun_out/mismatch_{w.name}_kv{kv}_{b}_{layer}_{head}.npz"
+            np.savez_compressed(path, x=bits16(run.kept[key][kv]), H=H,
+                                gpu_codes=g.codes, gpu_s8=g.s8, gpu_z8=g.z8, gpu_alpha=g.alpha,
+                                o_codes=e.codes, o_s8=e.s8, o_z8=e.z8, o_alpha=e.alpha)
+            say(f"[dump] wrote {path}")
+
+        assert_planes_equal(gpu, enc, f"{w.name} kv={kv} slice={key}", dump=dump)
     return ek, ev, HK, HV
 
 

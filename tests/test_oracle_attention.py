@@ -48,33 +48,33 @@ def _slice_inputs(d, L, N, seed, sig=(0.3, 0.2, 0.1)):
 def test_fused_equals_dense(mode, d, L):
     N = 150
     p = O.Params(d=d, mode=mode)
-    HK = O.rotation_matrix(d, _signs(d, 1))
-    HV = O.rotation_matrix(d, _signs(d, 2))
+    SK = _signs(d, 1)
+    SV = _signs(d, 2)
     xk = _slice_inputs(d, L, N, 10 + d)
     xv = _slice_inputs(d, L, N, 20 + d)
-    ek, ev = O.encode_slice(p, xk, HK), O.encode_slice(p, xv, HV)
+    ek, ev = O.encode_slice(p, xk, SK), O.encode_slice(p, xv, SV)
     rng = np.random.default_rng(3)
     for loop in range(L):
         q = O.bf16_encode(rng.standard_normal(d))
         for n in (N, 37, 1):
-            a = O.attention_slice(p, ek, ev, HK, HV, q, loop, n, 1 / np.sqrt(d), fused=False)
-            b = O.attention_slice(p, ek, ev, HK, HV, q, loop, n, 1 / np.sqrt(d), fused=True)
+            a = O.attention_slice(p, ek, ev, SK, SV, q, loop, n, 1 / np.sqrt(d), fused=False)
+            b = O.attention_slice(p, ek, ev, SK, SV, q, loop, n, 1 / np.sqrt(d), fused=True)
             assert np.allclose(a, b, rtol=1e-11, atol=1e-12), (loop, n)
 
 
 def test_dense_slice_is_softmax_over_reconstruction():
     d, L, N = 64, 4, 256
     p = O.Params(d=d)
-    HK = O.rotation_matrix(d, _signs(d, 5))
-    HV = O.rotation_matrix(d, _signs(d, 6))
-    ek = O.encode_slice(p, _slice_inputs(d, L, N, 50), HK)
-    ev = O.encode_slice(p, _slice_inputs(d, L, N, 51), HV)
+    SK = _signs(d, 5)
+    SV = _signs(d, 6)
+    ek = O.encode_slice(p, _slice_inputs(d, L, N, 50), SK)
+    ev = O.encode_slice(p, _slice_inputs(d, L, N, 51), SV)
     q = O.bf16_encode(np.random.default_rng(4).standard_normal(d))
     for loop in range(L):
-        K = O.reconstruct_slice(p, ek, HK, loop)
-        V = O.reconstruct_slice(p, ev, HV, loop)
+        K = O.reconstruct_slice(p, ek, SK, loop)
+        V = O.reconstruct_slice(p, ev, SV, loop)
         ref = _textbook(O.bf16_decode(q), K, V, 0.125)
-        out = O.attention_slice(p, ek, ev, HK, HV, q, loop, N, 0.125)
+        out = O.attention_slice(p, ek, ev, SK, SV, q, loop, N, 0.125)
         assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
 
 
@@ -96,13 +96,13 @@ def test_zero_residual_reduces_to_textbook_attention_on_raw_states():
         raw.append(a)
     xk = O.bf16_encode(np.broadcast_to(raw[0], (4, N, d)).copy())
     xv = O.bf16_encode(np.broadcast_to(raw[1], (4, N, d)).copy())
-    HK = O.rotation_matrix(d, _signs(d, 13))
-    HV = O.rotation_matrix(d, _signs(d, 14))
-    ek, ev = O.encode_slice(p, xk, HK), O.encode_slice(p, xv, HV)
+    SK = _signs(d, 13)
+    SV = _signs(d, 14)
+    ek, ev = O.encode_slice(p, xk, SK), O.encode_slice(p, xv, SV)
     assert np.all(ek.alpha == 0) and np.all(ek.s8[:3] == 0)
     q = O.bf16_encode(rng.standard_normal(d))
     ref = _textbook(O.bf16_decode(q), raw[0], raw[1], 0.125)
     for loop in range(4):
         for fused in (False, True):
-            out = O.attention_slice(p, ek, ev, HK, HV, q, loop, N, 0.125, fused=fused)
+            out = O.attention_slice(p, ek, ev, SK, SV, q, loop, N, 0.125, fused=fused)
             assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)

@@ -36,9 +36,9 @@ def _y_hat(p, codes, s8, z8, j):
 @pytest.mark.parametrize("d", [64, 96, 128])
 def test_anchor_is_last_loop_and_unrotated(d):
     p = O.Params(d=d)
-    H = O.rotation_matrix(d, _signs(d, 1))
+    S = _signs(d, 1)
     x = _group_inputs(d, 4, 100 + d)
-    codes, s8, z8, alpha = O.encode_group(p, x, H)
+    codes, s8, z8, alpha = O.encode_group(p, x, S)
     c2, s2, z2 = np.zeros(d, np.uint8), np.zeros(d // 16, np.uint8), np.zeros(d // 16, np.uint8)
     for gi in range(d // 16):
         s2[gi], z2[gi], c2[gi * 16:(gi + 1) * 16] = O.quant_group(x[3, gi * 16:(gi + 1) * 16], 4)
@@ -57,7 +57,7 @@ def test_residual_is_rotated_difference_to_dequantized_anchor(d):
     n_checked = 0
     for seed in range(40):
         x = _group_inputs(d, 4, 200 + seed)
-        codes, s8, z8, alpha = O.encode_group(p, x, H)
+        codes, s8, z8, alpha = O.encode_group(p, x, s)
         A = O.dequant_vector(codes[3], s8[3], z8[3], 16)
         for j in range(3):
             y = Hs @ (x[j] - A)
@@ -82,7 +82,7 @@ def test_alpha_is_least_squares_and_bf16_rounded():
     H = O.rotation_matrix(d, s)
     for seed in range(60):
         x = _group_inputs(d, 4, 300 + seed)
-        codes, s8, z8, alpha = O.encode_group(p, x, H)
+        codes, s8, z8, alpha = O.encode_group(p, x, s)
         A = O.dequant_vector(codes[3], s8[3], z8[3], 16)
         for j in range(3):
             y = Hs @ (x[j] - A)
@@ -120,9 +120,9 @@ def test_single_channel_residual_recovers_through_transpose():
         x = np.tile(anchor, (4, 1))
         delta = 0.5
         x[1, k] += delta
-        codes, s8, z8, alpha = O.encode_group(p, x, H)
+        codes, s8, z8, alpha = O.encode_group(p, x, s)
         assert np.array_equal(O.dequant_vector(codes[3], s8[3], z8[3], 16), anchor)
-        xh = O.reconstruct_group(p, codes, s8, z8, alpha, H, 1)
+        xh = O.reconstruct_group(p, codes, s8, z8, alpha, s, 1)
         r = np.zeros(d)
         r[k] = delta
         # y = +-delta/8 in every entry: two grid levels per group, so only the fp8
@@ -132,7 +132,7 @@ def test_single_channel_residual_recovers_through_transpose():
         assert np.abs(wrong - x[1]).max() > 0.5 * delta
         # the untouched loops reconstruct to the anchor exactly (zero residual)
         for j in (0, 2):
-            assert np.array_equal(O.reconstruct_group(p, codes, s8, z8, alpha, H, j), anchor)
+            assert np.array_equal(O.reconstruct_group(p, codes, s8, z8, alpha, s, j), anchor)
 
 
 @pytest.mark.parametrize("d", [64, 96, 128])
@@ -144,10 +144,10 @@ def test_reconstruction_error_bound(d):
     H = O.rotation_matrix(d, s)
     for seed in range(30):
         x = _group_inputs(d, 4, 600 + seed)
-        codes, s8, z8, alpha = O.encode_group(p, x, H)
+        codes, s8, z8, alpha = O.encode_group(p, x, s)
         A = O.dequant_vector(codes[3], s8[3], z8[3], 16)
         for j in range(3):
-            xh = O.reconstruct_group(p, codes, s8, z8, alpha, H, j)
+            xh = O.reconstruct_group(p, codes, s8, z8, alpha, s, j)
             y = H @ (x[j] - A)
             yh = _y_hat(p, codes, s8, z8, j)
             assert np.linalg.norm(x[j] - xh) <= np.linalg.norm(y - yh) + 1e-12
@@ -158,12 +158,12 @@ def test_two_read_identity():
     """Reconstructing loop l reads only the anchor and loop l's own planes."""
     d = 128
     p = O.Params(d=d)
-    H = O.rotation_matrix(d, _signs(d, 7))
+    S = _signs(d, 7)
     x = _group_inputs(d, 4, 700)
-    codes, s8, z8, alpha = O.encode_group(p, x, H)
+    codes, s8, z8, alpha = O.encode_group(p, x, S)
     rng = np.random.default_rng(8)
     for j in range(4):
-        ref = O.reconstruct_group(p, codes, s8, z8, alpha, H, j)
+        ref = O.reconstruct_group(p, codes, s8, z8, alpha, S, j)
         c2, s2, z2, a2 = codes.copy(), s8.copy(), z8.copy(), alpha.copy()
         for o in range(4):
             if o in (j, 3):
@@ -172,14 +172,14 @@ def test_two_read_identity():
             s2[o] = rng.integers(0, 0x70, d // 16)
             z2[o] = rng.integers(0, 0xFF, d // 16)
             a2[o] = rng.integers(0, 0x7F00)
-        assert np.array_equal(O.reconstruct_group(p, c2, s2, z2, a2, H, j), ref)
+        assert np.array_equal(O.reconstruct_group(p, c2, s2, z2, a2, S, j), ref)
 
 
 def test_direct_mode_quantizes_each_loop_alone():
     d = 64
     p = O.Params(d=d, mode=O.MODE_DIRECT)
     x = _group_inputs(d, 4, 900)
-    codes, s8, z8, alpha = O.encode_group(p, x, np.eye(d))
+    codes, s8, z8, alpha = O.encode_group(p, x, None)
     for j in range(4):
         bits = 4 if j == 3 else 2
         for gi in range(d // 16):
@@ -198,7 +198,7 @@ def test_alpha_variants():
     x = _group_inputs(d, 4, 950)
     for mode in (O.ALPHA_NORM_RATIO, O.ALPHA_ONE):
         p = O.Params(d=d, alpha_mode=mode)
-        codes, s8, z8, alpha = O.encode_group(p, x, H)
+        codes, s8, z8, alpha = O.encode_group(p, x, s)
         A = O.dequant_vector(codes[3], s8[3], z8[3], 16)
         for j in range(3):
             y = H @ (x[j] - A)
@@ -211,7 +211,7 @@ def test_rotation_off_quantizes_plain_difference():
     d = 64
     p = O.Params(d=d, rotate=0)
     x = _group_inputs(d, 4, 960)
-    codes, s8, z8, alpha = O.encode_group(p, x, np.eye(d) * 7.0)  # H must be ignored
+    codes, s8, z8, alpha = O.encode_group(p, x, np.full(d, -1, np.int8))  # signs ignored
     A = O.dequant_vector(codes[3], s8[3], z8[3], 16)
     for j in range(3):
         r = x[j] - A
@@ -223,19 +223,19 @@ def test_rotation_off_quantizes_plain_difference():
 def test_encode_slice_matches_groups():
     d, L, N = 64, 8, 5
     p = O.Params(d=d)
-    H = O.rotation_matrix(d, _signs(d, 10))
+    S = _signs(d, 10)
     rng = np.random.default_rng(11)
     xs = O.bf16_encode(rng.standard_normal((L, N, d)))
-    e = O.encode_slice(p, xs, H)
+    e = O.encode_slice(p, xs, S)
     for k in range(2):
         for t in range(N):
             xg = O.bf16_decode(xs[4 * k:4 * k + 4, t])
-            c, s8, z8, a = O.encode_group(p, xg, H)
+            c, s8, z8, a = O.encode_group(p, xg, S)
             assert np.array_equal(e.codes[4 * k:4 * k + 4, t], c)
             assert np.array_equal(e.s8[4 * k:4 * k + 4, t], s8)
             assert np.array_equal(e.z8[4 * k:4 * k + 4, t], z8)
             assert np.array_equal(e.alpha[4 * k:4 * k + 4, t], a)
             for j in range(4):
                 assert np.array_equal(
-                    O.reconstruct_slice(p, e, H, 4 * k + j, t, t + 1)[0],
-                    O.reconstruct_group(p, c, s8, z8, a, H, j))
+                    O.reconstruct_slice(p, e, S, 4 * k + j, t, t + 1)[0],
+                    O.reconstruct_group(p, c, s8, z8, a, S, j))

@@ -52,3 +52,27 @@ def test_columns_are_signed_hadamard_columns():
         e = np.zeros(d)
         e[j] = 1
         assert np.allclose(H @ e, s[j] * W[:, j] / np.sqrt(d), atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("d", [2, 16, 64, 96, 128])
+def test_rotate_applies_H_and_its_transpose(d):
+    s = _signs(d, 40 + d)
+    H = O.rotation_matrix(d, s)
+    rng = np.random.default_rng(d)
+    for _ in range(5):
+        r = rng.standard_normal(d)
+        assert np.allclose(O.rotate(d, s, r), H @ r, rtol=0, atol=1e-14)
+        assert np.allclose(O.rotate_t(d, s, r), H.T @ r, rtol=0, atol=1e-14)
+        assert np.allclose(O.rotate_t(d, s, O.rotate(d, s, r)), r, rtol=0, atol=1e-14)
+
+
+def test_rotate_keeps_exact_cancellation_exact():
+    """Signed inputs whose Walsh-Hadamard sum cancels give an exact zero (the
+    +-1 sums are exact for short dyadic inputs; only the final scale rounds)."""
+    d = 128
+    s = np.ones(d, np.int8)
+    r = np.zeros(d)
+    r[0], r[1] = 0.375, -0.375          # row i of S sums to r0 + (-1)^{i&1} r1
+    y = O.rotate(d, s, r)
+    assert np.all(y[0::2] == 0.0)
+    assert np.all(np.abs(y[1::2]) == np.float64(0.75) * (1 / np.sqrt(128.0)))
