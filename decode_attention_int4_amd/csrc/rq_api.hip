@@ -14,12 +14,13 @@ namespace rq {
 int decode_tile_tokens(int d);
 int bf16_tile_tokens();
 
-// Split-K planning.  The decode kernels run 4 waves per workgroup; a launch
-// needs well over 256 workgroups to occupy the 256 CUs, so small batch*heads
-// products are split along the tokens.  Splits never shrink below two tiles.
-// The result is non-decreasing in n_tokens, so a workspace sized for n serves
-// any smaller n.
-static constexpr int32_t kTargetBlocks = 1024;
+// Split-K planning.  The decode kernels run 4 waves per workgroup and keep two
+// workgroups resident per CU, so 512 workgroups occupy the 256 CUs once;
+// small batch*heads products are split along the tokens to reach that, and
+// longer splits amortize each workgroup's query setup and merge.  Splits never
+// shrink below two tiles.  The result is non-decreasing in n_tokens, so a
+// workspace sized for n serves any smaller n.
+static constexpr int32_t kTargetBlocks = 512;
 
 SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile) {
   SplitPlan p{1, tile};
@@ -171,7 +172,7 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, i
   if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
   const int32_t bh = desc->batch * q_heads;
   const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim));
-  return rq::align_up(4ull * bh, 256) + (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull;
+  return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
 rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
@@ -185,12 +186,13 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
     return RQ_ERR_INVALID_ARG;
   if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
   if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
-  if (!cache || !q_bf16 || !workspace || !out || (needs_signs(desc) && !signs))
+  const uint64_t need = rq_decode_workspace_bytes(desc, q_heads, n_tokens);
+  if (!cache || !q_bf16 || !out || (needs_signs(desc) && !signs) || (need && !workspace))
     return RQ_ERR_INVALID_ARG;
   if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q_bf16, 4) || !aligned(out, 4))
     return RQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
-  if (workspace_bytes < rq_decode_workspace_bytes(desc, q_heads, n_tokens)) return RQ_ERR_WORKSPACE;
+  if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
   const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim));
   rq::DecodeArgs a{};
@@ -199,8 +201,7 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   a.signs = signs;
   a.q = q_bf16;
   a.out = out;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rq::align_up(4ull * bh, 256));
+  a.partials = static_cast<float*>(workspace);
   a.loop = loop;
   a.layer = layer;
   a.q_heads = q_heads;
@@ -217,7 +218,7 @@ uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_hea
   if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
   const int32_t bh = desc->batch * q_heads;
   const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::bf16_tile_tokens());
-  return rq::align_up(4ull * bh, 256) + (uint64_t)bh * s * (2 + desc->head_dim) * 4ull;
+  return s > 1 ? (uint64_t)bh * s * (2 + desc->head_dim) * 4ull : 0;
 }
 
 rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_cache,
@@ -232,11 +233,12 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
     return RQ_ERR_INVALID_ARG;
   if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
   if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
-  if (!k_cache || !v_cache || !q_bf16 || !workspace || !out) return RQ_ERR_INVALID_ARG;
+  const uint64_t need = rq_bf16_decode_workspace_bytes(desc, q_heads, n_tokens);
+  if (!k_cache || !v_cache || !q_bf16 || !out || (need && !workspace)) return RQ_ERR_INVALID_ARG;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 256) ||
       !aligned(q_bf16, 4) || !aligned(out, 4))
     return RQ_ERR_ALIGNMENT;
-  if (workspace_bytes < rq_bf16_decode_workspace_bytes(desc, q_heads, n_tokens)) return RQ_ERR_WORKSPACE;
+  if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
   const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens());
   rq::Bf16DecodeArgs a{};
@@ -250,8 +252,7 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
   a.v = v_cache;
   a.q = q_bf16;
   a.out = out;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rq::align_up(4ull * bh, 256));
+  a.partials = static_cast<float*>(workspace);
   a.loop = loop;
   a.layer = layer;
   a.q_heads = q_heads;

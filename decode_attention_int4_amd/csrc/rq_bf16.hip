@@ -2,7 +2,8 @@
 // baseline the packed path is compared against (ai4snews summary, paragraph 4,
 // compares against BF16 attention).  Same decomposition as rq_decode.hip:
 // 4 lanes per token, each lane owning d/4 contiguous elements (16-byte loads),
-// per-slot online softmax, shuffle + LDS merges, last-workgroup split merge.
+// per-slot online softmax, shuffle + LDS merges, and a combine kernel for the
+// splits.
 #include <hip/hip_runtime.h>
 
 #include "rq_device.h"
@@ -22,7 +23,6 @@ __global__ void __launch_bounds__(NW * 64) bf16_decode_kernel(Bf16DecodeArgs a) 
   constexpr int W = E / 8;       // uint4 loads per lane per token
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
-  __shared__ int sm_last;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -46,24 +46,28 @@ __global__ void __launch_bounds__(NW * 64) bf16_decode_kernel(Bf16DecodeArgs a) 
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(a.n_tokens, t_begin + a.tokens_per_split);
 
+  // Slots past the end of the range load the range's last token (finite data)
+  // and are masked out with p = 0.
   uint4 ck[W], cv[W], nk[W], nv[W];
   int base = t_begin + w * TPW;
   bool cur_ok = base + slot < t_end;
-  if (cur_ok) {
+  if (base < t_end) {
+    const int t = min(base + slot, t_end - 1);
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      ck[i] = reinterpret_cast<const uint4*>(kp + (uint64_t)(base + slot) * D)[i];
-      cv[i] = reinterpret_cast<const uint4*>(vp + (uint64_t)(base + slot) * D)[i];
+      ck[i] = reinterpret_cast<const uint4*>(kp + (uint64_t)t * D)[i];
+      cv[i] = reinterpret_cast<const uint4*>(vp + (uint64_t)t * D)[i];
     }
   }
   for (; base < t_end; base += NW * TPW) {
     const int nb = base + NW * TPW;
     const bool nxt_ok = nb + slot < t_end;
-    if (nxt_ok) {
+    if (nb < t_end) {
+      const int t = min(nb + slot, t_end - 1);
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        nk[i] = reinterpret_cast<const uint4*>(kp + (uint64_t)(nb + slot) * D)[i];
-        nv[i] = reinterpret_cast<const uint4*>(vp + (uint64_t)(nb + slot) * D)[i];
+        nk[i] = reinterpret_cast<const uint4*>(kp + (uint64_t)t * D)[i];
+        nv[i] = reinterpret_cast<const uint4*>(vp + (uint64_t)t * D)[i];
       }
     }
     float dot = 0.f;
@@ -124,53 +128,53 @@ __global__ void __launch_bounds__(NW * 64) bf16_decode_kernel(Bf16DecodeArgs a) 
     }
   }
   __syncthreads();
+  float M = sm_m[0];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww]);
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) L += sm_l[ww] * exp2f(sm_m[ww] - M);
+  float A = 0.f;
+  if (tid < D) {
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) A += sm_acc[ww][tid] * exp2f(sm_m[ww] - M);
+  }
+  if (a.splits == 1) {
+    if (tid < D) a.out[(uint64_t)bh * D + tid] = L > 0.f ? A / L : 0.f;
+    return;
+  }
+  // partial state for the combine kernel (ordered by the kernel boundary)
   float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + D);
-  {
-    float M = sm_m[0];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww]);
-    if (tid < D) {
-      float s = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) s += sm_acc[ww][tid] * exp2f(sm_m[ww] - M);
-      mine[2 + tid] = s;
-    }
-    if (tid == 0) {
-      float L = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) L += sm_l[ww] * exp2f(sm_m[ww] - M);
-      mine[0] = M;
-      mine[1] = L;
-    }
-  }
-  __threadfence();
-  __syncthreads();
+  if (tid < D) mine[2 + tid] = A;
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[bh], 1u);
-    sm_last = (prev == (uint32_t)(a.splits - 1));
-    __threadfence();
+    mine[0] = M;
+    mine[1] = L;
   }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
+}
+
+template <int D>
+__global__ void __launch_bounds__(128) bf16_combine_kernel(Bf16DecodeArgs a) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const float* all = a.partials + (uint64_t)bh * a.splits * (2 + D);
-  float M = kEmpty;
-  for (int s = 0; s < a.splits; ++s)
-    M = fmaxf(M, __hip_atomic_load(all + (uint64_t)s * (2 + D), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  float L = 0.f, A = 0.f;
+  float M = kEmpty, L = 0.f, A = 0.f;
   for (int s = 0; s < a.splits; ++s) {
     const float* ps = all + (uint64_t)s * (2 + D);
-    const float f = exp2f(__hip_atomic_load(ps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-    L += f * __hip_atomic_load(ps + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < D) A += f * __hip_atomic_load(ps + 2 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float ms = ps[0];
+    const float Mn = fmaxf(M, ms);
+    const float fo = exp2f(M - Mn), fs = exp2f(ms - Mn);
+    L = L * fo + ps[1] * fs;
+    if (tid < D) A = A * fo + ps[2 + tid] * fs;
+    M = Mn;
   }
   if (tid < D) a.out[(uint64_t)bh * D + tid] = L > 0.f ? A / L : 0.f;
-  if (tid == 0) a.counters[bh] = 0u;
 }
 
 template <int D>
 hipError_t launch_t(const Bf16DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bf16_decode_kernel<D>), dim3(a.splits, a.batch * a.q_heads), dim3(NW * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL((bf16_combine_kernel<D>), dim3(a.batch * a.q_heads), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

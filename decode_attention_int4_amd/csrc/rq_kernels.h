@@ -29,14 +29,14 @@ struct ReconArgs {
 };
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 
-// Split-K decode: partial states live in the workspace after the counters.
+// Split-K decode: with more than one split, partial states live in the
+// workspace and a combine kernel merges them.
 struct DecodeArgs {
   Geometry g;
   const uint8_t* cache;
   const int8_t* signs;
   const uint16_t* q;      // [B][Hq][d]
   float* out;             // [B][Hq][d]
-  uint32_t* counters;     // [B*Hq]
   float* partials;        // [B*Hq][splits][2 + 2d]
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;
@@ -50,7 +50,6 @@ struct Bf16DecodeArgs {
   const uint16_t* v;
   const uint16_t* q;
   float* out;
-  uint32_t* counters;
   float* partials;        // [B*Hq][splits][2 + d]
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;

@@ -168,8 +168,8 @@ def alloc_cache(desc: CacheDesc, device="cuda") -> torch.Tensor:
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the split counters must start at zero)."""
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """Workspace for split-K partial states (no initialization needed)."""
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- device calls

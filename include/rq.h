@@ -170,10 +170,10 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
  * term.  Query head h reads kv head h / (q_heads / kv_heads).
  *   q_bf16     device BF16 [batch][q_heads][d], contiguous, 4-byte aligned
  *   workspace  device, >= rq_decode_workspace_bytes(desc, q_heads, n_tokens),
- *              256-byte aligned.  Its first 4*batch*q_heads bytes are
- *              counters that must be ZERO before the first call (e.g. a
- *              zero-filled allocation); every completed call leaves them zero.
- *              Calls that share a workspace must not run concurrently.
+ *              256-byte aligned (may be NULL when that size is 0).  Holds the
+ *              split-K partial states between the decode kernel and the
+ *              combine kernel; needs no initialization.  Calls that share a
+ *              workspace must be ordered (same stream), not concurrent.
  *   out        device fp32 [batch][q_heads][d]; n_tokens == 0 writes zeros.
  * Errors: RQ_ERR_UNSUPPORTED when q_heads is not a multiple of kv_heads;
  * RQ_ERR_CAPACITY when n_tokens > max_tokens; RQ_ERR_WORKSPACE.

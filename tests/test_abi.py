@@ -118,7 +118,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rq_decode_attention(D, FAKE, FAKE, 0, 1, FAKE, 2, 10, f, FAKE, ws, FAKE, None) == 1
     assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 3, 10, f, FAKE, ws, FAKE, None) == 2
     assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 257, f, FAKE, ws, FAKE, None) == 3
-    assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, FAKE, 16, FAKE, None) == 4
+    big = rq.make_desc(1, 4, 1, 2, 8192, 64)
+    need = rq.decode_workspace_bytes(big, 2, 8192)
+    assert need > 0
+    assert L.rq_decode_attention(ctypes.byref(big), FAKE, FAKE, 0, 0, FAKE, 2, 8192, f, FAKE,
+                                 need - 4, FAKE, None) == 4
+    assert L.rq_decode_attention(ctypes.byref(big), FAKE, FAKE, 0, 0, FAKE, 2, 8192, f, None,
+                                 need, FAKE, None) == 1
     assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, MISALIGNED, ws, FAKE,
                                  None) == 5
     assert L.rq_decode_attention(D, FAKE, None, 0, 0, FAKE, 2, 256, f, FAKE, ws, FAKE, None) == 1
@@ -128,8 +134,10 @@ def test_entry_points_reject_bad_arguments_before_launch():
     wb = rq.bf16_decode_workspace_bytes(d, 2, 256)
     assert L.rq_bf16_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 300, f, FAKE, wb, FAKE,
                                       None) == 3
-    assert L.rq_bf16_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, f, FAKE, 8, FAKE,
-                                      None) == 4
+    wbig = rq.bf16_decode_workspace_bytes(big, 2, 8192)
+    assert wbig > 0
+    assert L.rq_bf16_decode_attention(ctypes.byref(big), FAKE, FAKE, 0, 0, FAKE, 2, 8192, f, FAKE,
+                                      8, FAKE, None) == 4
     # probe
     assert L.rq_read_probe(FAKE, 12, FAKE, None) == 1
     assert L.rq_read_probe(MISALIGNED, 16, FAKE, None) == 5
@@ -141,7 +149,7 @@ def test_workspace_bound_is_monotone():
             prev = 0
             for n in [0, 1, 63, 64, 65, 500, 4096, 8192, 16384]:
                 w = rq.decode_workspace_bytes(d, hq, n)
-                assert w >= prev and w >= 256
+                assert w >= prev
                 prev = w
 
 

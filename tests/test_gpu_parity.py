@@ -93,11 +93,23 @@ def test_tiny_step_and_append(tiny):
                 assert np.array_equal(getattr(g, name), getattr(e, name)), name
 
 
-def test_workspace_counters_return_to_zero(tiny):
-    w, run, _ = tiny
-    torch.cuda.synchronize()
-    nbh = w.batch * w.q_heads
-    assert torch.all(run.ws[:4 * nbh] == 0)
+def test_workspace_needs_no_initialization():
+    """A NaN-filled workspace and a NaN-filled output do not leak into results
+    (several splits, so the combine kernel reads what the decode kernel wrote)."""
+    w = Workload("ws_poison", batch=2, loops=4, layers=1, kv_heads=2, q_heads=2, head_dim=128,
+                 n_tokens=4000, seed=5)
+    keep = [(1, 0, 1)]
+    run = RQDecode(w, keep=keep)
+    need = rq.decode_workspace_bytes(run.desc, w.q_heads, run.N)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
+    out = torch.full((2, 2, 128), float("nan"), device="cuda")
+    ek, ev, HK, HV = encode_kept(w, run.kept[keep[0]], 0)
+    for loop in range(4):
+        rq.decode_attention(run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], run.N,
+                            w.softmax_scale, ws, out=out)
+        ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, 0, 1, 1]), loop, run.N)
+        assert_close_attention(out[1, 1].cpu().numpy(), ref, f"poisoned workspace loop {loop}")
 
 
 def test_bf16_baseline_tiny():
