@@ -37,6 +37,8 @@
 #include "rq_device.h"
 #include "rq_kernels.h"
 
+#include <type_traits>
+
 namespace rq {
 namespace {
 
@@ -366,7 +368,7 @@ struct Stage {
   }
   static constexpr int N_DMA = 2 * (dma_of(C1, R1) + dma_of(SZ, RS)) +
                                (B2 ? 2 * (dma_of(C2, R2) + dma_of(SZ, RS) + 1) : 0);
-  static constexpr int COUNT = (D != 96 && 3 * N_DMA < 64) ? 4 : 3;  // ring depth
+  static constexpr int COUNT = 3;  // ring depth
   static_assert((COUNT - 1) * N_DMA < 64, "pending DMA count must fit vmcnt");
 };
 
@@ -376,32 +378,36 @@ struct Stage {
 // or beyond `valid` (the bytes of the tile's in-range tokens) are redirected
 // to the last valid granule, so nothing past the range is read and every value
 // stays finite.
-template <int BYTES, int ROW>
+template <int BYTES, int ROW, bool CLAMP>
 __device__ __forceinline__ void dma_piece(const uint8_t* src, int valid, lds_u8* dst, int lane) {
   constexpr int KB = (ROW % 16 == 0) ? BYTES / 1024 : 0;
   constexpr int REST = BYTES - KB * 1024;
   constexpr int FULL = REST / 256, REM = REST % 256;
 #pragma unroll
-  for (int c = 0; c < KB; ++c)
-    __builtin_amdgcn_global_load_lds(src + min(c * 1024 + lane * 16, valid - 16), dst + c * 1024, 16, 0, 0);
-  const int last = valid - 4;
+  for (int c = 0; c < KB; ++c) {
+    const int o = c * 1024 + lane * 16;
+    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(o, valid - 16) : o), dst + c * 1024, 16, 0, 0);
+  }
 #pragma unroll
   for (int c = 0; c < FULL; ++c) {
     const int o = KB * 1024 + c * 256;
-    __builtin_amdgcn_global_load_lds(src + min(o + lane * 4, last), dst + o, 4, 0, 0);
+    const int ol = o + lane * 4;
+    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(ol, valid - 4) : ol), dst + o, 4, 0, 0);
   }
   if constexpr (REM != 0) {
     const int o = KB * 1024 + FULL * 256;
-    if (lane < REM / 4) __builtin_amdgcn_global_load_lds(src + min(o + lane * 4, last), dst + o, 4, 0, 0);
+    const int ol = o + lane * 4;
+    if (lane < REM / 4)
+      __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(ol, valid - 4) : ol), dst + o, 4, 0, 0);
   }
 }
 
 // Same for a BF16 alpha piece (2 bytes per token), one ushort DMA; as for
 // every sub-dword DMA, lane l lands at dst + 4*l.
-template <int TOKENS>
+template <int TOKENS, bool CLAMP>
 __device__ __forceinline__ void dma_alpha(const uint8_t* src, int valid, lds_u8* dst, int lane) {
   if (lane < TOKENS)
-    __builtin_amdgcn_global_load_lds(src + min(lane * 2, valid - 2), dst, 2, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(lane * 2, valid - 2) : lane * 2), dst, 2, 0, 0);
 }
 
 // s_waitcnt that waits until at most n vector-memory operations are pending.
@@ -524,6 +530,55 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
   uint32_t magic;
   asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
 
+  const int t_begin = split * a.tokens_per_split;
+  const int t_end = min(a.n_tokens, t_begin + a.tokens_per_split);
+  // ---- plane bases
+  const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
+  const uint8_t* k1 = a.cache + g.slot_offset(0, b, a.layer, loop1, kvh);
+  const uint8_t* v1 = a.cache + g.slot_offset(1, b, a.layer, loop1, kvh);
+  const uint8_t* k1s = k1 + g.sz_rel(loop1);
+  const uint8_t* v1s = v1 + g.sz_rel(loop1);
+  const uint8_t* k2 = a.cache + g.slot_offset(0, b, a.layer, a.loop, kvh);
+  const uint8_t* v2 = a.cache + g.slot_offset(1, b, a.layer, a.loop, kvh);
+  const uint8_t* k2s = k2 + g.sz_rel(a.loop);
+  const uint8_t* v2s = v2 + g.sz_rel(a.loop);
+  const uint16_t* k2a = reinterpret_cast<const uint16_t*>(k2 + g.alpha_rel(a.loop));
+  const uint16_t* v2a = reinterpret_cast<const uint16_t*>(v2 + g.alpha_rel(a.loop));
+
+
+  // ---- stream this wave's tiles through its LDS ring
+  lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
+  const int first = t_begin + w * TPW;
+  const int n_tiles = first < t_end ? (t_end - first + NW * TPW - 1) / (NW * TPW) : 0;
+  auto issue_t = [&](auto clamp, int tb, lds_u8* st, int vt) {
+    constexpr bool C = decltype(clamp)::value;
+    dma_piece<ST::C1, ST::R1, C>(k1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
+    dma_piece<ST::SZ, ST::RS, C>(k1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
+    dma_piece<ST::C1, ST::R1, C>(v1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
+    dma_piece<ST::SZ, ST::RS, C>(v1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
+    if constexpr (TWO) {
+      dma_piece<ST::C2, ST::R2, C>(k2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::k2c, lane);
+      dma_piece<ST::SZ, ST::RS, C>(k2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k2s, lane);
+      dma_piece<ST::C2, ST::R2, C>(v2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::v2c, lane);
+      dma_piece<ST::SZ, ST::RS, C>(v2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v2s, lane);
+      dma_alpha<TPW, C>(reinterpret_cast<const uint8_t*>(k2a + tb), vt * 2, st + ST::ka, lane);
+      dma_alpha<TPW, C>(reinterpret_cast<const uint8_t*>(v2a + tb), vt * 2, st + ST::va, lane);
+    }
+  };
+  auto issue = [&](int tile) {
+    const int tb = first + tile * NW * TPW;
+    lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
+    const int vt = t_end - tb;  // in-range tokens of this tile (>= 1)
+    if (vt >= TPW)
+      issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
+    else
+      issue_t(std::integral_constant<bool, true>{}, tb, st, vt);
+  };
+#pragma unroll
+  for (int i = 0; i < ST::COUNT - 1; ++i)
+    if (i < n_tiles) issue(i);
+
+
   // ---- query, u = H q and their fp16 prescales (wave 0)
   if (w == 0) {
     const bool v1ok = (D > 64) && (lane + 64 < D);
@@ -579,20 +634,6 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
   }
   const float ipq = 1.f / pq;
 
-  // ---- plane bases
-  const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
-  const uint8_t* k1 = a.cache + g.slot_offset(0, b, a.layer, loop1, kvh);
-  const uint8_t* v1 = a.cache + g.slot_offset(1, b, a.layer, loop1, kvh);
-  const uint8_t* k1s = k1 + g.sz_rel(loop1);
-  const uint8_t* v1s = v1 + g.sz_rel(loop1);
-  const uint8_t* k2 = a.cache + g.slot_offset(0, b, a.layer, a.loop, kvh);
-  const uint8_t* v2 = a.cache + g.slot_offset(1, b, a.layer, a.loop, kvh);
-  const uint8_t* k2s = k2 + g.sz_rel(a.loop);
-  const uint8_t* v2s = v2 + g.sz_rel(a.loop);
-  const uint16_t* k2a = reinterpret_cast<const uint16_t*>(k2 + g.alpha_rel(a.loop));
-  const uint16_t* v2a = reinterpret_cast<const uint16_t*>(v2 + g.alpha_rel(a.loop));
-
-
   float accA[E], accR[TWO ? E : 1], zA[GPL], zR[GPL];
 #pragma unroll
   for (int i = 0; i < E; ++i) accA[i] = 0.f;
@@ -603,33 +644,6 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
   float m = kEmpty, l = 0.f;
   const float qs = a.qscale;
 
-  const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(a.n_tokens, t_begin + a.tokens_per_split);
-
-  // ---- stream this wave's tiles through its LDS ring
-  lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
-  const int first = t_begin + w * TPW;
-  const int n_tiles = first < t_end ? (t_end - first + NW * TPW - 1) / (NW * TPW) : 0;
-  auto issue = [&](int tile) {
-    const int tb = first + tile * NW * TPW;
-    lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
-    const int vt = t_end - tb;  // in-range tokens of this tile (>= 1)
-    dma_piece<ST::C1, ST::R1>(k1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
-    dma_piece<ST::SZ, ST::RS>(k1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
-    dma_piece<ST::C1, ST::R1>(v1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
-    dma_piece<ST::SZ, ST::RS>(v1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
-    if constexpr (TWO) {
-      dma_piece<ST::C2, ST::R2>(k2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::k2c, lane);
-      dma_piece<ST::SZ, ST::RS>(k2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k2s, lane);
-      dma_piece<ST::C2, ST::R2>(v2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::v2c, lane);
-      dma_piece<ST::SZ, ST::RS>(v2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v2s, lane);
-      dma_alpha<TPW>(reinterpret_cast<const uint8_t*>(k2a + tb), vt * 2, st + ST::ka, lane);
-      dma_alpha<TPW>(reinterpret_cast<const uint8_t*>(v2a + tb), vt * 2, st + ST::va, lane);
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < ST::COUNT - 1; ++i)
-    if (i < n_tiles) issue(i);
 
   for (int it = 0; it < n_tiles; ++it) {
     if (it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
@@ -784,23 +798,38 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
 // sum and writes the fp32 output.
 template <int D, bool TWO>
 __global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+  constexpr int W = 2 + 2 * D;
+  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.splits;
   const bool v1ok = (D > 64) && (lane + 64 < D);
-  const float* all = a.partials + (uint64_t)bh * a.splits * (2 + 2 * D);
-  float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* ps = all + (uint64_t)s * (2 + 2 * D);
-    const float ms = ps[0];
-    const float Mn = fmaxf(M, ms);
-    const float fo = exp2f(M - Mn), fs = exp2f(ms - Mn);
-    L = L * fo + ps[1] * fs;
-    A0 = A0 * fo + ps[2 + lane] * fs;
-    if (v1ok) A1 = A1 * fo + ps[2 + lane + 64] * fs;
-    if constexpr (TWO) {
-      R0 = R0 * fo + ps[2 + D + lane] * fs;
-      if (v1ok) R1 = R1 * fo + ps[2 + D + lane + 64] * fs;
+  const float* all = a.partials + (uint64_t)bh * ns * W;
+  float M = kEmpty;
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, all[(uint64_t)(s0 + lane) * W]);
+  M = wave_max(M);
+  float L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
+  // eight splits per round: their loads are independent and issue together
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float ms[8], ls[8], a0[8], a1[8], r0[8], r1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sj = min(s0 + j, ns - 1);
+      const float* ps = all + (uint64_t)sj * W;
+      ms[j] = (s0 + j < ns) ? ps[0] : kEmpty;
+      ls[j] = ps[1];
+      a0[j] = ps[2 + lane];
+      a1[j] = v1ok ? ps[2 + lane + 64] : 0.f;
+      r0[j] = TWO ? ps[2 + D + lane] : 0.f;
+      r1[j] = (TWO && v1ok) ? ps[2 + D + lane + 64] : 0.f;
     }
-    M = Mn;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = exp2f(ms[j] - M);
+      L = fmaf(f, ls[j], L);
+      A0 = fmaf(f, a0[j], A0);
+      A1 = fmaf(f, a1[j], A1);
+      R0 = fmaf(f, r0[j], R0);
+      R1 = fmaf(f, r1[j], R1);
+    }
   }
   if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
     wave_wht<D>(R0, R1, lane);
