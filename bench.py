@@ -67,30 +67,42 @@ def time_steps(step, steps: int, torch):
 
 
 def dominant_kernel_ms(run, steps: int, torch):
-    """Average duration of the residual-loop decode-attention launch, bracketed
-    by events on the stream the kernel runs on, over `steps` full steps."""
+    """Average duration of one decode-attention call of the dominant kind (the
+    residual loops of a residual cache, the INT4 anchor loops of a direct one:
+    the decode kernel and its split-combine kernel), from events on the stream the kernels
+    run on.  Each run of consecutive residual calls in a step (different layers
+    and loops, so no call re-reads another's data) is bracketed by one event
+    pair, so event overhead is not charged to the calls."""
     stream = torch.cuda.current_stream()
     w = run.w
     P = w.loops_per_group
-    pairs = []
+    spans = []
     torch.cuda.synchronize()
     for _ in range(steps):
+        open_ev = None
+        count = 0
         for loop in range(w.loops):
+            dominant = (loop % P != P - 1) == (w.mode == 0)
+            if dominant and open_ev is None:
+                open_ev = torch.cuda.Event(enable_timing=True)
+                open_ev.record(stream)
+            if not dominant and open_ev is not None:
+                close = torch.cuda.Event(enable_timing=True)
+                close.record(stream)
+                spans.append((open_ev, close, count))
+                open_ev, count = None, 0
             for layer in range(w.layers):
-                dominant = (w.mode == 0 and loop % P != P - 1)
-                if dominant:
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    run.attend(loop, layer)
-                    b.record(stream)
-                    pairs.append((a, b))
-                else:
-                    run.attend(loop, layer)
+                run.attend(loop, layer)
+                count += dominant
+        if open_ev is not None:
+            close = torch.cuda.Event(enable_timing=True)
+            close.record(stream)
+            spans.append((open_ev, close, count))
         run.append_new()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in pairs]
-    return sum(ms) / len(ms), len(ms)
+    total = sum(a.elapsed_time(b) for a, b, _ in spans)
+    n = sum(c for _, _, c in spans)
+    return total / n, n
 
 
 def read_peak_gbps(torch, rq, nbytes=8 << 30, reps=5):
@@ -194,6 +206,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--calibrate-counters", action="store_true",
+                    help="only run a 1 GiB device copy and a 1 GiB read (known byte counts) "
+                         "to calibrate FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -207,6 +222,18 @@ def main():
     from decode_attention_int4_amd import rq
     from decode_attention_int4_amd.synth import WORKLOADS
     from decode_attention_int4_amd.workload import BF16Decode, RQDecode
+
+    if args.calibrate_counters:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        sink = torch.zeros(rq.read_probe_sink_words(), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)                       # reads and writes exactly 1 GiB
+        rq.read_probe(src, sink)             # reads exactly 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_bytes": n}), flush=True)
+        return
 
     w = WORKLOADS[args.config]
     log(f"[bench] {w}")
@@ -229,7 +256,10 @@ def main():
     dom_loop = 0 if w.mode == 0 else P - 1
     dom_bytes = run.call_bytes(dom_loop)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    log(f"[bench] residual-loop attention: {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
+    two = w.mode == 0
+    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0}> + "
+             f"combine_kernel<{w.head_dim},{str(two).lower()}>")
+    log(f"[bench] dominant call ({kname}): {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
         f"{achieved:.0f} GB/s")
 
     extra = {}
@@ -281,7 +311,7 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<128,4,2> (residual loop)",
+                     "traffic": traffic, "kernel": kname,
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 2)},
         "cpu_baseline": cpu,
