@@ -14,33 +14,33 @@ namespace rq {
 int decode_tile_tokens(int d);
 int bf16_tile_tokens();
 
-// Split-K planning.  The decode kernels run 4 waves per workgroup and keep two
-// workgroups resident per CU, so 512 workgroups occupy the 256 CUs once;
-// small batch*heads products are split along the tokens to reach that, and
-// longer splits amortize each workgroup's query setup and merge.  Splits never
-// shrink below two tiles.  The result is non-decreasing in n_tokens, so a
-// workspace sized for n serves any smaller n.
-static constexpr int32_t kTargetBlocks = 512;
+// Split-K planning.  Small batch*heads products are split along the tokens
+// until the grid fills the GPU once: the packed-cache decode kernels keep
+// three 4-wave workgroups resident per CU (768 on 256 CUs), the BF16 baseline
+// two (512).  Longer splits amortize each workgroup's query setup and merge,
+// so no more splits than that, and splits never shrink below two tiles.  The
+// result is non-decreasing in n_tokens, so a workspace sized for n serves any
+// smaller n.
+static constexpr int32_t kDecodeTarget = 768;
+static constexpr int32_t kBf16Target = 512;
 
-SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile) {
+static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
+  if (n_tokens <= 0 || bh <= 0) return 1;
+  const int32_t n_tiles = (n_tokens + tile - 1) / tile;
+  const int32_t splits = (target + bh - 1) / bh;
+  const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+  return splits < max_splits ? splits : max_splits;
+}
+
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
   SplitPlan p{1, tile};
   if (n_tokens <= 0 || bh <= 0) return p;
   const int32_t n_tiles = (n_tokens + tile - 1) / tile;
-  int32_t splits = (kTargetBlocks + bh - 1) / bh;
-  const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
-  if (splits > max_splits) splits = max_splits;
+  const int32_t splits = max_splits_bound(bh, n_tokens, tile, target);
   const int32_t tiles_per = (n_tiles + splits - 1) / splits;
   p.tokens_per_split = tiles_per * tile;
   p.splits = (n_tokens + p.tokens_per_split - 1) / p.tokens_per_split;
   return p;
-}
-
-static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile) {
-  if (n_tokens <= 0 || bh <= 0) return 1;
-  const int32_t n_tiles = (n_tokens + tile - 1) / tile;
-  int32_t splits = (kTargetBlocks + bh - 1) / bh;
-  const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
-  return splits < max_splits ? splits : max_splits;
 }
 
 }  // namespace rq
@@ -171,7 +171,8 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
   if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
   const int32_t bh = desc->batch * q_heads;
-  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim));
+  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim),
+                                         rq::kDecodeTarget);
   return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
@@ -194,7 +195,8 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
-  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim));
+  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim),
+                                                  rq::kDecodeTarget);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);
@@ -217,7 +219,7 @@ uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_hea
                                         int32_t max_n_tokens) {
   if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
   const int32_t bh = desc->batch * q_heads;
-  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::bf16_tile_tokens());
+  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::bf16_tile_tokens(), rq::kBf16Target);
   return s > 1 ? (uint64_t)bh * s * (2 + desc->head_dim) * 4ull : 0;
 }
 
@@ -240,7 +242,7 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
     return RQ_ERR_ALIGNMENT;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
-  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens());
+  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens(), rq::kBf16Target);
   rq::Bf16DecodeArgs a{};
   a.batch = desc->batch;
   a.loops = desc->loops;

@@ -11,25 +11,35 @@
 // the saved memory traffic).
 //
 // gfx950 mapping.
-//   grid (splits, batch * q_heads), 4 waves per workgroup.  LPT lanes share one
-//   token; each owns GPL consecutive groups of 16, i.e. a contiguous byte range
-//   of every plane, so a wave reads 64 lanes x 16 bytes of anchor codes per
-//   instruction, contiguous across lanes.
-//   Code unpacking never goes through per-element shifts: one v_and_or_b32
-//   drops two codes into the mantissas of an fp16 pair whose exponent encodes
-//   1024 (the "magic number" conversion), giving 1024 + m*c.  The query side
-//   consumes the pair with v_dot2_f32_f16 against (q_a, q_b)/m, the constant
-//   1024*sum(q)/m being subtracted once per group; the query is held in fp16
-//   after an exact power-of-two prescale (BF16 fits fp16's mantissa).  H q is
-//   not exact in fp16, so against the residual codes, and on the value side,
-//   the pair is first turned into the exact codes with one v_pk_fma_f16 and
-//   accumulated in fp32 with v_fma_mix_f32.  FP8 scale/offset bytes are
-//   decoded by v_cvt_pk_f32_fp8 (OCP e4m3fn on gfx950).
-//   Each lane slot keeps its own online-softmax state; the running maximum is
-//   only raised when a logit exceeds it by 8 (log2 units), so the rescale of
-//   the accumulators is rare.  Slots are merged with DPP row rotations and
-//   LDS.  With one split the workgroup's first wave applies H^T and writes the
-//   fp32 output; otherwise each workgroup stores its partial state and a small
+//   grid (splits, batch * q_heads), 4 waves per workgroup.  A wave takes its
+//   tokens in PAIRS (t, t+1); LPP lanes share a pair and each owns one
+//   quantization group (16 head_dim elements) of both tokens, so a lane's
+//   accumulators cover just 16 elements.
+//   Codes are never converted element by element: one v_and_or_b32 drops two
+//   codes into the mantissas of an fp16 pair whose exponent encodes 1024 (the
+//   "magic number" conversion), giving 1024 + m*c.
+//   * Keys: the pair holds two elements of ONE token and meets
+//     (q_a, q_b)/m in v_dot2_f32_f16; the constant 1024*sum(q)/m is
+//     subtracted once per group.  The query is exact in fp16 after a
+//     power-of-two prescale (BF16 fits fp16's mantissa); H q is not, so it is
+//     split into fp16 high and low parts and each meets the codes in a dot2.
+//   * Values: v_perm_b32 first interleaves the same 16-bit unit of the two
+//     tokens, so the pair holds ONE element of BOTH tokens and meets the fp16
+//     weight pair (p_t s_t, p_t' s_t') in v_dot2_f32_f16 -- one instruction
+//     per two multiply-adds.  The first plane's weights go in as an fp16 high
+//     and low part (two dot2s); the residual plane, a smaller term, uses one
+//     fp16 weight against codes centred on the middle code.  The magic
+//     constant is taken out per lane at the end from the running sum of the
+//     fp16 weights.
+//   FP8 scale/offset bytes are decoded by v_cvt_pk_f32_fp8 (OCP e4m3fn on
+//   gfx950).  Each wave streams its tiles through a private ring in LDS filled
+//   by buffer_load ... lds DMA with scalar offsets, so issuing a tile costs no
+//   vector instructions.
+//   Each lane keeps its own online-softmax state; the running maximum is only
+//   raised when a logit exceeds it by 8 (log2 units), so the rescale of the
+//   accumulators is rare.  Lanes are merged with DPP row rotations and LDS.
+//   With one split the workgroup's first wave applies H^T and writes the fp32
+//   output; otherwise each workgroup stores its partial state and a small
 //   combine kernel merges the splits (the kernel boundary orders the two, so
 //   no device-scope fences, which would write back L2, are needed).
 #include <hip/hip_runtime.h>
@@ -44,32 +54,35 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int NW = 4;              // waves per workgroup
 constexpr float kEmpty = -1e30f;   // running max of an empty stream (finite on purpose)
 constexpr float kLazy = 8.f;       // log2-domain headroom before the running max moves
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024, 1024)
+// Value weights enter fp16 scaled by these powers of two, so that
+// p (<= 2^8) times an FP8 scale (<= 448), times alpha for residuals, fits.
+constexpr float kWA = 1.f / 16.f, kWR = 1.f / 256.f;
 
 template <int D>
-struct Shape {
+struct Lay {
   static constexpr int NG = D / 16;
-  static constexpr int LPT = (D == 96) ? 2 : NG / 2;  // lanes per token
-  static constexpr int GPL = NG / LPT;                 // groups per lane
-  static constexpr int E = GPL * 16;                   // elements per lane
-  static constexpr int TPW = 64 / LPT;                 // tokens per wave step
+  static constexpr int LPP = D == 64 ? 4 : 8;  // lanes per token pair (d = 96: 6 of 8 busy)
+  static constexpr int PAIRS = 64 / LPP;        // token pairs per wave step
+  static constexpr int TPW = 2 * PAIRS;         // tokens per wave step
 };
 
 // ------------------------------------------------------------ code pairs
-// A dword of BITS-bit codes holds 32/BITS codes (element j at bit j*BITS).
-// Pair k takes two of them into the two fp16 halves: after an optional right
-// shift, masking leaves code_lo at bit position p of the low half and code_hi
-// at the same position of the high half; OR-ing 1024's exponent makes the
-// halves 1024 + 2^p * code.
+// A dword of BITS-bit codes holds 32/BITS codes (element j at bit j*BITS),
+// i.e. two 16-bit units.  Pair k takes code k of each unit into the two fp16
+// halves: after an optional right shift, masking leaves code k of the low
+// unit at bit position p of the low half and code k of the high unit at the
+// same position of the high half; OR-ing 1024's exponent makes the halves
+// 1024 + 2^p * code.
 template <int BITS>
 struct Pairs {
-  static constexpr int PER_DWORD = 16 / BITS;  // 4 pairs (int4) or 8 pairs (int2)
-  __host__ __device__ static constexpr int lo(int k) { return k; }
-  __host__ __device__ static constexpr int hi(int k) { return k + 32 / BITS / 2; }
+  static constexpr int PER_UNIT = 16 / BITS;  // 4 (int4) or 8 (int2)
   __host__ __device__ static constexpr int shift(int k) {
     return BITS == 4 ? (k < 2 ? 0 : 8) : (k < 5 ? 0 : 10);
   }
@@ -89,12 +102,20 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t m
 }
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ uint32_t as_u32(h2 h) { return __builtin_bit_cast(uint32_t, h); }
 
 template <int BITS, int K>
-__device__ __forceinline__ uint32_t pair_bits(uint32_t w, uint32_t magic) {
+__device__ __forceinline__ h2 pair_of(uint32_t w, uint32_t magic) {
   using PR = Pairs<BITS>;
-  return and_or(PR::shift(K) ? (w >> PR::shift(K)) : w, PR::mask(K), magic);
+  return as_h2(and_or(PR::shift(K) ? (w >> PR::shift(K)) : w, PR::mask(K), magic));
+}
+
+// Calls f(integral_constant<K>) for K = 0..N-1 (keeps K a compile-time constant).
+template <int N, int K = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<N, K + 1>(f);
+  }
 }
 
 // ------------------------------------------------------------ DPP helpers
@@ -103,311 +124,125 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
                                                             0xF, false));
 }
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;   // lane i <-> 7-i inside each half row
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
-// Sum over the LPT lanes of one token (consecutive lanes inside a quad).
-template <int LPT>
-__device__ __forceinline__ float token_sum(float v) {
+// Sum over the LPP lanes of one token pair.
+template <int LPP>
+__device__ __forceinline__ float pair_sum(float v) {
   v += dpp<kQuadSwap1>(v);
-  if constexpr (LPT == 4) v += dpp<kQuadSwap2>(v);
+  v += dpp<kQuadSwap2>(v);
+  if constexpr (LPP == 8) v += dpp<kHalfMirror>(v);
   return v;
 }
 
-// ------------------------------------------------------------ loads
-template <int BYTES, int ALIGN>
-__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
-  if constexpr (BYTES % 16 == 0 && ALIGN % 16 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 16; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (BYTES % 8 == 0 && ALIGN % 8 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 8; ++i) {
-      const uint2 v = reinterpret_cast<const uint2*>(p)[i];
-      w[2 * i] = v.x; w[2 * i + 1] = v.y;
-    }
-  } else if constexpr (BYTES % 4 == 0 && ALIGN % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
-  } else {
-    static_assert(BYTES % 2 == 0 && ALIGN % 2 == 0, "unsupported load shape");
-#pragma unroll
-    for (int i = 0; i < (BYTES + 3) / 4; ++i) w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < BYTES / 2; ++i)
-      w[i / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << (16 * (i % 2));
-  }
+// Sum over the lanes of a 16-lane row that own the same group (equal lane
+// index mod LPP); the result lands in every such lane.
+template <int LPP>
+__device__ __forceinline__ float row_group_sum(float v) {
+  v += dpp<kRowRor8>(v);
+  if constexpr (LPP == 4) v += dpp<kRowRor4>(v);
+  return v;
 }
 
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
-
-template <int D, int BITS>
-struct PlaneView {
-  using S = Shape<D>;
-  static constexpr int CB = S::E * BITS / 8;          // code bytes per lane
-  static constexpr int CW = CB / 4;                   // code dwords per lane
-  static constexpr int DPG = 16 * BITS / 32;          // code dwords per group
-  static constexpr int SB = 2 * S::GPL;               // sz bytes per lane
-  static constexpr int SW = (SB + 3) / 4;
-  static constexpr int ROW = D * BITS / 8;            // code bytes per token
-  static constexpr int CALIGN = gcd_c(gcd_c(ROW, CB), 256);
-  static constexpr int SALIGN = gcd_c(gcd_c(2 * S::NG, SB), 256);
-};
-
-template <int D, int BITS>
-struct PlaneData {
-  uint32_t c[PlaneView<D, BITS>::CW];
-  uint32_t s[PlaneView<D, BITS>::SW];
-};
-
-template <int D, int BITS>
-__device__ __forceinline__ void load_plane(PlaneData<D, BITS>& pd, const uint8_t* codes,
-                                           const uint8_t* sz, int t, int part) {
-  using V = PlaneView<D, BITS>;
-  load_bytes<V::CB, V::CALIGN>(codes + (uint64_t)t * V::ROW + part * V::CB, pd.c);
-  load_bytes<V::SB, V::SALIGN>(sz + (uint64_t)t * (2 * Shape<D>::NG) + part * V::SB, pd.s);
-}
-
-// (scale, offset) of the lane's group g, decoded by the hardware.
-template <int D, int BITS>
-__device__ __forceinline__ f2 group_sz(const PlaneData<D, BITS>& pd, int g) {
-  return (g & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(pd.s[g / 2], true)
-                 : __builtin_amdgcn_cvt_pk_f32_fp8(pd.s[g / 2], false);
-}
-
-// ------------------------------------------------------------ per-lane query
-// fp16 pairs matching the code pairs of one plane, plus the per-group constant
-// 1024 * sum(pair) that the magic exponent adds.
-template <int D, int BITS>
-struct QueryPairs {
-  static constexpr int NP = PlaneView<D, BITS>::CW * Pairs<BITS>::PER_DWORD;
-  h2 p[NP];
-  float off[Shape<D>::GPL];
-};
-
-template <int D, int BITS>
-__device__ __forceinline__ void build_pairs(QueryPairs<D, BITS>& qp, const float* v, float prescale) {
-  using PR = Pairs<BITS>;
-  using V = PlaneView<D, BITS>;
-#pragma unroll
-  for (int g = 0; g < Shape<D>::GPL; ++g) qp.off[g] = 0.f;
-#pragma unroll
-  for (int dw = 0; dw < V::CW; ++dw) {
-#pragma unroll
-    for (int k = 0; k < PR::PER_DWORD; ++k) {
-      const int base = dw * (32 / BITS);
-      const float m = PR::mult(k);
-      const _Float16 a = (_Float16)(v[base + PR::lo(k)] * prescale / m);
-      const _Float16 b = (_Float16)(v[base + PR::hi(k)] * prescale / m);
-      qp.p[dw * PR::PER_DWORD + k] = (h2){a, b};
-      qp.off[dw / V::DPG] += 1024.f * ((float)a + (float)b);
-    }
-  }
-}
-
-// sum over the lane's groups of  s_g * (sum_i w_i c_i) * inv_prescale + z_g * wsum_g
-template <int D, int BITS>
-__device__ __forceinline__ float plane_logit(const PlaneData<D, BITS>& pd, const QueryPairs<D, BITS>& qp,
-                                             const float* wsum, float inv_prescale, uint32_t magic) {
-  using PR = Pairs<BITS>;
-  using V = PlaneView<D, BITS>;
-  float sdot = 0.f, zsum = 0.f;
-#pragma unroll
-  for (int g = 0; g < Shape<D>::GPL; ++g) {
-    float acc = -qp.off[g];
-#pragma unroll
-    for (int dd = 0; dd < V::DPG; ++dd) {
-      const int dw = g * V::DPG + dd;
-      const uint32_t w = pd.c[dw];
-#pragma unroll
-      for (int k = 0; k < PR::PER_DWORD; ++k) {
-        uint32_t bits;
-        switch (k) {  // keeps K a compile-time constant
-          case 0: bits = pair_bits<BITS, 0>(w, magic); break;
-          case 1: bits = pair_bits<BITS, 1>(w, magic); break;
-          case 2: bits = pair_bits<BITS, 2>(w, magic); break;
-          case 3: bits = pair_bits<BITS, 3>(w, magic); break;
-          case 4: bits = pair_bits<BITS, 4>(w, magic); break;
-          case 5: bits = pair_bits<BITS, 5>(w, magic); break;
-          case 6: bits = pair_bits<BITS, 6>(w, magic); break;
-          default: bits = pair_bits<BITS, 7>(w, magic); break;
-        }
-        acc = __builtin_amdgcn_fdot2(as_h2(bits), qp.p[dw * PR::PER_DWORD + k], acc, false);
-      }
-    }
-    const f2 sz = group_sz<D, BITS>(pd, g);
-    sdot = fmaf(sz.x, acc, sdot);
-    zsum = fmaf(sz.y, wsum[g], zsum);
-  }
-  return fmaf(sdot, inv_prescale, zsum);
-}
-
-// Same quantity with fp32 weights: the codes become exact fp16 values (one
-// v_pk_fma_f16 per pair) and meet the weights in v_fma_mix_f32, so the weights
-// need no fp16 rounding (used for H q, which is not exact in fp16).
-template <int D, int BITS>
-__device__ __forceinline__ float plane_logit_mix(const PlaneData<D, BITS>& pd, const float* wv,
-                                                 const float* wsum, uint32_t magic) {
-  using PR = Pairs<BITS>;
-  using V = PlaneView<D, BITS>;
-  float sdot = 0.f, zsum = 0.f;
-#pragma unroll
-  for (int g = 0; g < Shape<D>::GPL; ++g) {
-    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-    for (int dd = 0; dd < V::DPG; ++dd) {
-      const int dw = g * V::DPG + dd;
-      const uint32_t w = pd.c[dw];
-#pragma unroll
-      for (int k = 0; k < PR::PER_DWORD; ++k) {
-        uint32_t bits;
-        switch (k) {
-          case 0: bits = pair_bits<BITS, 0>(w, magic); break;
-          case 1: bits = pair_bits<BITS, 1>(w, magic); break;
-          case 2: bits = pair_bits<BITS, 2>(w, magic); break;
-          case 3: bits = pair_bits<BITS, 3>(w, magic); break;
-          case 4: bits = pair_bits<BITS, 4>(w, magic); break;
-          case 5: bits = pair_bits<BITS, 5>(w, magic); break;
-          case 6: bits = pair_bits<BITS, 6>(w, magic); break;
-          default: bits = pair_bits<BITS, 7>(w, magic); break;
-        }
-        const float m = PR::mult(k);
-        const _Float16 im = (_Float16)(1.f / m), ib = (_Float16)(-1024.f / m);
-        const h2 c = __builtin_elementwise_fma(as_h2(bits), (h2){im, im}, (h2){ib, ib});  // exact codes
-        const int e = dw * (32 / BITS);
-        acc0 = fmaf((float)c.x, wv[e + PR::lo(k)], acc0);
-        acc1 = fmaf((float)c.y, wv[e + PR::hi(k)], acc1);
-      }
-    }
-    const f2 sz = group_sz<D, BITS>(pd, g);
-    sdot = fmaf(sz.x, acc0 + acc1, sdot);
-    zsum = fmaf(sz.y, wsum[g], zsum);
-  }
-  return sdot + zsum;
-}
-
-// acc_i += w * s_g * c_i for the lane's elements; zacc_g += w * z_g
-template <int D, int BITS>
-__device__ __forceinline__ void plane_accumulate(const PlaneData<D, BITS>& pd, float w, float* acc,
-                                                 float* zacc, uint32_t magic) {
-  using PR = Pairs<BITS>;
-  using V = PlaneView<D, BITS>;
-#pragma unroll
-  for (int g = 0; g < Shape<D>::GPL; ++g) {
-    const f2 sz = group_sz<D, BITS>(pd, g);
-    const float ws = w * sz.x;
-    zacc[g] = fmaf(w, sz.y, zacc[g]);
-#pragma unroll
-    for (int dd = 0; dd < V::DPG; ++dd) {
-      const int dw = g * V::DPG + dd;
-      const uint32_t wd = pd.c[dw];
-#pragma unroll
-      for (int k = 0; k < PR::PER_DWORD; ++k) {
-        uint32_t bits;
-        switch (k) {
-          case 0: bits = pair_bits<BITS, 0>(wd, magic); break;
-          case 1: bits = pair_bits<BITS, 1>(wd, magic); break;
-          case 2: bits = pair_bits<BITS, 2>(wd, magic); break;
-          case 3: bits = pair_bits<BITS, 3>(wd, magic); break;
-          case 4: bits = pair_bits<BITS, 4>(wd, magic); break;
-          case 5: bits = pair_bits<BITS, 5>(wd, magic); break;
-          case 6: bits = pair_bits<BITS, 6>(wd, magic); break;
-          default: bits = pair_bits<BITS, 7>(wd, magic); break;
-        }
-        const float m = PR::mult(k);
-        const _Float16 im = (_Float16)(1.f / m), ib = (_Float16)(-1024.f / m);
-        const h2 c = __builtin_elementwise_fma(as_h2(bits), (h2){im, im}, (h2){ib, ib});  // exact codes
-        const int e = dw * (32 / BITS);
-        acc[e + PR::lo(k)] = fmaf((float)c.x, ws, acc[e + PR::lo(k)]);
-        acc[e + PR::hi(k)] = fmaf((float)c.y, ws, acc[e + PR::hi(k)]);
-      }
-    }
-  }
-}
+// (scale, offset) decoded by the hardware from the low or high FP8 byte pair.
+__device__ __forceinline__ f2 sz_pair(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
 
 // ------------------------------------------------------------ LDS staging
 // Each wave streams its tiles (TPW consecutive tokens) through a private ring
-// of STAGES buffers in LDS, filled by global_load_lds DMA: the bytes in
-// flight occupy LDS instead of VGPRs, so STAGES-1 tiles stay in flight while
-// one is consumed.  A tile buffer mirrors the contiguous global bytes of each
-// plane piece, so lane l later reads back exactly the bytes a direct load of
-// its own (token, part) would have returned: piece_base + l * bytes_per_lane.
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
+// of COUNT buffers in LDS, filled by DMA: the bytes in flight occupy LDS
+// instead of VGPRs, so COUNT-1 tiles stay in flight while one is consumed.  A
+// tile buffer mirrors the contiguous global bytes of each plane piece.
 __host__ __device__ constexpr int al16(int x) { return (x + 15) / 16 * 16; }
+
+// DMA granule of a piece: 16 bytes per lane when whole 1 KB instructions
+// cover it and tokens stay 16-byte aligned, else 4 bytes per lane.  Every DMA
+// instruction runs on all 64 lanes (a lane-masked DMA invites the compiler
+// to merge calls across divergent branches, and the LDS base of the merged
+// call would no longer be uniform), so each piece's LDS span is rounded up to
+// whole instructions and surplus lanes re-read the piece's last granule.
+__host__ __device__ constexpr int gran_of(int bytes, int row) {
+  return (bytes % 1024 == 0 && row % 16 == 0) ? 16 : 4;
+}
+__host__ __device__ constexpr int span_of(int bytes, int row) {
+  return (bytes + 64 * gran_of(bytes, row) - 1) / (64 * gran_of(bytes, row)) * 64 * gran_of(bytes, row);
+}
 
 template <int D, int B1, int B2>
 struct Stage {
-  using S = Shape<D>;
-  static constexpr int TPW = S::TPW;
+  using LY = Lay<D>;
+  static constexpr int TPW = LY::TPW;
   static constexpr int R1 = D * B1 / 8;                 // code bytes per token, first plane
   static constexpr int R2 = D * (B2 ? B2 : 2) / 8;      // second plane
-  static constexpr int RS = 2 * S::NG;                  // sz bytes per token
-  // alpha pieces: a 2-byte DMA still advances 4 bytes per lane in LDS
-  static constexpr int C1 = TPW * R1, C2 = TPW * R2, SZ = TPW * RS, AL = TPW * 4;
+  static constexpr int RS = 2 * LY::NG;                 // sz bytes per token
+  static constexpr int C1 = TPW * R1, C2 = TPW * R2, SZ = TPW * RS;
+  // alpha: a 2-byte DMA still advances 4 bytes per lane in LDS (token i at 4 i)
+  static constexpr int AL = 64 * 4;
   static constexpr int k1c = 0;
-  static constexpr int k1s = al16(k1c + C1);
-  static constexpr int v1c = al16(k1s + SZ);
-  static constexpr int v1s = al16(v1c + C1);
-  static constexpr int k2c = al16(v1s + SZ);
-  static constexpr int k2s = al16(k2c + (B2 ? C2 : 0));
-  static constexpr int v2c = al16(k2s + (B2 ? SZ : 0));
-  static constexpr int v2s = al16(v2c + (B2 ? C2 : 0));
-  static constexpr int ka = al16(v2s + (B2 ? SZ : 0));
-  static constexpr int va = al16(ka + (B2 ? AL : 0));
-  static constexpr int BYTES = al16(va + (B2 ? AL : 0));
-  // DMA instructions for a piece: 1 KB granules (16 bytes per lane) while the
-  // row size keeps them 16-byte aligned, then 256-byte dword granules.
-  static constexpr int dma_of(int bytes, int row) {
-    return (row % 16 == 0 ? bytes / 1024 + (bytes % 1024 + 255) / 256 : (bytes + 255) / 256);
-  }
-  static constexpr int N_DMA = 2 * (dma_of(C1, R1) + dma_of(SZ, RS)) +
-                               (B2 ? 2 * (dma_of(C2, R2) + dma_of(SZ, RS) + 1) : 0);
-  static constexpr int COUNT = 3;  // ring depth
+  static constexpr int k1s = k1c + span_of(C1, R1);
+  static constexpr int v1c = k1s + span_of(SZ, RS);
+  static constexpr int v1s = v1c + span_of(C1, R1);
+  static constexpr int k2c = v1s + span_of(SZ, RS);
+  static constexpr int k2s = k2c + (B2 ? span_of(C2, R2) : 0);
+  static constexpr int v2c = k2s + (B2 ? span_of(SZ, RS) : 0);
+  static constexpr int v2s = v2c + (B2 ? span_of(C2, R2) : 0);
+  static constexpr int ka = v2s + (B2 ? span_of(SZ, RS) : 0);
+  static constexpr int va = ka + (B2 ? AL : 0);
+  static constexpr int BYTES = va + (B2 ? AL : 0);
+  static constexpr int n_of(int bytes, int row) { return span_of(bytes, row) / (64 * gran_of(bytes, row)); }
+  static constexpr int N_DMA = 2 * (n_of(C1, R1) + n_of(SZ, RS)) +
+                               (B2 ? 2 * (n_of(C2, R2) + n_of(SZ, RS) + 1) : 0);
+  static constexpr int COUNT = 2;  // ring depth
   static_assert((COUNT - 1) * N_DMA < 64, "pending DMA count must fit vmcnt");
+  static_assert(R1 % 4 == 0 && R2 % 4 == 0 && RS % 4 == 0, "token rows are whole dwords");
 };
 
-// Copies `BYTES` (a multiple of 4) starting at `src` into LDS at `dst` by DMA:
-// 1 KB per instruction (16 bytes per lane) while ROW (the bytes per token)
-// keeps lanes 16-byte aligned, then 256 bytes per instruction.  Lane reads at
-// or beyond `valid` (the bytes of the tile's in-range tokens) are redirected
-// to the last valid granule, so nothing past the range is read and every value
-// stays finite.
-template <int BYTES, int ROW, bool CLAMP>
-__device__ __forceinline__ void dma_piece(const uint8_t* src, int valid, lds_u8* dst, int lane) {
-  constexpr int KB = (ROW % 16 == 0) ? BYTES / 1024 : 0;
-  constexpr int REST = BYTES - KB * 1024;
-  constexpr int FULL = REST / 256, REM = REST % 256;
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  // raw (unstrided) buffer; 0x00020000 is the 32-bit data format that gfx9
+  // requires for untyped buffer loads
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// DMA of one plane piece (BYTES of tokens ROW bytes each) from buffer offset
+// `so` into LDS `dst`: lane l of instruction c moves granule c*64 + l.  Lanes
+// past the piece, and in a partial tile lanes past `valid` (the bytes of the
+// in-range tokens), re-read the last granule in range, so nothing outside the
+// range is read and every staged value stays finite.
+// one DMA instruction of G bytes per lane (G a literal for the builtin)
+template <int G>
+__device__ __forceinline__ void dma1(rsrc_t r, lds_u8* dst, int vo, uint32_t so) {
+  if constexpr (G == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, vo, so, 0, 0);
+  else if constexpr (G == 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, vo, so, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 2, vo, so, 0, 0);
+}
+
+template <int BYTES, int ROW, bool FULL>
+__device__ __forceinline__ void dma_piece(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
+  constexpr int G = gran_of(BYTES, ROW), STEP = 64 * G, N = span_of(BYTES, ROW) / STEP;
 #pragma unroll
-  for (int c = 0; c < KB; ++c) {
-    const int o = c * 1024 + lane * 16;
-    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(o, valid - 16) : o), dst + c * 1024, 16, 0, 0);
-  }
-#pragma unroll
-  for (int c = 0; c < FULL; ++c) {
-    const int o = KB * 1024 + c * 256;
-    const int ol = o + lane * 4;
-    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(ol, valid - 4) : ol), dst + o, 4, 0, 0);
-  }
-  if constexpr (REM != 0) {
-    const int o = KB * 1024 + FULL * 256;
-    const int ol = o + lane * 4;
-    if (lane < REM / 4)
-      __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(ol, valid - 4) : ol), dst + o, 4, 0, 0);
+  for (int c = 0; c < N; ++c) {
+    const int o = c * STEP + lane * G;
+    if constexpr (FULL) {
+      // the c * STEP part rides in the scalar offset
+      const int vo = (c * STEP + STEP <= BYTES) ? lane * G : min(o, BYTES - G) - c * STEP;
+      dma1<G>(r, dst + c * STEP, vo, so + c * STEP);
+    } else {
+      dma1<G>(r, dst + c * STEP, min(o, valid - G), so);
+    }
   }
 }
 
-// Same for a BF16 alpha piece (2 bytes per token), one ushort DMA; as for
-// every sub-dword DMA, lane l lands at dst + 4*l.
-template <int TOKENS, bool CLAMP>
-__device__ __forceinline__ void dma_alpha(const uint8_t* src, int valid, lds_u8* dst, int lane) {
-  if (lane < TOKENS)
-    __builtin_amdgcn_global_load_lds(src + (CLAMP ? min(lane * 2, valid - 2) : lane * 2), dst, 2, 0, 0);
+// BF16 alphas of a tile, one 2-byte DMA over all lanes (lane l lands at
+// dst + 4 l); lanes past the tile's in-range tokens re-read the last one.
+__device__ __forceinline__ void dma_alpha(rsrc_t r, uint32_t so, int tokens, lds_u8* dst, int lane) {
+  dma1<2>(r, dst, min(lane, tokens - 1) * 2, so);
 }
 
 // s_waitcnt that waits until at most n vector-memory operations are pending.
@@ -417,52 +252,157 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int BYTES, int ALIGN>
-__device__ __forceinline__ void lds_bytes(const lds_u8* p, uint32_t* w) {
-  typedef __attribute__((address_space(3))) const u32x4 l4;
+template <int BYTES>
+__device__ __forceinline__ void lds_codes(const lds_u8* p, uint32_t* w) {
   typedef __attribute__((address_space(3))) const u32x2 l2;
   typedef __attribute__((address_space(3))) const uint32_t l1;
-  typedef __attribute__((address_space(3))) const uint16_t lh;
-  if constexpr (BYTES % 16 == 0 && ALIGN % 16 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 16; ++i) {
-      const u32x4 v = reinterpret_cast<l4*>(p)[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (BYTES % 8 == 0 && ALIGN % 8 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 8; ++i) {
-      const u32x2 v = reinterpret_cast<l2*>(p)[i];
-      w[2 * i] = v.x; w[2 * i + 1] = v.y;
-    }
-  } else if constexpr (BYTES % 4 == 0 && ALIGN % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < BYTES / 4; ++i) w[i] = reinterpret_cast<l1*>(p)[i];
+  if constexpr (BYTES == 8) {
+    const u32x2 v = *reinterpret_cast<l2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
   } else {
-#pragma unroll
-    for (int i = 0; i < (BYTES + 3) / 4; ++i) w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < BYTES / 2; ++i) w[i / 2] |= (uint32_t)reinterpret_cast<lh*>(p)[i] << (16 * (i % 2));
+    static_assert(BYTES == 4, "a lane holds 16 codes of 2 or 4 bits");
+    w[0] = *reinterpret_cast<l1*>(p);
   }
 }
 
-template <int D, int BITS>
-__device__ __forceinline__ void lds_plane(PlaneData<D, BITS>& pd, const lds_u8* codes, const lds_u8* sz,
-                                          int lane) {
-  using V = PlaneView<D, BITS>;
-  lds_bytes<V::CB, gcd_c(V::CB, 16)>(codes + lane * V::CB, pd.c);
-  lds_bytes<V::SB, gcd_c(V::SB, 16)>(sz + lane * V::SB, pd.s);
+__device__ __forceinline__ uint32_t lds_u16(const lds_u8* p) {
+  typedef __attribute__((address_space(3))) const uint16_t lh;
+  return *reinterpret_cast<lh*>(p);
 }
 
-template <int D, int B1, int B2>
-struct TokenData {
-  PlaneData<D, B1> k1, v1;
-  PlaneData<D, (B2 ? B2 : 2)> k2, v2;
-  uint32_t ka, va;  // BF16 alphas
+// One plane of one token pair as a lane sees it: 16 codes of each token and
+// the (scale, offset) bytes of its group.
+template <int BITS>
+struct PairPlane {
+  static constexpr int CW = 16 * BITS / 32;  // code dwords per token
+  uint32_t c0[CW], c1[CW];
+  uint32_t sz0, sz1;
 };
+
+template <int BITS>
+__device__ __forceinline__ void lds_pair(PairPlane<BITS>& pp, const lds_u8* codes, const lds_u8* sz,
+                                         int row, int rs) {
+  constexpr int CB = 16 * BITS / 8;
+  lds_codes<CB>(codes, pp.c0);
+  lds_codes<CB>(codes + row, pp.c1);
+  pp.sz0 = lds_u16(sz);
+  pp.sz1 = lds_u16(sz + rs);
+}
+
+// ------------------------------------------------------------ query side
+// fp16 pairs matching the code pairs of one token's 16 codes (plane BITS),
+// plus the constant 1024 * sum(pair) that the magic exponent adds.
+template <int BITS>
+struct QPairs {
+  static constexpr int N = 8;  // 16 elements
+  h2 p[N];
+  float off;
+};
+
+// Element indices (in the lane's group) of code pair k of dword dw.
+template <int BITS>
+__host__ __device__ constexpr int elem_lo(int dw, int k) { return dw * (32 / BITS) + k; }
+template <int BITS>
+__host__ __device__ constexpr int elem_hi(int dw, int k) { return dw * (32 / BITS) + k + 16 / BITS; }
+
+template <int BITS>
+__device__ __forceinline__ void build_qpairs(QPairs<BITS>& qp, const float* v, float prescale) {
+  using PR = Pairs<BITS>;
+  float off = 0.f;
+#pragma unroll
+  for (int dw = 0; dw < 16 * BITS / 32; ++dw) {
+#pragma unroll
+    for (int k = 0; k < PR::PER_UNIT; ++k) {
+      const float m = PR::mult(k);
+      const _Float16 a = (_Float16)(v[elem_lo<BITS>(dw, k)] * prescale / m);
+      const _Float16 b = (_Float16)(v[elem_hi<BITS>(dw, k)] * prescale / m);
+      qp.p[dw * PR::PER_UNIT + k] = (h2){a, b};
+      off += 1024.f * ((float)a + (float)b);
+    }
+  }
+  qp.off = off;
+}
+
+// H q split into fp16 high and low parts (each prescaled and divided by m).
+template <int BITS>
+__device__ __forceinline__ void build_upairs(QPairs<BITS>& hi, QPairs<BITS>& lo, const float* v,
+                                             float prescale) {
+  using PR = Pairs<BITS>;
+  float off = 0.f;
+#pragma unroll
+  for (int dw = 0; dw < 16 * BITS / 32; ++dw) {
+#pragma unroll
+    for (int k = 0; k < PR::PER_UNIT; ++k) {
+      const float m = PR::mult(k);
+      const float xa = v[elem_lo<BITS>(dw, k)] * prescale / m;
+      const float xb = v[elem_hi<BITS>(dw, k)] * prescale / m;
+      const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
+      const _Float16 la = (_Float16)(xa - (float)ha), lb = (_Float16)(xb - (float)hb);
+      hi.p[dw * PR::PER_UNIT + k] = (h2){ha, hb};
+      lo.p[dw * PR::PER_UNIT + k] = (h2){la, lb};
+      off += 1024.f * (((float)ha + (float)hb) + ((float)la + (float)lb));
+    }
+  }
+  hi.off = off;
+  lo.off = 0.f;
+}
+
+// sum_i w_i c_i over one token's 16 codes, times the prescale (plus the magic
+// offset, removed by starting from -off).
+template <int BITS>
+__device__ __forceinline__ float key_dot(const uint32_t* c, const QPairs<BITS>& qp, uint32_t magic) {
+  using PR = Pairs<BITS>;
+  float acc = -qp.off;
+#pragma unroll
+  for (int dw = 0; dw < 16 * BITS / 32; ++dw)
+    static_for<PR::PER_UNIT>([&](auto K) {
+      acc = __builtin_amdgcn_fdot2(pair_of<BITS, K>(c[dw], magic), qp.p[dw * PR::PER_UNIT + K], acc,
+                                   false);
+    });
+  return acc;
+}
+
+template <int BITS>
+__device__ __forceinline__ float key_dot2(const uint32_t* c, const QPairs<BITS>& hi, const QPairs<BITS>& lo,
+                                          uint32_t magic) {
+  using PR = Pairs<BITS>;
+  float acc = -hi.off;
+#pragma unroll
+  for (int dw = 0; dw < 16 * BITS / 32; ++dw)
+    static_for<PR::PER_UNIT>([&](auto K) {
+      const h2 x = pair_of<BITS, K>(c[dw], magic);
+      acc = __builtin_amdgcn_fdot2(x, hi.p[dw * PR::PER_UNIT + K], acc, false);
+      acc = __builtin_amdgcn_fdot2(x, lo.p[dw * PR::PER_UNIT + K], acc, false);
+    });
+  return acc;
+}
+
+// acc_i += w_t (1024 + m_i c_{t,i}) + w_t' (1024 + m_i c_{t',i}) for the 16
+// elements: v_perm_b32 interleaves unit u of the two tokens, then each code
+// pair feeds one dot2 against the weight pair (two with HILO: the weights as
+// an fp16 high part plus an fp16 low part).
+template <int BITS, bool HILO>
+__device__ __forceinline__ void value_acc(const PairPlane<BITS>& pp, h2 wh, h2 wl, float* acc,
+                                          uint32_t magic) {
+  using PR = Pairs<BITS>;
+#pragma unroll
+  for (int dw = 0; dw < PairPlane<BITS>::CW; ++dw) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // bytes 2h, 2h+1 of token t (low half) and of token t' (high half)
+      const uint32_t x = __builtin_amdgcn_perm(pp.c1[dw], pp.c0[dw], h ? 0x07060302u : 0x05040100u);
+      const int base = (2 * dw + h) * PR::PER_UNIT;
+      static_for<PR::PER_UNIT>([&](auto K) {
+        const h2 c = pair_of<BITS, K>(x, magic);
+        acc[base + K] = __builtin_amdgcn_fdot2(c, wh, acc[base + K], false);
+        if constexpr (HILO) acc[base + K] = __builtin_amdgcn_fdot2(c, wl, acc[base + K], false);
+      });
+    }
+  }
+}
 
 // Walsh-Hadamard transform of a vector held two elements per lane (l, l+64)
 // by one wave; block diagonal 64+32 when D == 96.  Unscaled.
@@ -504,11 +444,12 @@ __device__ __forceinline__ float fp16_prescale(float maxabs) {
 }
 
 template <int D, int B1, int B2>
-__global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
-  using S = Shape<D>;
-  constexpr int E = S::E, LPT = S::LPT, TPW = S::TPW, GPL = S::GPL;
+__global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
+  using LY = Lay<D>;
+  constexpr int NG = LY::NG, LPP = LY::LPP, TPW = LY::TPW;
   constexpr bool TWO = B2 != 0;
   constexpr int B2E = TWO ? B2 : 2;
+  constexpr int CB1 = 16 * B1 / 8, CB2 = 16 * B2E / 8;  // code bytes per lane and token
   const Geometry& g = a.g;
 
   using ST = Stage<D, B1, B2>;
@@ -517,67 +458,67 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
   // the epilogue buffers reuse the staging area once every wave has finished
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
   __shared__ float sq[D], su[D];
-  __shared__ float s_scale[4];
+  __shared__ float s_scale[2];
   __shared__ float sm_m[NW];
   typedef float AccRow[4][2 * D + 1];
   AccRow* sm_acc = reinterpret_cast<AccRow*>(smem);               // [wave][row][acc | l]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.q_heads, hq = bh % a.q_heads, kvh = hq / a.group_ratio;
-  const int slot = lane / LPT, part = lane % LPT;
+  const int pj = lane / LPP, e = lane % LPP;   // token pair, group
+  const bool active = e < NG;
+  const int eg = active ? e : NG - 1;           // idle lanes (d = 96) shadow the last group
   const bool rotated = TWO && g.rotation == RQ_ROT_HADAMARD;
   uint32_t magic;
   asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
 
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(a.n_tokens, t_begin + a.tokens_per_split);
-  // ---- plane bases
-  const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
-  const uint8_t* k1 = a.cache + g.slot_offset(0, b, a.layer, loop1, kvh);
-  const uint8_t* v1 = a.cache + g.slot_offset(1, b, a.layer, loop1, kvh);
-  const uint8_t* k1s = k1 + g.sz_rel(loop1);
-  const uint8_t* v1s = v1 + g.sz_rel(loop1);
-  const uint8_t* k2 = a.cache + g.slot_offset(0, b, a.layer, a.loop, kvh);
-  const uint8_t* v2 = a.cache + g.slot_offset(1, b, a.layer, a.loop, kvh);
-  const uint8_t* k2s = k2 + g.sz_rel(a.loop);
-  const uint8_t* v2s = v2 + g.sz_rel(a.loop);
-  const uint16_t* k2a = reinterpret_cast<const uint16_t*>(k2 + g.alpha_rel(a.loop));
-  const uint16_t* v2a = reinterpret_cast<const uint16_t*>(v2 + g.alpha_rel(a.loop));
 
+  // ---- one buffer resource per slot (codes | sz | alpha of one stream)
+  const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
+  const uint32_t sb1 = (uint32_t)g.slot_bytes[g.is_anchor(loop1) ? 0 : 1];
+  const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
+  const rsrc_t rk1 = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, loop1, kvh), sb1);
+  const rsrc_t rv1 = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, loop1, kvh), sb1);
+  const rsrc_t rk2 = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, a.loop, kvh), sb2);
+  const rsrc_t rv2 = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, a.loop, kvh), sb2);
+  const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
+  const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
 
   // ---- stream this wave's tiles through its LDS ring
   lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
   const int first = t_begin + w * TPW;
   const int n_tiles = first < t_end ? (t_end - first + NW * TPW - 1) / (NW * TPW) : 0;
-  auto issue_t = [&](auto clamp, int tb, lds_u8* st, int vt) {
-    constexpr bool C = decltype(clamp)::value;
-    dma_piece<ST::C1, ST::R1, C>(k1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
-    dma_piece<ST::SZ, ST::RS, C>(k1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
-    dma_piece<ST::C1, ST::R1, C>(v1 + (uint64_t)tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
-    dma_piece<ST::SZ, ST::RS, C>(v1s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
+  auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
+    constexpr bool F = decltype(full)::value;
+    dma_piece<ST::C1, ST::R1, F>(rk1, tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
+    dma_piece<ST::SZ, ST::RS, F>(rk1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
+    dma_piece<ST::C1, ST::R1, F>(rv1, tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
+    dma_piece<ST::SZ, ST::RS, F>(rv1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
     if constexpr (TWO) {
-      dma_piece<ST::C2, ST::R2, C>(k2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::k2c, lane);
-      dma_piece<ST::SZ, ST::RS, C>(k2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::k2s, lane);
-      dma_piece<ST::C2, ST::R2, C>(v2 + (uint64_t)tb * ST::R2, vt * ST::R2, st + ST::v2c, lane);
-      dma_piece<ST::SZ, ST::RS, C>(v2s + (uint64_t)tb * ST::RS, vt * ST::RS, st + ST::v2s, lane);
-      dma_alpha<TPW, C>(reinterpret_cast<const uint8_t*>(k2a + tb), vt * 2, st + ST::ka, lane);
-      dma_alpha<TPW, C>(reinterpret_cast<const uint8_t*>(v2a + tb), vt * 2, st + ST::va, lane);
+      dma_piece<ST::C2, ST::R2, F>(rk2, tb * ST::R2, vt * ST::R2, st + ST::k2c, lane);
+      dma_piece<ST::SZ, ST::RS, F>(rk2, s2rel + tb * ST::RS, vt * ST::RS, st + ST::k2s, lane);
+      dma_piece<ST::C2, ST::R2, F>(rv2, tb * ST::R2, vt * ST::R2, st + ST::v2c, lane);
+      dma_piece<ST::SZ, ST::RS, F>(rv2, s2rel + tb * ST::RS, vt * ST::RS, st + ST::v2s, lane);
+      dma_alpha(rk2, arel + tb * 2, F ? TPW : vt, st + ST::ka, lane);
+      dma_alpha(rv2, arel + tb * 2, F ? TPW : vt, st + ST::va, lane);
     }
   };
-  auto issue = [&](int tile) {
-    const int tb = first + tile * NW * TPW;
-    lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
-    const int vt = t_end - tb;  // in-range tokens of this tile (>= 1)
+  auto issue = [&](int tile, auto stage) __attribute__((always_inline)) {
+    const uint32_t tb = (uint32_t)(first + tile * NW * TPW);
+    lds_u8* st = ring + decltype(stage)::value * ST::BYTES;
+    const int vt = t_end - (int)tb;  // in-range tokens of this tile (>= 1)
     if (vt >= TPW)
-      issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
+      issue_t(std::integral_constant<bool, true>{}, tb, st, TPW);
     else
-      issue_t(std::integral_constant<bool, true>{}, tb, st, vt);
+      issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
-#pragma unroll
-  for (int i = 0; i < ST::COUNT - 1; ++i)
-    if (i < n_tiles) issue(i);
-
+  static_for<ST::COUNT - 1>([&](auto S) {
+    if (S < n_tiles) issue(S, S);
+  });
 
   // ---- query, u = H q and their fp16 prescales (wave 0)
   if (w == 0) {
@@ -600,145 +541,197 @@ __global__ void __launch_bounds__(NW * 64, 2) decode_kernel(DecodeArgs a) {
       if (v1ok) su[lane + 64] = u1;
     }
     const float mq = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
-    if (lane == 0) s_scale[0] = fp16_prescale(mq);
+    const float mu = TWO ? wave_max(fmaxf(fabsf(u0), fabsf(u1))) : 0.f;
+    if (lane == 0) {
+      s_scale[0] = fp16_prescale(mq);
+      s_scale[1] = fp16_prescale(mu);
+    }
   }
   __syncthreads();
 
-  const float pq = s_scale[0];
-  QueryPairs<D, B1> qp;
-  float ur[TWO ? E : 1];
-  float qsum[GPL], usum[GPL];
+  // ---- this lane's group of the query: fp16 pairs and sums
+  const float pq = s_scale[0], pu = s_scale[1];
+  QPairs<B1> qp;
+  QPairs<B2E> uh, ul;
+  float qsum = 0.f, usum = 0.f;
   {
-    float v[E];
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = sq[part * E + i];
+    for (int i = 0; i < 16; ++i) v[i] = sq[eg * 16 + i];
 #pragma unroll
-    for (int gi = 0; gi < GPL; ++gi) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s += v[gi * 16 + i];
-      qsum[gi] = s;
-    }
-    build_pairs<D, B1>(qp, v, pq);
+    for (int i = 0; i < 16; ++i) qsum += v[i];
+    build_qpairs<B1>(qp, v, pq);
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) ur[i] = su[part * E + i];
+      for (int i = 0; i < 16; ++i) v[i] = su[eg * 16 + i];
 #pragma unroll
-      for (int gi = 0; gi < GPL; ++gi) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += ur[gi * 16 + i];
-        usum[gi] = s;
-      }
+      for (int i = 0; i < 16; ++i) usum += v[i];
+      build_upairs<B2E>(uh, ul, v, pu);
     }
   }
-  const float ipq = 1.f / pq;
-
-  float accA[E], accR[TWO ? E : 1], zA[GPL], zR[GPL];
-#pragma unroll
-  for (int i = 0; i < E; ++i) accA[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < (TWO ? E : 1); ++i) accR[i] = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < GPL; ++gi) zA[gi] = zR[gi] = 0.f;
-  float m = kEmpty, l = 0.f;
+  const float ipq = 1.f / pq, ipu = 1.f / pu;
   const float qs = a.qscale;
+  const h2 ones = (h2){(_Float16)1.f, (_Float16)1.f};
 
+  float accA[16], accR[TWO ? 16 : 1];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) accA[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (TWO ? 16 : 1); ++i) accR[i] = 0.f;
+  float WA = 0.f, WR = 0.f, zA = 0.f, zR = 0.f;  // fp16 weight sums, offset sums
+  float m = kEmpty, l = 0.f;
 
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
+  // lane-constant LDS offsets inside a tile buffer (token 2 pj of the tile)
+  const int t0 = 2 * pj;
+  const int o1c = t0 * ST::R1 + eg * CB1, o2c = t0 * ST::R2 + eg * CB2;
+  const int osz = t0 * ST::RS + eg * 2, oal = t0 * 4;
+
+  // one tile; `stage` (= it % COUNT) is a compile-time constant, so every LDS
+  // address is a lane constant plus an immediate
+  auto step = [&](int it, auto stage) __attribute__((always_inline)) {
+    constexpr int SG = decltype(stage)::value;
+    if (it + ST::COUNT - 1 < n_tiles)
+      issue(it + ST::COUNT - 1, std::integral_constant<int, (SG + ST::COUNT - 1) % ST::COUNT>{});
     // wait for tile `it`: the tiles issued after it may stay in flight
     const int later = min(ST::COUNT - 1, n_tiles - 1 - it);
-    if constexpr (ST::COUNT > 3) {
-      if (later >= 3) wait_vm<3 * ST::N_DMA>();
-    }
-    if (later == 2) wait_vm<2 * ST::N_DMA>();
-    else if (later == 1) wait_vm<ST::N_DMA>();
-    else if (later == 0) wait_vm<0>();
-    const lds_u8* st = ring + (it % ST::COUNT) * ST::BYTES;
-    TokenData<D, B1, B2> cur;
-    lds_plane<D, B1>(cur.k1, st + ST::k1c, st + ST::k1s, lane);
-    lds_plane<D, B1>(cur.v1, st + ST::v1c, st + ST::v1s, lane);
-    if constexpr (TWO) {
-      lds_plane<D, B2E>(cur.k2, st + ST::k2c, st + ST::k2s, lane);
-      lds_plane<D, B2E>(cur.v2, st + ST::v2c, st + ST::v2s, lane);
-      typedef __attribute__((address_space(3))) const uint16_t lh;
-      cur.ka = reinterpret_cast<lh*>(st + ST::ka)[2 * slot];
-      cur.va = reinterpret_cast<lh*>(st + ST::va)[2 * slot];
-    }
-    const bool cur_ok = first + it * NW * TPW + slot < t_end;
+    static_assert(ST::COUNT == 2, "wait counts below assume a 2-deep ring");
+    if (later == 1) wait_vm<ST::N_DMA>();
+    else wait_vm<0>();
+    const lds_u8* st = ring + SG * ST::BYTES;
+    const int tt = first + it * NW * TPW + t0;
+    const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
-    float part_logit = plane_logit<D, B1>(cur.k1, qp, qsum, ipq, magic);
-    if constexpr (TWO)
-      part_logit = fmaf(bf16_to_f32(cur.ka), plane_logit_mix<D, B2E>(cur.k2, ur, usum, magic), part_logit);
-    const float logit = cur_ok ? token_sum<LPT>(part_logit) * qs : kEmpty;
-    if (logit > m + kLazy) {
-      const float corr = exp2f(m - logit);
-      l *= corr;
-#pragma unroll
-      for (int i = 0; i < E; ++i) accA[i] *= corr;
-#pragma unroll
-      for (int gi = 0; gi < GPL; ++gi) zA[gi] *= corr;
-      if constexpr (TWO) {
-#pragma unroll
-        for (int i = 0; i < E; ++i) accR[i] *= corr;
-#pragma unroll
-        for (int gi = 0; gi < GPL; ++gi) zR[gi] *= corr;
-      }
-      m = logit;
+    PairPlane<B1> k1, v1;
+    lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
+    lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, ST::R1, ST::RS);
+    PairPlane<B2E> k2, v2;
+    uint32_t ka0 = 0, ka1 = 0, va0 = 0, va1 = 0;
+    if constexpr (TWO) {
+      lds_pair<B2E>(k2, st + ST::k2c + o2c, st + ST::k2s + osz, ST::R2, ST::RS);
+      lds_pair<B2E>(v2, st + ST::v2c + o2c, st + ST::v2s + osz, ST::R2, ST::RS);
+      ka0 = lds_u16(st + ST::ka + oal);
+      ka1 = lds_u16(st + ST::ka + oal + 4);
+      va0 = lds_u16(st + ST::va + oal);
+      va1 = lds_u16(st + ST::va + oal + 4);
     }
-    const float p = cur_ok ? exp2f(logit - m) : 0.f;
-    l += p;
-    plane_accumulate<D, B1>(cur.v1, p, accA, zA, magic);
-    if constexpr (TWO) plane_accumulate<D, B2E>(cur.v2, p * bf16_to_f32(cur.va), accR, zR, magic);
+
+    // ---- logits of the pair
+    float part0, part1;
+    {
+      f2 s0 = sz_pair(k1.sz0), s1 = sz_pair(k1.sz1);
+      if (!active) s0 = s1 = (f2){0.f, 0.f};
+      part0 = fmaf(s0.x * key_dot<B1>(k1.c0, qp, magic), ipq, s0.y * qsum);
+      part1 = fmaf(s1.x * key_dot<B1>(k1.c1, qp, magic), ipq, s1.y * qsum);
+    }
+    if constexpr (TWO) {
+      f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
+      if (!active) s0 = s1 = (f2){0.f, 0.f};
+      const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
+      const float r1 = fmaf(s1.x * key_dot2<B2E>(k2.c1, uh, ul, magic), ipu, s1.y * usum);
+      part0 = fmaf(bf16_to_f32(ka0), r0, part0);
+      part1 = fmaf(bf16_to_f32(ka1), r1, part1);
+    }
+    const float lg0 = ok0 ? pair_sum<LPP>(part0) * qs : kEmpty;
+    const float lg1 = ok1 ? pair_sum<LPP>(part1) * qs : kEmpty;
+
+    // ---- online softmax
+    const float mx = fmaxf(lg0, lg1);
+    if (mx > m + kLazy) {
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
+      l *= corr;
+      WA *= corr;
+      zA *= corr;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) accA[i] *= corr;
+      if constexpr (TWO) {
+        WR *= corr;
+        zR *= corr;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accR[i] *= corr;
+      }
+      m = mx;
+    }
+    const float p0 = ok0 ? __builtin_amdgcn_exp2f(lg0 - m) : 0.f;
+    const float p1 = ok1 ? __builtin_amdgcn_exp2f(lg1 - m) : 0.f;
+    l += p0 + p1;
+
+    // ---- values
+    {
+      // first plane: fp16 high + low weights, so the weights are exact to ~2^-22
+      f2 s0 = sz_pair(v1.sz0), s1 = sz_pair(v1.sz1);
+      if (!active) s0 = s1 = (f2){0.f, 0.f};
+      const float w0 = p0 * s0.x * kWA, w1 = p1 * s1.x * kWA;
+      const h2 wh = (h2){(_Float16)w0, (_Float16)w1};
+      const h2 wl = (h2){(_Float16)(w0 - (float)wh.x), (_Float16)(w1 - (float)wh.y)};
+      WA = __builtin_amdgcn_fdot2(wh, ones, WA, false);
+      WA = __builtin_amdgcn_fdot2(wl, ones, WA, false);
+      zA = fmaf(p0, s0.y, fmaf(p1, s1.y, zA));
+      value_acc<B1, true>(v1, wh, wl, accA, magic);
+    }
+    if constexpr (TWO) {
+      // residual plane: single fp16 weights against codes centred on c0 (the
+      // centre is added back exactly through the offset sum), which halves the
+      // weight-rounding error of this smaller term
+      constexpr float c0 = (float)((1 << B2E) - 1) * 0.5f;
+      f2 s0 = sz_pair(v2.sz0), s1 = sz_pair(v2.sz1);
+      if (!active) s0 = s1 = (f2){0.f, 0.f};
+      const float pa0 = p0 * bf16_to_f32(va0), pa1 = p1 * bf16_to_f32(va1);
+      const h2 wr = (h2){(_Float16)(pa0 * s0.x * kWR), (_Float16)(pa1 * s1.x * kWR)};
+      WR = __builtin_amdgcn_fdot2(wr, ones, WR, false);
+      zR = fmaf(pa0, fmaf(s0.x, c0, s0.y), fmaf(pa1, fmaf(s1.x, c0, s1.y), zR));
+      value_acc<B2E, false>(v2, wr, wr, accR, magic);
+    }
+  };
+  for (int it = 0; it < n_tiles; ++it) {
+    if (it & 1)
+      step(it, std::integral_constant<int, 1>{});
+    else
+      step(it, std::integral_constant<int, 0>{});
   }
   __syncthreads();  // every wave is done with its ring before the epilogue reuses it
 
-  // ---- fold the offset sums, align every slot to the wave maximum
-#pragma unroll
-  for (int i = 0; i < E; ++i) accA[i] += zA[i / 16];
-  if constexpr (TWO) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) accR[i] += zR[i / 16];
-  }
+  // ---- take out the magic constant: element i holds sum w (1024 + m_i c_i);
+  // the residual sum also takes out its centre c0 * sum w
+  static_for<16>([&](auto I) {
+    constexpr int k1 = decltype(I)::value % Pairs<B1>::PER_UNIT;
+    constexpr float mA = Pairs<B1>::mult(k1);
+    accA[I] = fmaf(accA[I], 1.f / (mA * kWA), zA - WA * (1024.f / (mA * kWA)));
+    if constexpr (TWO) {
+      constexpr int k2 = decltype(I)::value % Pairs<B2E>::PER_UNIT;
+      constexpr float mR = Pairs<B2E>::mult(k2);
+      constexpr float c0 = (float)((1 << B2E) - 1) * 0.5f;
+      accR[I] = fmaf(accR[I], 1.f / (mR * kWR), zR - WR * (1024.f / (mR * kWR) + c0 / kWR));
+    }
+  });
+  // ---- align every lane to the wave maximum
   const float Mw = wave_max(m);
   {
     const float f = exp2f(m - Mw);
     l *= f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) accA[i] *= f;
+    for (int i = 0; i < 16; ++i) accA[i] *= f;
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) accR[i] *= f;
+      for (int i = 0; i < 16; ++i) accR[i] *= f;
     }
   }
-  // ---- sum the slots of each 16-lane row (lanes equal mod LPT) with row rotations
+  // ---- sum the token pairs of each 16-lane row (lanes equal mod LPP)
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    accA[i] += dpp<kRowRor8>(accA[i]);
-    if constexpr (LPT == 2) accA[i] += dpp<kRowRor4>(accA[i]);
-    accA[i] += dpp<(LPT == 4 ? kRowRor4 : 0x122)>(accA[i]);
-  }
+  for (int i = 0; i < 16; ++i) accA[i] = row_group_sum<LPP>(accA[i]);
   if constexpr (TWO) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      accR[i] += dpp<kRowRor8>(accR[i]);
-      if constexpr (LPT == 2) accR[i] += dpp<kRowRor4>(accR[i]);
-      accR[i] += dpp<(LPT == 4 ? kRowRor4 : 0x122)>(accR[i]);
-    }
+    for (int i = 0; i < 16; ++i) accR[i] = row_group_sum<LPP>(accR[i]);
   }
-  l += dpp<kRowRor8>(l);
-  if constexpr (LPT == 2) l += dpp<kRowRor4>(l);
-  l += dpp<(LPT == 4 ? kRowRor4 : 0x122)>(l);
+  l = row_group_sum<LPP>(l);
   const int row = lane >> 4;
-  if ((lane & 15) < LPT) {
+  if ((lane & 15) < LPP && active) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) sm_acc[w][row][part * E + i] = accA[i];
+    for (int i = 0; i < 16; ++i) sm_acc[w][row][e * 16 + i] = accA[i];
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) sm_acc[w][row][D + part * E + i] = accR[i];
+      for (int i = 0; i < 16; ++i) sm_acc[w][row][D + e * 16 + i] = accR[i];
     }
-    if (part == 0) sm_acc[w][row][2 * D] = l;
+    if (e == 0) sm_acc[w][row][2 * D] = l;
   }
   if (lane == 0) sm_m[w] = Mw;
   __syncthreads();
@@ -870,9 +863,9 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 
 int decode_tile_tokens(int d) {
   switch (d) {
-    case 64: return NW * Shape<64>::TPW;
-    case 96: return NW * Shape<96>::TPW;
-    default: return NW * Shape<128>::TPW;
+    case 64: return NW * Lay<64>::TPW;
+    case 96: return NW * Lay<96>::TPW;
+    default: return NW * Lay<128>::TPW;
   }
 }
 

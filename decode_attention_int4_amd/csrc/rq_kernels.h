@@ -65,6 +65,6 @@ struct SplitPlan {
   int32_t splits;
   int32_t tokens_per_split;
 };
-SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile_tokens);
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile_tokens, int32_t target_blocks);
 
 }  // namespace rq
