@@ -66,43 +66,47 @@ def time_steps(step, steps: int, torch):
     return s.elapsed_time(e) / steps, wall
 
 
-def dominant_kernel_ms(run, steps: int, torch):
-    """Average duration of one decode-attention call of the dominant kind (the
-    residual loops of a residual cache, the INT4 anchor loops of a direct one:
-    the decode kernel and its split-combine kernel), from events on the stream the kernels
-    run on.  Each run of consecutive residual calls in a step (different layers
-    and loops, so no call re-reads another's data) is bracketed by one event
-    pair, so event overhead is not charged to the calls."""
-    stream = torch.cuda.current_stream()
+def graphed(fn, torch):
+    """Captures fn's launches (made on the current stream) into one HIP graph,
+    after one warm call on a side stream as graph capture requires."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def dominant_calls(run):
+    """The decode-attention calls of the dominant kind in step order (the
+    residual loops of a residual cache, the INT4 anchor loops of a direct
+    one); every call reads a different (loop, layer) of the cache."""
     w = run.w
     P = w.loops_per_group
-    spans = []
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        open_ev = None
-        count = 0
-        for loop in range(w.loops):
-            dominant = (loop % P != P - 1) == (w.mode == 0)
-            if dominant and open_ev is None:
-                open_ev = torch.cuda.Event(enable_timing=True)
-                open_ev.record(stream)
-            if not dominant and open_ev is not None:
-                close = torch.cuda.Event(enable_timing=True)
-                close.record(stream)
-                spans.append((open_ev, close, count))
-                open_ev, count = None, 0
-            for layer in range(w.layers):
-                run.attend(loop, layer)
-                count += dominant
-        if open_ev is not None:
-            close = torch.cuda.Event(enable_timing=True)
-            close.record(stream)
-            spans.append((open_ev, close, count))
-        run.append_new()
-    torch.cuda.synchronize()
-    total = sum(a.elapsed_time(b) for a, b, _ in spans)
-    n = sum(c for _, _, c in spans)
-    return total / n, n
+    return [(loop, layer) for loop in range(w.loops) for layer in range(w.layers)
+            if (loop % P != P - 1) == (w.mode == 0)]
+
+
+def dominant_kernel_ms(run, steps: int, torch, use_graph: bool):
+    """Average duration of one dominant call (its decode kernel and split-combine
+    kernel), from events on the stream the kernels run on around `steps`
+    back-to-back passes over all dominant calls of a step."""
+    calls = dominant_calls(run)
+
+    def once():
+        for loop, layer in calls:
+            run.attend(loop, layer)
+
+    g = graphed(once, torch) if use_graph else None
+    fn = g.replay if use_graph else once
+    fn()
+    ms, _ = time_steps(fn, steps, torch)
+    return ms / len(calls), steps * len(calls)
 
 
 def read_peak_gbps(torch, rq, nbytes=8 << 30, reps=5):
@@ -206,6 +210,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from Python instead of replaying a HIP graph of the step")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run a 1 GiB device copy and a 1 GiB read (known byte counts) "
                          "to calibrate FETCH_SIZE / WRITE_SIZE counters")
@@ -244,14 +250,19 @@ def main():
     log(f"[bench] packed cache {rq.cache_bytes(run.desc) / 1e9:.2f} GB filled in "
         f"{time.perf_counter() - t:.1f} s")
 
+    use_graph = not args.eager
     for _ in range(args.warmup):
         run.step()
-    ms, wall = time_steps(run.step, args.steps, torch)
+    step_graph = graphed(run.step, torch) if use_graph else None
+    step_fn = step_graph.replay if use_graph else run.step
+    for _ in range(args.warmup):
+        step_fn()
+    ms, wall = time_steps(step_fn, args.steps, torch)
     tok_s = w.batch / (ms * 1e-3)
     step_bytes = run.step_bytes()
     log(f"[bench] {ms:.3f} ms/step, {tok_s:.1f} tokens/s, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
 
-    dom_ms, n_launch = dominant_kernel_ms(run, args.steps, torch)
+    dom_ms, n_launch = dominant_kernel_ms(run, args.steps, torch, use_graph)
     P = w.loops_per_group
     dom_loop = 0 if w.mode == 0 else P - 1
     dom_bytes = run.call_bytes(dom_loop)
@@ -273,13 +284,15 @@ def main():
         base = BF16Decode(w)
         for _ in range(args.warmup):
             base.step()
-        bms, _ = time_steps(base.step, args.steps, torch)
+        base_graph = graphed(base.step, torch) if use_graph else None
+        base_fn = base_graph.replay if use_graph else base.step
+        bms, _ = time_steps(base_fn, args.steps, torch)
         extra["bf16_baseline"] = {
             "ms_per_step": round(bms, 4), "tokens_per_s": round(w.batch / (bms * 1e-3), 2),
             "hbm_gbps": round(base.step_bytes() / (bms * 1e-3) / 1e9, 1),
             "speedup_of_residual": round(bms / ms, 3)}
         log(f"[bench] bf16 baseline: {bms:.3f} ms/step, {w.batch / (bms * 1e-3):.1f} tokens/s")
-        del base
+        del base, base_graph, base_fn
         torch.cuda.empty_cache()
 
     cpu = None
@@ -306,7 +319,8 @@ def main():
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
                    "context_tokens": w.n_tokens, "anchor_bits": w.anchor_bits,
                    "residual_bits": w.residual_bits, "group": 16,
-                   "mode": "residual" if w.mode == 0 else "direct"},
+                   "mode": "residual" if w.mode == 0 else "direct",
+                   "launch": "hip graph of one step" if use_graph else "eager"},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,

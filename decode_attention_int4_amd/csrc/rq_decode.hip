@@ -40,8 +40,9 @@
 //   accumulators is rare.  Lanes are merged with DPP row rotations and LDS.
 //   With one split the workgroup's first wave applies H^T and writes the fp32
 //   output; otherwise each workgroup stores its partial state and a small
-//   combine kernel merges the splits (the kernel boundary orders the two, so
-//   no device-scope fences, which would write back L2, are needed).
+//   combine kernel merges the splits.  The kernel boundary orders the two:
+//   merging in the last workgroup to finish would need an agent-scope release
+//   per workgroup, an L2 write-back that costs far more than the extra launch.
 #include <hip/hip_runtime.h>
 
 #include "rq_device.h"
@@ -127,8 +128,6 @@ __device__ __forceinline__ float dpp(float v) {
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;   // lane i <-> 7-i inside each half row
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
 
 // Sum over the LPP lanes of one token pair.
 template <int LPP>
@@ -136,15 +135,6 @@ __device__ __forceinline__ float pair_sum(float v) {
   v += dpp<kQuadSwap1>(v);
   v += dpp<kQuadSwap2>(v);
   if constexpr (LPP == 8) v += dpp<kHalfMirror>(v);
-  return v;
-}
-
-// Sum over the lanes of a 16-lane row that own the same group (equal lane
-// index mod LPP); the result lands in every such lane.
-template <int LPP>
-__device__ __forceinline__ float row_group_sum(float v) {
-  v += dpp<kRowRor8>(v);
-  if constexpr (LPP == 4) v += dpp<kRowRor4>(v);
   return v;
 }
 
@@ -308,46 +298,15 @@ __host__ __device__ constexpr int elem_lo(int dw, int k) { return dw * (32 / BIT
 template <int BITS>
 __host__ __device__ constexpr int elem_hi(int dw, int k) { return dw * (32 / BITS) + k + 16 / BITS; }
 
+// Pair k of a group (runtime k): its two element indices and the bit
+// position of its codes, matching pair_of<BITS, k mod units> on dword k / units.
 template <int BITS>
-__device__ __forceinline__ void build_qpairs(QPairs<BITS>& qp, const float* v, float prescale) {
-  using PR = Pairs<BITS>;
-  float off = 0.f;
-#pragma unroll
-  for (int dw = 0; dw < 16 * BITS / 32; ++dw) {
-#pragma unroll
-    for (int k = 0; k < PR::PER_UNIT; ++k) {
-      const float m = PR::mult(k);
-      const _Float16 a = (_Float16)(v[elem_lo<BITS>(dw, k)] * prescale / m);
-      const _Float16 b = (_Float16)(v[elem_hi<BITS>(dw, k)] * prescale / m);
-      qp.p[dw * PR::PER_UNIT + k] = (h2){a, b};
-      off += 1024.f * ((float)a + (float)b);
-    }
-  }
-  qp.off = off;
-}
-
-// H q split into fp16 high and low parts (each prescaled and divided by m).
-template <int BITS>
-__device__ __forceinline__ void build_upairs(QPairs<BITS>& hi, QPairs<BITS>& lo, const float* v,
-                                             float prescale) {
-  using PR = Pairs<BITS>;
-  float off = 0.f;
-#pragma unroll
-  for (int dw = 0; dw < 16 * BITS / 32; ++dw) {
-#pragma unroll
-    for (int k = 0; k < PR::PER_UNIT; ++k) {
-      const float m = PR::mult(k);
-      const float xa = v[elem_lo<BITS>(dw, k)] * prescale / m;
-      const float xb = v[elem_hi<BITS>(dw, k)] * prescale / m;
-      const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
-      const _Float16 la = (_Float16)(xa - (float)ha), lb = (_Float16)(xb - (float)hb);
-      hi.p[dw * PR::PER_UNIT + k] = (h2){ha, hb};
-      lo.p[dw * PR::PER_UNIT + k] = (h2){la, lb};
-      off += 1024.f * (((float)ha + (float)hb) + ((float)la + (float)lb));
-    }
-  }
-  hi.off = off;
-  lo.off = 0.f;
+__device__ __forceinline__ void pair_layout(int k, int& ea, int& eb, int& pos) {
+  constexpr int PU = Pairs<BITS>::PER_UNIT;
+  const int dw = k / PU, kk = k % PU;
+  ea = dw * (32 / BITS) + kk;
+  eb = ea + 16 / BITS;
+  pos = BITS == 4 ? 4 * (kk & 1) : 2 * (kk < 5 ? kk : kk - 5);
 }
 
 // sum_i w_i c_i over one token's 16 codes, times the prescale (plus the magic
@@ -443,6 +402,64 @@ __device__ __forceinline__ float fp16_prescale(float maxabs) {
   return ldexpf(1.f, 14 - e);
 }
 
+// Merges the split partial states (m, l, accA[D], accR[D]) of one (batch row,
+// query head), applies H^T to the residual sum and writes the fp32 output;
+// one wave per workgroup, two elements per lane.  Splits are merged online,
+// sixteen per round, so each round's loads issue together and the merge
+// waits on memory about once per sixteen splits.
+template <int D, bool TWO>
+__global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
+  constexpr int W = 2 + 2 * D;
+  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.splits;
+  const bool v1ok = (D > 64) && (lane + 64 < D);
+  const float* all = a.partials + (uint64_t)bh * ns * W;
+  auto ld = [](const float* p) { return *p; };
+  float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
+  constexpr int R = 16;  // splits per round
+  for (int s0 = 0; s0 < ns; s0 += R) {
+    float ms[R], ls[R], a0[R], a1[R], r0[R], r1[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int sj = min(s0 + j, ns - 1);
+      const float* ps = all + (uint64_t)sj * W;
+      ms[j] = (s0 + j < ns) ? ld(ps) : kEmpty;
+      ls[j] = ld(ps + 1);
+      a0[j] = ld(ps + 2 + lane);
+      a1[j] = v1ok ? ld(ps + 2 + lane + 64) : 0.f;
+      r0[j] = TWO ? ld(ps + 2 + D + lane) : 0.f;
+      r1[j] = (TWO && v1ok) ? ld(ps + 2 + D + lane + 64) : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < R; ++j) Mn = fmaxf(Mn, ms[j]);
+    const float c = exp2f(M - Mn);
+    L *= c;
+    A0 *= c;
+    A1 *= c;
+    R0 *= c;
+    R1 *= c;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float f = exp2f(ms[j] - Mn);
+      L = fmaf(f, ls[j], L);
+      A0 = fmaf(f, a0[j], A0);
+      A1 = fmaf(f, a1[j], A1);
+      R0 = fmaf(f, r0[j], R0);
+      R1 = fmaf(f, r1[j], R1);
+    }
+    M = Mn;
+  }
+  if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
+    wave_wht<D>(R0, R1, lane);
+    const int8_t* sg = a.signs + ((uint64_t)a.g.layers + a.layer) * D;  // V signs
+    R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
+    if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  a.out[(uint64_t)bh * D + lane] = (A0 + R0) * inv;
+  if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
+}
+
 template <int D, int B1, int B2>
 __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   using LY = Lay<D>;
@@ -454,14 +471,16 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
 
   using ST = Stage<D, B1, B2>;
   constexpr int kStaging = NW * ST::COUNT * ST::BYTES;
-  constexpr int kEpilogue = NW * 4 * (2 * D + 1) * 4;
+  constexpr int kRow = (TWO ? 2 * D : D) + 1;              // accA | accR | l
+  constexpr int kEpilogue = NW * LY::PAIRS * kRow * 4;
   // the epilogue buffers reuse the staging area once every wave has finished
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
   __shared__ float sq[D], su[D];
   __shared__ float s_scale[2];
+  __shared__ __attribute__((aligned(16))) uint32_t spre[8][32];  // per-group query pairs
   __shared__ float sm_m[NW];
-  typedef float AccRow[4][2 * D + 1];
-  AccRow* sm_acc = reinterpret_cast<AccRow*>(smem);               // [wave][row][acc | l]
+  typedef float AccRows[LY::PAIRS][kRow];
+  AccRows* sm_acc = reinterpret_cast<AccRows*>(smem);             // [wave][pair][accA | accR | l]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -520,7 +539,9 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     if (S < n_tiles) issue(S, S);
   });
 
-  // ---- query, u = H q and their fp16 prescales (wave 0)
+  // ---- query side, once per workgroup (wave 0): q, u = H q, their fp16
+  // prescales, and for every group the fp16 pairs matching the code pairs,
+  // the magic constants 1024 * sum(pair) and the plain sums
   if (w == 0) {
     const bool v1ok = (D > 64) && (lane + 64 < D);
     const float q0 = bf16_to_f32(a.q[(uint64_t)bh * D + lane]);
@@ -540,34 +561,71 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
       su[lane] = u0;
       if (v1ok) su[lane + 64] = u1;
     }
-    const float mq = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
-    const float mu = TWO ? wave_max(fmaxf(fabsf(u0), fabsf(u1))) : 0.f;
+    const float pq0 = fp16_prescale(wave_max(fmaxf(fabsf(q0), fabsf(q1))));
+    const float pu0 = TWO ? fp16_prescale(wave_max(fmaxf(fabsf(u0), fabsf(u1)))) : 1.f;
     if (lane == 0) {
-      s_scale[0] = fp16_prescale(mq);
-      s_scale[1] = fp16_prescale(mu);
+      s_scale[0] = pq0;
+      s_scale[1] = pu0;
+    }
+    // lane = (group g, pair k); sq / su were written by this same wave
+    const int g8 = lane >> 3, k = lane & 7;
+    const int gg = g8 < NG ? g8 : NG - 1;
+    int ea, eb, pos;
+    pair_layout<B1>(k, ea, eb, pos);
+    float qa = sq[gg * 16 + ea], qb = sq[gg * 16 + eb];
+    const float im = 1.f / (float)(1 << pos);
+    const _Float16 ha = (_Float16)(qa * pq0 * im), hb = (_Float16)(qb * pq0 * im);
+    float offq = 1024.f * ((float)ha + (float)hb), qsum = qa + qb;
+    uint32_t uhw = 0, ulw = 0;
+    float offu = 0.f, usum = 0.f;
+    if constexpr (TWO) {
+      pair_layout<B2E>(k, ea, eb, pos);
+      const float ua = su[gg * 16 + ea], ub = su[gg * 16 + eb];
+      const float iu = 1.f / (float)(1 << pos);
+      const float xa = ua * pu0 * iu, xb = ub * pu0 * iu;
+      const _Float16 ya = (_Float16)xa, yb = (_Float16)xb;
+      const _Float16 za = (_Float16)(xa - (float)ya), zb = (_Float16)(xb - (float)yb);
+      uhw = __builtin_bit_cast(uint32_t, (h2){ya, yb});
+      ulw = __builtin_bit_cast(uint32_t, (h2){za, zb});
+      offu = 1024.f * (((float)ya + (float)yb) + ((float)za + (float)zb));
+      usum = ua + ub;
+    }
+    offq = pair_sum<8>(offq);
+    qsum = pair_sum<8>(qsum);
+    offu = pair_sum<8>(offu);
+    usum = pair_sum<8>(usum);
+    if (g8 < NG) {
+      spre[g8][k] = __builtin_bit_cast(uint32_t, (h2){ha, hb});
+      spre[g8][8 + k] = uhw;
+      spre[g8][16 + k] = ulw;
+      if (k == 0) {
+        spre[g8][24] = __builtin_bit_cast(uint32_t, offq);
+        spre[g8][25] = __builtin_bit_cast(uint32_t, offu);
+        spre[g8][26] = __builtin_bit_cast(uint32_t, qsum);
+        spre[g8][27] = __builtin_bit_cast(uint32_t, usum);
+      }
     }
   }
   __syncthreads();
 
-  // ---- this lane's group of the query: fp16 pairs and sums
+  // ---- this lane's group of the query
   const float pq = s_scale[0], pu = s_scale[1];
   QPairs<B1> qp;
   QPairs<B2E> uh, ul;
-  float qsum = 0.f, usum = 0.f;
-  {
-    float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = sq[eg * 16 + i];
+  for (int k = 0; k < 8; ++k) qp.p[k] = as_h2(spre[eg][k]);
+  qp.off = __builtin_bit_cast(float, spre[eg][24]);
+  const float qsum = __builtin_bit_cast(float, spre[eg][26]);
+  float usum = 0.f;
+  if constexpr (TWO) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qsum += v[i];
-    build_qpairs<B1>(qp, v, pq);
-    if constexpr (TWO) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = su[eg * 16 + i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) usum += v[i];
-      build_upairs<B2E>(uh, ul, v, pu);
+    for (int k = 0; k < 8; ++k) {
+      uh.p[k] = as_h2(spre[eg][8 + k]);
+      ul.p[k] = as_h2(spre[eg][16 + k]);
     }
+    uh.off = __builtin_bit_cast(float, spre[eg][25]);
+    ul.off = 0.f;
+    usum = __builtin_bit_cast(float, spre[eg][27]);
   }
   const float ipq = 1.f / pq, ipu = 1.f / pu;
   const float qs = a.qscale;
@@ -690,53 +748,38 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // every wave is done with its ring before the epilogue reuses it
 
-  // ---- take out the magic constant: element i holds sum w (1024 + m_i c_i);
-  // the residual sum also takes out its centre c0 * sum w
+  // ---- take out the magic constant (element i holds sum w (1024 + m_i c_i);
+  // the residual sum also takes out its centre c0 * sum w) and align every
+  // lane to the wave maximum in the same step
+  const float Mw = wave_max(m);
+  const float f = exp2f(m - Mw);
+  l *= f;
   static_for<16>([&](auto I) {
     constexpr int k1 = decltype(I)::value % Pairs<B1>::PER_UNIT;
     constexpr float mA = Pairs<B1>::mult(k1);
-    accA[I] = fmaf(accA[I], 1.f / (mA * kWA), zA - WA * (1024.f / (mA * kWA)));
+    accA[I] = fmaf(accA[I], f * (1.f / (mA * kWA)), f * (zA - WA * (1024.f / (mA * kWA))));
     if constexpr (TWO) {
       constexpr int k2 = decltype(I)::value % Pairs<B2E>::PER_UNIT;
       constexpr float mR = Pairs<B2E>::mult(k2);
       constexpr float c0 = (float)((1 << B2E) - 1) * 0.5f;
-      accR[I] = fmaf(accR[I], 1.f / (mR * kWR), zR - WR * (1024.f / (mR * kWR) + c0 / kWR));
+      accR[I] = fmaf(accR[I], f * (1.f / (mR * kWR)),
+                     f * (zR - WR * (1024.f / (mR * kWR) + c0 / kWR)));
     }
   });
-  // ---- align every lane to the wave maximum
-  const float Mw = wave_max(m);
-  {
-    const float f = exp2f(m - Mw);
-    l *= f;
+  // ---- every lane's partial sums to LDS: [wave][token pair][accA | accR | l]
+  if (active) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) accA[i] *= f;
+    for (int i = 0; i < 16; ++i) sm_acc[w][pj][e * 16 + i] = accA[i];
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) accR[i] *= f;
+      for (int i = 0; i < 16; ++i) sm_acc[w][pj][D + e * 16 + i] = accR[i];
     }
-  }
-  // ---- sum the token pairs of each 16-lane row (lanes equal mod LPP)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) accA[i] = row_group_sum<LPP>(accA[i]);
-  if constexpr (TWO) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) accR[i] = row_group_sum<LPP>(accR[i]);
-  }
-  l = row_group_sum<LPP>(l);
-  const int row = lane >> 4;
-  if ((lane & 15) < LPP && active) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm_acc[w][row][e * 16 + i] = accA[i];
-    if constexpr (TWO) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm_acc[w][row][D + e * 16 + i] = accR[i];
-    }
-    if (e == 0) sm_acc[w][row][2 * D] = l;
+    if (e == 0) sm_acc[w][pj][kRow - 1] = l;
   }
   if (lane == 0) sm_m[w] = Mw;
   __syncthreads();
 
-  // ---- merge the waves: this workgroup's state for its token range
+  // ---- merge the waves and token pairs: this workgroup's state for its range
   float M = sm_m[0];
 #pragma unroll
   for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww]);
@@ -745,9 +788,13 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   for (int ww = 0; ww < NW; ++ww) fw[ww] = exp2f(sm_m[ww] - M);
   auto merged = [&](int i) {
     float s = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww)
-      s += (sm_acc[ww][0][i] + sm_acc[ww][1][i] + sm_acc[ww][2][i] + sm_acc[ww][3][i]) * fw[ww];
+#pragma unroll 1
+    for (int ww = 0; ww < NW; ++ww) {
+      float t = 0.f;
+#pragma unroll 4
+      for (int j = 0; j < LY::PAIRS; ++j) t += sm_acc[ww][j][i];
+      s = fmaf(t, fw[ww], s);
+    }
     return s;
   };
   if (a.splits > 1) {
@@ -755,12 +802,11 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     // kernel boundary orders these stores before its loads
     float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + 2 * D);
     for (int i = tid; i <= 2 * D; i += NW * 64) {
-      const float v = (TWO || i < D || i == 2 * D) ? merged(i) : 0.f;
       if (i == 2 * D) {
         mine[0] = M;
-        mine[1] = v;
+        mine[1] = merged(kRow - 1);
       } else {
-        mine[2 + i] = v;
+        mine[2 + i] = (TWO || i < D) ? merged(i) : 0.f;
       }
     }
     return;
@@ -768,7 +814,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   // ---- a single split: finish here (first wave, two elements per lane)
   if (w != 0) return;
   const bool v1ok = (D > 64) && (lane + 64 < D);
-  const float L = merged(2 * D);
+  const float L = merged(kRow - 1);
   const float A0 = merged(lane), A1 = v1ok ? merged(lane + 64) : 0.f;
   float R0 = 0.f, R1 = 0.f;
   if constexpr (TWO) {
@@ -778,55 +824,6 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   if (rotated) {
     wave_wht<D>(R0, R1, lane);
     const int8_t* sg = a.signs + ((uint64_t)g.layers + a.layer) * D;  // V signs
-    R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
-    if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  a.out[(uint64_t)bh * D + lane] = (A0 + R0) * inv;
-  if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
-}
-
-// Merges the split partial states of one (batch row, query head) per
-// workgroup (one wave, two elements per lane), applies H^T to the residual
-// sum and writes the fp32 output.
-template <int D, bool TWO>
-__global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
-  constexpr int W = 2 + 2 * D;
-  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.splits;
-  const bool v1ok = (D > 64) && (lane + 64 < D);
-  const float* all = a.partials + (uint64_t)bh * ns * W;
-  float M = kEmpty;
-  for (int s0 = 0; s0 < ns; s0 += 64)
-    if (s0 + lane < ns) M = fmaxf(M, all[(uint64_t)(s0 + lane) * W]);
-  M = wave_max(M);
-  float L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
-  // eight splits per round: their loads are independent and issue together
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float ms[8], ls[8], a0[8], a1[8], r0[8], r1[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sj = min(s0 + j, ns - 1);
-      const float* ps = all + (uint64_t)sj * W;
-      ms[j] = (s0 + j < ns) ? ps[0] : kEmpty;
-      ls[j] = ps[1];
-      a0[j] = ps[2 + lane];
-      a1[j] = v1ok ? ps[2 + lane + 64] : 0.f;
-      r0[j] = TWO ? ps[2 + D + lane] : 0.f;
-      r1[j] = (TWO && v1ok) ? ps[2 + D + lane + 64] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = exp2f(ms[j] - M);
-      L = fmaf(f, ls[j], L);
-      A0 = fmaf(f, a0[j], A0);
-      A1 = fmaf(f, a1[j], A1);
-      R0 = fmaf(f, r0[j], R0);
-      R1 = fmaf(f, r1[j], R1);
-    }
-  }
-  if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
-    wave_wht<D>(R0, R1, lane);
-    const int8_t* sg = a.signs + ((uint64_t)a.g.layers + a.layer) * D;  // V signs
     R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
     if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
   }

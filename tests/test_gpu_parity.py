@@ -112,6 +112,36 @@ def test_workspace_needs_no_initialization():
         assert_close_attention(out[1, 1].cpu().numpy(), ref, f"poisoned workspace loop {loop}")
 
 
+def test_graph_replay_matches_eager():
+    """A whole decode step captured in a HIP graph (as the benchmark replays
+    it) gives bit-identical outputs and cache bytes on every replay, with
+    eager work and synchronization between the replays."""
+    w = Workload("graph", batch=2, loops=4, layers=2, kv_heads=2, q_heads=4, head_dim=128,
+                 n_tokens=3000, seed=9)
+    run = RQDecode(w)
+    assert rq.decode_workspace_bytes(run.desc, w.q_heads, run.N) > 0   # split + combine path
+    run.step()
+    torch.cuda.synchronize()
+    eager_out = run.out.clone()
+    eager_cache = run.cache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.step()
+    for rep in range(3):
+        run.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(run.out, eager_out), f"replay {rep}: outputs differ"
+        assert torch.equal(run.cache, eager_cache), f"replay {rep}: cache differs"
+
+
 def test_bf16_baseline_tiny():
     w = WORKLOADS["tiny"]
     base = BF16Decode(w)
