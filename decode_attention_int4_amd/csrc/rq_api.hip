@@ -15,13 +15,16 @@ int decode_tile_tokens(int d);
 int bf16_tile_tokens();
 
 // Split-K planning.  Small batch*heads products are split along the tokens
-// until the grid fills the GPU once: the packed-cache decode kernels keep
-// three 4-wave workgroups resident per CU (768 on 256 CUs), the BF16 baseline
-// two (512).  Longer splits amortize each workgroup's query setup and merge,
-// so no more splits than that, and splits never shrink below two tiles.  The
-// result is non-decreasing in n_tokens, so a workspace sized for n serves any
-// smaller n.
-static constexpr int32_t kDecodeTarget = 768;
+// until the grid fills the GPU once: three 4-wave workgroups per CU for a
+// two-plane (residual-loop) decode kernel (768 on 256 CUs), four for a
+// one-plane kernel, two for the BF16 baseline (measured best; longer splits
+// amortize each workgroup's query setup and merge).  Splits never shrink
+// below two tiles.  The result is non-decreasing in
+// n_tokens, so a workspace sized for n serves any smaller n.
+static constexpr int32_t kDecodeTargetTwo = 768;
+static constexpr int32_t kDecodeTargetOne = 1024;
+static constexpr int32_t kDecodeTarget =
+    kDecodeTargetTwo > kDecodeTargetOne ? kDecodeTargetTwo : kDecodeTargetOne;  // workspace bound
 static constexpr int32_t kBf16Target = 512;
 
 static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
@@ -195,8 +198,10 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
+  const bool two = desc->mode == RQ_MODE_RESIDUAL && loop % desc->loops_per_group !=
+                                                         desc->loops_per_group - 1;
   const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim),
-                                                  rq::kDecodeTarget);
+                                             two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);

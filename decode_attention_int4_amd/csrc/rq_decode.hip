@@ -185,7 +185,8 @@ struct Stage {
   static constexpr int n_of(int bytes, int row) { return span_of(bytes, row) / (64 * gran_of(bytes, row)); }
   static constexpr int N_DMA = 2 * (n_of(C1, R1) + n_of(SZ, RS)) +
                                (B2 ? 2 * (n_of(C2, R2) + n_of(SZ, RS) + 1) : 0);
-  static constexpr int COUNT = 2;  // ring depth
+  // ring depth (two measured faster than three for both kernel kinds)
+  static constexpr int COUNT = 2;
   static_assert((COUNT - 1) * N_DMA < 64, "pending DMA count must fit vmcnt");
   static_assert(R1 % 4 == 0 && R2 % 4 == 0 && RS % 4 == 0, "token rows are whole dwords");
 };
@@ -243,6 +244,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int BYTES>
 __device__ __forceinline__ void lds_codes(const lds_u8* p, uint32_t* w) {
@@ -526,18 +528,18 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
       dma_alpha(rv2, arel + tb * 2, F ? TPW : vt, st + ST::va, lane);
     }
   };
-  auto issue = [&](int tile, auto stage) __attribute__((always_inline)) {
+  auto issue = [&](int tile) __attribute__((always_inline)) {
     const uint32_t tb = (uint32_t)(first + tile * NW * TPW);
-    lds_u8* st = ring + decltype(stage)::value * ST::BYTES;
+    lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
     const int vt = t_end - (int)tb;  // in-range tokens of this tile (>= 1)
     if (vt >= TPW)
       issue_t(std::integral_constant<bool, true>{}, tb, st, TPW);
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
-  static_for<ST::COUNT - 1>([&](auto S) {
-    if (S < n_tiles) issue(S, S);
-  });
+#pragma unroll
+  for (int i = 0; i < ST::COUNT - 1; ++i)
+    if (i < n_tiles) issue(i);
 
   // ---- query side, once per workgroup (wave 0): q, u = H q, their fp16
   // prescales, and for every group the fp16 pairs matching the code pairs,
@@ -608,25 +610,16 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- this lane's group of the query
+  // ---- this lane's group of the query: the sums stay in registers; the fp16
+  // pairs are re-read from LDS every tile (broadcast reads), which keeps 24
+  // VGPRs free for occupancy
   const float pq = s_scale[0], pu = s_scale[1];
-  QPairs<B1> qp;
-  QPairs<B2E> uh, ul;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) qp.p[k] = as_h2(spre[eg][k]);
-  qp.off = __builtin_bit_cast(float, spre[eg][24]);
+  const float qoff = __builtin_bit_cast(float, spre[eg][24]);
+  const float uoff = __builtin_bit_cast(float, spre[eg][25]);
   const float qsum = __builtin_bit_cast(float, spre[eg][26]);
-  float usum = 0.f;
-  if constexpr (TWO) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uh.p[k] = as_h2(spre[eg][8 + k]);
-      ul.p[k] = as_h2(spre[eg][16 + k]);
-    }
-    uh.off = __builtin_bit_cast(float, spre[eg][25]);
-    ul.off = 0.f;
-    usum = __builtin_bit_cast(float, spre[eg][27]);
-  }
+  const float usum = TWO ? __builtin_bit_cast(float, spre[eg][27]) : 0.f;
+  typedef __attribute__((address_space(3))) const u32x4 lq4;
+  const lq4* prow = (const lq4*)((lds_u8*)&spre[0][0] + eg * (int)sizeof(spre[0]));
   const float ipq = 1.f / pq, ipu = 1.f / pu;
   const float qs = a.qscale;
   const h2 ones = (h2){(_Float16)1.f, (_Float16)1.f};
@@ -644,36 +637,61 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   const int o1c = t0 * ST::R1 + eg * CB1, o2c = t0 * ST::R2 + eg * CB2;
   const int osz = t0 * ST::RS + eg * 2, oal = t0 * 4;
 
-  // one tile; `stage` (= it % COUNT) is a compile-time constant, so every LDS
-  // address is a lane constant plus an immediate
-  auto step = [&](int it, auto stage) __attribute__((always_inline)) {
-    constexpr int SG = decltype(stage)::value;
-    if (it + ST::COUNT - 1 < n_tiles)
-      issue(it + ST::COUNT - 1, std::integral_constant<int, (SG + ST::COUNT - 1) % ST::COUNT>{});
+  // one loop body for every stage: stage-specialized copies would make the
+  // compiler shuffle all live accumulators between them on every iteration
+  for (int it = 0; it < n_tiles; ++it) {
+    if (it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
     // wait for tile `it`: the tiles issued after it may stay in flight
     const int later = min(ST::COUNT - 1, n_tiles - 1 - it);
-    static_assert(ST::COUNT == 2, "wait counts below assume a 2-deep ring");
-    if (later == 1) wait_vm<ST::N_DMA>();
+    static_assert(ST::COUNT <= 3, "wait counts below cover rings up to 3 deep");
+    if (ST::COUNT == 3 && later == 2) wait_vm<(ST::COUNT - 1) * ST::N_DMA>();
+    else if (later >= 1) wait_vm<ST::N_DMA>();
     else wait_vm<0>();
-    const lds_u8* st = ring + SG * ST::BYTES;
+    const lds_u8* st = ring + (it % ST::COUNT) * ST::BYTES;
     const int tt = first + it * NW * TPW + t0;
     const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
-    PairPlane<B1> k1, v1;
+    // keys now; the value planes are read after the softmax update, so their
+    // registers are not live across the logit computation
+    PairPlane<B1> k1;
     lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
-    lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, ST::R1, ST::RS);
-    PairPlane<B2E> k2, v2;
-    uint32_t ka0 = 0, ka1 = 0, va0 = 0, va1 = 0;
+    PairPlane<B2E> k2;
+    uint32_t ka0 = 0, ka1 = 0;
     if constexpr (TWO) {
       lds_pair<B2E>(k2, st + ST::k2c + o2c, st + ST::k2s + osz, ST::R2, ST::RS);
-      lds_pair<B2E>(v2, st + ST::v2c + o2c, st + ST::v2s + osz, ST::R2, ST::RS);
       ka0 = lds_u16(st + ST::ka + oal);
       ka1 = lds_u16(st + ST::ka + oal + 4);
-      va0 = lds_u16(st + ST::va + oal);
-      va1 = lds_u16(st + ST::va + oal + 4);
     }
 
     // ---- logits of the pair
+    asm volatile("" ::: "memory");  // keep the pair reads inside the loop
+    QPairs<B1> qp;
+    QPairs<B2E> uh, ul;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 x = prow[j];
+      qp.p[4 * j] = as_h2(x.x);
+      qp.p[4 * j + 1] = as_h2(x.y);
+      qp.p[4 * j + 2] = as_h2(x.z);
+      qp.p[4 * j + 3] = as_h2(x.w);
+    }
+    qp.off = qoff;
+    if constexpr (TWO) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 x = prow[2 + j], y = prow[4 + j];
+        uh.p[4 * j] = as_h2(x.x);
+        uh.p[4 * j + 1] = as_h2(x.y);
+        uh.p[4 * j + 2] = as_h2(x.z);
+        uh.p[4 * j + 3] = as_h2(x.w);
+        ul.p[4 * j] = as_h2(y.x);
+        ul.p[4 * j + 1] = as_h2(y.y);
+        ul.p[4 * j + 2] = as_h2(y.z);
+        ul.p[4 * j + 3] = as_h2(y.w);
+      }
+      uh.off = uoff;
+      ul.off = 0.f;
+    }
     float part0, part1;
     {
       f2 s0 = sz_pair(k1.sz0), s1 = sz_pair(k1.sz1);
@@ -714,6 +732,15 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     l += p0 + p1;
 
     // ---- values
+    PairPlane<B1> v1;
+    lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, ST::R1, ST::RS);
+    PairPlane<B2E> v2;
+    uint32_t va0 = 0, va1 = 0;
+    if constexpr (TWO) {
+      lds_pair<B2E>(v2, st + ST::v2c + o2c, st + ST::v2s + osz, ST::R2, ST::RS);
+      va0 = lds_u16(st + ST::va + oal);
+      va1 = lds_u16(st + ST::va + oal + 4);
+    }
     {
       // first plane: fp16 high + low weights, so the weights are exact to ~2^-22
       f2 s0 = sz_pair(v1.sz0), s1 = sz_pair(v1.sz1);
@@ -739,12 +766,6 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
       zR = fmaf(pa0, fmaf(s0.x, c0, s0.y), fmaf(pa1, fmaf(s1.x, c0, s1.y), zR));
       value_acc<B2E, false>(v2, wr, wr, accR, magic);
     }
-  };
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it & 1)
-      step(it, std::integral_constant<int, 1>{});
-    else
-      step(it, std::integral_constant<int, 0>{});
   }
   __syncthreads();  // every wave is done with its ring before the epilogue reuses it
 
