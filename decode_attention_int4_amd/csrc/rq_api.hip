@@ -125,15 +125,12 @@ rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, in
   return RQ_OK;
 }
 
-rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
-                             int32_t n_tokens, int32_t t_new, const int8_t* signs, void* stream) {
-  rq_status st = check_desc(desc);
-  if (st != RQ_OK) return st;
-  if (n_tokens < 0 || t_new < 0) return RQ_ERR_INVALID_ARG;
-  if ((int64_t)n_tokens + t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
+static rq_status quantize_append_impl(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
+                                      int32_t n_tokens, const int32_t* positions, int32_t t_new,
+                                      const int8_t* signs, void* stream) {
   if (t_new == 0) return RQ_OK;
   if (!cache || !kv_bf16 || (needs_signs(desc) && !signs)) return RQ_ERR_INVALID_ARG;
-  if (!aligned(cache, 256) || !aligned(kv_bf16, 4)) return RQ_ERR_ALIGNMENT;
+  if (!aligned(cache, 256) || !aligned(kv_bf16, 4) || !aligned(positions, 4)) return RQ_ERR_ALIGNMENT;
   rq::QuantArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<uint8_t*>(cache);
@@ -141,10 +138,31 @@ rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint1
   a.signs = signs;
   a.n_tokens = n_tokens;
   a.t_new = t_new;
+  a.positions = positions;
   a.items = 2ull * desc->batch * desc->layers * desc->kv_heads *
             (uint64_t)(desc->loops / desc->loops_per_group) * (uint64_t)t_new;
   return rq::launch_quant_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK
                                                                                       : RQ_ERR_LAUNCH;
+}
+
+rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
+                             int32_t n_tokens, int32_t t_new, const int8_t* signs, void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (n_tokens < 0 || t_new < 0) return RQ_ERR_INVALID_ARG;
+  if ((int64_t)n_tokens + t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
+  return quantize_append_impl(desc, cache, kv_bf16, n_tokens, nullptr, t_new, signs, stream);
+}
+
+rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
+                                    const int32_t* positions, int32_t t_new, const int8_t* signs,
+                                    void* stream) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (t_new < 0) return RQ_ERR_INVALID_ARG;
+  if (t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
+  if (t_new > 0 && !positions) return RQ_ERR_INVALID_ARG;
+  return quantize_append_impl(desc, cache, kv_bf16, 0, positions, t_new, signs, stream);
 }
 
 rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
@@ -179,10 +197,11 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, i
   return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
-rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
-                              int32_t loop, int32_t layer, const uint16_t* q_bf16, int32_t q_heads,
-                              int32_t n_tokens, float softmax_scale, void* workspace,
-                              uint64_t workspace_bytes, float* out, void* stream) {
+static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* cache,
+                                       const int8_t* signs, int32_t loop, int32_t layer,
+                                       const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                                       const int32_t* lengths, float softmax_scale, void* workspace,
+                                       uint64_t workspace_bytes, float* out, void* stream) {
   rq_status st = check_desc(desc);
   if (st != RQ_OK) return st;
   if (loop < 0 || loop >= desc->loops || layer < 0 || layer >= desc->layers || q_heads <= 0 ||
@@ -193,7 +212,8 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   const uint64_t need = rq_decode_workspace_bytes(desc, q_heads, n_tokens);
   if (!cache || !q_bf16 || !out || (needs_signs(desc) && !signs) || (need && !workspace))
     return RQ_ERR_INVALID_ARG;
-  if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q_bf16, 4) || !aligned(out, 4))
+  if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q_bf16, 4) || !aligned(out, 4) ||
+      !aligned(lengths, 4))
     return RQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
@@ -209,6 +229,7 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   a.q = q_bf16;
   a.out = out;
   a.partials = static_cast<float*>(workspace);
+  a.lengths = lengths;
   a.loop = loop;
   a.layer = layer;
   a.q_heads = q_heads;
@@ -218,6 +239,24 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
   a.tokens_per_split = plan.tokens_per_split;
   a.qscale = softmax_scale * 1.4426950408889634f;
   return rq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
+}
+
+rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
+                              int32_t loop, int32_t layer, const uint16_t* q_bf16, int32_t q_heads,
+                              int32_t n_tokens, float softmax_scale, void* workspace,
+                              uint64_t workspace_bytes, float* out, void* stream) {
+  return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, n_tokens, nullptr,
+                               softmax_scale, workspace, workspace_bytes, out, stream);
+}
+
+rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cache,
+                                     const int8_t* signs, int32_t loop, int32_t layer,
+                                     const uint16_t* q_bf16, int32_t q_heads, const int32_t* lengths,
+                                     int32_t max_n_tokens, float softmax_scale, void* workspace,
+                                     uint64_t workspace_bytes, float* out, void* stream) {
+  if (!lengths) return RQ_ERR_INVALID_ARG;
+  return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, max_n_tokens,
+                               lengths, softmax_scale, workspace, workspace_bytes, out, stream);
 }
 
 uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,

@@ -495,8 +495,11 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   uint32_t magic;
   asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
 
+  // tokens of this batch row (per-row lengths come from device memory and are
+  // clamped to the planned maximum)
+  const int n_row = a.lengths ? min(max(a.lengths[b], 0), a.n_tokens) : a.n_tokens;
   const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(a.n_tokens, t_begin + a.tokens_per_split);
+  const int t_end = min(n_row, t_begin + a.tokens_per_split);
 
   // ---- one buffer resource per slot (codes | sz | alpha of one stream)
   const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);

@@ -14,6 +14,7 @@ struct QuantArgs {
   const uint16_t* kv;     // [2][B][L][layers][H][t_new][d] BF16
   const int8_t* signs;    // [2][layers][d]
   int32_t n_tokens, t_new;
+  const int32_t* positions;  // [B] first position per batch row, or null (all at n_tokens)
   uint64_t items;         // 2*B*layers*H*(L/P)*t_new
 };
 hipError_t launch_quant_append(const QuantArgs& a, hipStream_t s);
@@ -38,6 +39,7 @@ struct DecodeArgs {
   const uint16_t* q;      // [B][Hq][d]
   float* out;             // [B][Hq][d]
   float* partials;        // [B*Hq][splits][2 + 2d]
+  const int32_t* lengths;  // [B] tokens per batch row (clamped to n_tokens), or null
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;
   float qscale;           // softmax scale * log2(e)

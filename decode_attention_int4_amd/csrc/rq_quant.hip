@@ -141,7 +141,14 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
     c /= g.layers;
     const int b = (int)(c % g.batch);
     const int kv = (int)(c / g.batch);
-    const int pos = a.n_tokens + t;
+    int pos = a.n_tokens + t;
+    if (a.positions) {
+      // per-row positions come from device memory: a row whose range does not
+      // fit the cache is skipped (the whole wave agrees, b is wave-uniform)
+      const int p0 = a.positions[b];
+      if (p0 < 0 || p0 > g.max_tokens - a.t_new) continue;
+      pos = p0 + t;
+    }
 
     auto src = [&](int loop) {
       return a.kv + ((((uint64_t)(kv * g.batch + b) * g.loops + loop) * g.layers + layer) *

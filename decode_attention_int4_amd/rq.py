@@ -29,8 +29,9 @@ OUT_F32, OUT_BF16 = 0, 1
 # Every symbol include/rq.h declares.
 EXPORTS = (
     "rq_status_string", "rq_validate_desc", "rq_cache_bytes", "rq_cache_slot",
-    "rq_quantize_append", "rq_reconstruct", "rq_decode_workspace_bytes",
-    "rq_decode_attention", "rq_bf16_decode_workspace_bytes", "rq_bf16_decode_attention",
+    "rq_quantize_append", "rq_quantize_append_ragged", "rq_reconstruct",
+    "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ragged",
+    "rq_bf16_decode_workspace_bytes", "rq_bf16_decode_attention",
     "rq_read_probe_sink_words", "rq_read_probe",
 )
 
@@ -84,11 +85,14 @@ def lib() -> ctypes.CDLL:
         L.rq_cache_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_uint64)]
         L.rq_cache_slot.argtypes = [D, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Slot)]
         L.rq_quantize_append.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _vp]
+        L.rq_quantize_append_ragged.argtypes = [D, _vp, _vp, _vp, _i32, _vp, _vp]
         L.rq_reconstruct.argtypes = [D, _vp, _vp, _i32, _i32, _i32, _vp, _vp]
         L.rq_decode_workspace_bytes.argtypes = [D, _i32, _i32]
         L.rq_decode_workspace_bytes.restype = _u64
         L.rq_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
                                           ctypes.c_float, _vp, _u64, _vp, _vp]
+        L.rq_decode_attention_ragged.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
+                                                 ctypes.c_float, _vp, _u64, _vp, _vp]
         L.rq_bf16_decode_workspace_bytes.argtypes = [D, _i32, _i32]
         L.rq_bf16_decode_workspace_bytes.restype = _u64
         L.rq_bf16_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
@@ -96,8 +100,8 @@ def lib() -> ctypes.CDLL:
         L.rq_read_probe_sink_words.restype = ctypes.c_uint32
         L.rq_read_probe.argtypes = [_vp, _u64, _vp, _vp]
         for name in ("rq_validate_desc", "rq_cache_bytes", "rq_cache_slot", "rq_quantize_append",
-                     "rq_reconstruct", "rq_decode_attention", "rq_bf16_decode_attention",
-                     "rq_read_probe"):
+                     "rq_quantize_append_ragged", "rq_reconstruct", "rq_decode_attention",
+                     "rq_decode_attention_ragged", "rq_bf16_decode_attention", "rq_read_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +193,28 @@ def quantize_append(desc: CacheDesc, cache: torch.Tensor, kv_bf16: torch.Tensor,
                                     _stream(stream)), "rq_quantize_append")
 
 
+def quantize_append_ragged(desc: CacheDesc, cache: torch.Tensor, kv_bf16: torch.Tensor,
+                           positions: torch.Tensor, signs: Optional[torch.Tensor],
+                           stream=None) -> None:
+    """kv_bf16: [2, B, loops, layers, kv_heads, t_new, d] BF16; batch row b is
+    appended at positions[b] (device int32 [B])."""
+    c = _dev(cache, torch.uint8, "cache")
+    x = _dev(kv_bf16, torch.bfloat16, "kv_bf16")
+    if kv_bf16.dim() != 7 or tuple(kv_bf16.shape[:5]) != (2, desc.batch, desc.loops, desc.layers,
+                                                          desc.kv_heads) \
+            or kv_bf16.shape[6] != desc.head_dim:
+        raise ValueError(f"kv_bf16 shape {tuple(kv_bf16.shape)} does not match {desc}")
+    if tuple(positions.shape) != (desc.batch,):
+        raise ValueError(f"positions shape {tuple(positions.shape)} != ({desc.batch},)")
+    s = _dev(signs, torch.int8, "signs") if signs is not None else None
+    if cache.numel() < cache_bytes(desc):
+        raise ValueError("cache tensor smaller than rq_cache_bytes()")
+    _check(lib().rq_quantize_append_ragged(ctypes.byref(desc), c, x,
+                                           _dev(positions, torch.int32, "positions"),
+                                           kv_bf16.shape[5], s, _stream(stream)),
+           "rq_quantize_append_ragged")
+
+
 def reconstruct(desc: CacheDesc, cache: torch.Tensor, signs: Optional[torch.Tensor],
                 tok_begin: int, tok_end: int, out: Optional[torch.Tensor] = None,
                 out_dtype=torch.float32, stream=None) -> torch.Tensor:
@@ -222,6 +248,27 @@ def decode_attention(desc: CacheDesc, cache: torch.Tensor, signs: Optional[torch
         _dev(q, torch.bfloat16, "q"), q.shape[1], n_tokens, float(softmax_scale),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _dev(out, torch.float32, "out"), _stream(stream)), "rq_decode_attention")
+    return out
+
+
+def decode_attention_ragged(desc: CacheDesc, cache: torch.Tensor, signs: Optional[torch.Tensor],
+                            loop: int, layer: int, q: torch.Tensor, lengths: torch.Tensor,
+                            max_n_tokens: int, softmax_scale: float, workspace: torch.Tensor,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q: [B, q_heads, d] BF16, lengths: device int32 [B] -> out [B, q_heads, d] fp32."""
+    if q.dim() != 3 or q.shape[0] != desc.batch or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match {desc}")
+    if tuple(lengths.shape) != (desc.batch,):
+        raise ValueError(f"lengths shape {tuple(lengths.shape)} != ({desc.batch},)")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    s = _dev(signs, torch.int8, "signs") if signs is not None else None
+    _check(lib().rq_decode_attention_ragged(
+        ctypes.byref(desc), _dev(cache, torch.uint8, "cache"), s, loop, layer,
+        _dev(q, torch.bfloat16, "q"), q.shape[1], _dev(lengths, torch.int32, "lengths"),
+        max_n_tokens, float(softmax_scale), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _dev(out, torch.float32, "out"), _stream(stream)),
+        "rq_decode_attention_ragged")
     return out
 
 

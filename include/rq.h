@@ -154,6 +154,22 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
                          int32_t tok_begin, int32_t tok_end, int32_t out_dtype, void* out,
                          void* stream);
 
+/*
+ * Quantize-and-append with a position per batch row, for batches whose
+ * sequences have different lengths (the serving case; ai4snews para. 4
+ * describes the method inside a batching inference server).  Identical to
+ * rq_quantize_append except that batch row b is written at token positions
+ * [positions[b], positions[b] + t_new).
+ *   positions  device int32 [batch], 4-byte aligned.  They are read on the
+ *              device: a row whose range does not fit [0, max_tokens) is
+ *              skipped (nothing of it is written) rather than reported.
+ * Errors: RQ_ERR_CAPACITY when t_new > max_tokens; RQ_ERR_INVALID_ARG when
+ * positions is NULL and t_new > 0.
+ */
+rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache,
+                                    const uint16_t* kv_bf16, const int32_t* positions,
+                                    int32_t t_new, const int8_t* signs, void* stream);
+
 /* Bytes of workspace rq_decode_attention needs for `q_heads` query heads and
  * any n_tokens <= max_n_tokens. */
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
@@ -183,6 +199,24 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache,
                               const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
                               float softmax_scale, void* workspace, uint64_t workspace_bytes,
                               float* out, void* stream);
+
+/*
+ * Decode attention with a length per batch row: row b attends to tokens
+ * [0, lengths[b]) of its slots; otherwise identical to rq_decode_attention.
+ *   lengths       device int32 [batch], 4-byte aligned, read on the device and
+ *                 clamped to [0, max_n_tokens]; a row of length 0 gets zeros.
+ *   max_n_tokens  bound on the lengths; plans the split-K grid and sizes the
+ *                 workspace (rq_decode_workspace_bytes(desc, q_heads,
+ *                 max_n_tokens)).  Work scales with max_n_tokens per row.
+ * Errors: as rq_decode_attention with n_tokens = max_n_tokens;
+ * RQ_ERR_INVALID_ARG when lengths is NULL.
+ */
+rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cache,
+                                     const int8_t* signs, int32_t loop, int32_t layer,
+                                     const uint16_t* q_bf16, int32_t q_heads,
+                                     const int32_t* lengths, int32_t max_n_tokens,
+                                     float softmax_scale, void* workspace,
+                                     uint64_t workspace_bytes, float* out, void* stream);
 
 /*
  * Baseline: split-K flash decode over an uncompressed BF16 cache of the same

@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "rq.h")
 
 FAKE = ctypes.c_void_p(1 << 20)        # 256-aligned, never dereferenced
 MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+ODD = ctypes.c_void_p((1 << 20) + 2)      # not 4-byte aligned
 
 
 def _declared():
@@ -130,6 +131,17 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rq_decode_attention(D, FAKE, None, 0, 0, FAKE, 2, 256, f, FAKE, ws, FAKE, None) == 1
     assert L.rq_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 256, ctypes.c_float(float("nan")),
                                  FAKE, ws, FAKE, None) == 1
+    # ragged variants
+    assert L.rq_quantize_append_ragged(D, FAKE, FAKE, None, 1, FAKE, None) == 1
+    assert L.rq_quantize_append_ragged(D, FAKE, FAKE, FAKE, 300, FAKE, None) == 3
+    assert L.rq_quantize_append_ragged(D, FAKE, FAKE, ODD, 1, FAKE, None) == 5
+    assert L.rq_quantize_append_ragged(D, FAKE, FAKE, None, 0, FAKE, None) == 0
+    assert L.rq_decode_attention_ragged(D, FAKE, FAKE, 0, 0, FAKE, 2, None, 10, f, FAKE, ws, FAKE,
+                                        None) == 1
+    assert L.rq_decode_attention_ragged(D, FAKE, FAKE, 0, 0, FAKE, 2, FAKE, 257, f, FAKE, ws, FAKE,
+                                        None) == 3
+    assert L.rq_decode_attention_ragged(D, FAKE, FAKE, 0, 0, FAKE, 2, ODD, 10, f, FAKE,
+                                        ws, FAKE, None) == 5
     # BF16 baseline
     wb = rq.bf16_decode_workspace_bytes(d, 2, 256)
     assert L.rq_bf16_decode_attention(D, FAKE, FAKE, 0, 0, FAKE, 2, 300, f, FAKE, wb, FAKE,

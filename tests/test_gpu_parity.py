@@ -195,3 +195,76 @@ def test_variants_small(d, variant):
                                        loop, run.N)
                 assert_close_attention(out[loop, layer, b, hq], ref,
                                        f"{w.name} loop {loop} hq {hq}")
+
+
+@pytest.mark.parametrize("P", [8, 16])
+def test_larger_loop_groups(P):
+    """Loop groups of 8 and 16 (the appendix sizes): one anchor per group, every
+    other loop of the group a residual against it; sigma decays linearly from
+    0.3 to 0.05 across the group."""
+    sig = tuple(0.3 - (0.3 - 0.05) * j / (P - 2) for j in range(P - 1))
+    w = Workload(f"group{P}", batch=2, loops=16, layers=1, kv_heads=2, q_heads=2, head_dim=128,
+                 n_tokens=300, seed=P, loops_per_group=P, sigmas=sig)
+    keep = [(1, 0, 1)]
+    say(f"[groups] {w.name}")
+    run = RQDecode(w, keep=keep, chunk_tokens=128)
+    run.step()
+    torch.cuda.synchronize()
+    out = run.out.cpu().numpy()
+    b, layer, head = keep[0]
+    ek, ev, HK, HV = check_slice_planes(w, run, keep[0])
+    for loop in range(w.loops):
+        ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, layer, b, head]), loop, run.N)
+        assert_close_attention(out[loop, layer, b, head], ref, f"{w.name} loop {loop}")
+
+
+def test_ragged_rows():
+    """Per-row lengths and positions: row b attends to its first lengths[b]
+    tokens (0 gives zeros), and a ragged append writes row b's new token at
+    positions[b]; a row whose position does not fit is left untouched."""
+    w = Workload("ragged", batch=3, loops=4, layers=1, kv_heads=2, q_heads=4, head_dim=128,
+                 n_tokens=700, seed=11)
+    keep = [(0, 0, 1), (1, 0, 1), (2, 0, 1)]
+    run = RQDecode(w, keep=keep, chunk_tokens=256)
+    lengths = torch.tensor([700, 123, 0], dtype=torch.int32, device="cuda")
+    ws = rq.alloc_workspace(rq.decode_workspace_bytes(run.desc, w.q_heads, 700))
+    for loop in range(w.loops):
+        out = rq.decode_attention_ragged(run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0],
+                                         lengths, 700, w.softmax_scale, ws).cpu().numpy()
+        for (b, layer, head) in keep:
+            n = int(lengths[b])
+            for hq in (2 * head, 2 * head + 1):
+                if n == 0:
+                    assert np.all(out[b, hq] == 0), f"row {b} of length 0"
+                    continue
+                ek, ev, HK, HV = encode_kept(w, run.kept[(b, layer, head)], layer)
+                ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, 0, b, hq]), loop, n)
+                assert_close_attention(out[b, hq], ref, f"ragged row {b} n {n} loop {loop} hq {hq}")
+    # ragged append: rows 0 and 1 at their own positions, row 2 out of range
+    positions = torch.tensor([700, 5, 701], dtype=torch.int32, device="cuda")
+    before = run.cache.clone()
+    rq.quantize_append_ragged(run.desc, run.cache, run.new_kv, positions, run.signs)
+    torch.cuda.synchronize()
+    geom = Geom.of(run.desc)
+    for b, pos in ((0, 700), (1, 5)):
+        for head in range(w.kv_heads):
+            new = run.new_kv[:, b, :, 0, head]                 # [2, loops, 1, d]
+            nk, nv, _, _ = encode_kept(w, new, 0)
+            for kv, e in ((0, nk), (1, nv)):
+                g = decode_slice(run.cache, geom, kv, b, 0, head, 1, pos)
+                for name in ("codes", "s8", "z8", "alpha"):
+                    assert np.array_equal(getattr(g, name), getattr(e, name)), (b, head, kv, name)
+    # everything outside the two written tokens is unchanged
+    changed = (run.cache != before).nonzero().flatten().cpu().numpy()
+    allowed = set()
+    for b, pos in ((0, 700), (1, 5)):
+        for kv in range(2):
+            for head in range(w.kv_heads):
+                for loop in range(w.loops):
+                    s = rq.cache_slot(run.desc, kv, b, 0, loop, head)
+                    cb = s.code_bytes
+                    allowed.update(range(s.codes_offset + pos * cb, s.codes_offset + (pos + 1) * cb))
+                    allowed.update(range(s.sz_offset + pos * 16, s.sz_offset + (pos + 1) * 16))
+                    if s.alpha_offset != 2 ** 64 - 1:
+                        allowed.update(range(s.alpha_offset + pos * 2, s.alpha_offset + pos * 2 + 2))
+    assert set(changed.tolist()) <= allowed
