@@ -201,6 +201,46 @@ def cpu_baseline(run, budget_s: float = 12.0):
     }
 
 
+def capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
+    """Batch doubling 1, 2, 4, ... on the configured shapes, for the packed
+    cache and for BF16, while each cache fits in device memory (with a margin
+    for the step's workspace and generation chunks).  One JSON line per batch."""
+    base = WORKLOADS[args.config]
+    margin = 8 << 30
+    b = 1
+    while b <= 1024:
+        w = base.with_(batch=b, name=f"{base.name}_batch{b}")
+        rec = {"sweep": "capacity", "workload": base.name, "batch": b}
+        for kind in ("rq", "bf16"):
+            torch.cuda.empty_cache()
+            free, _ = torch.cuda.mem_get_info()
+            if kind == "rq":
+                from decode_attention_int4_amd.workload import desc_for
+                need = rq.cache_bytes(desc_for(w, w.n_tokens + 1))
+            else:
+                need = 2 * w.batch * w.loops * w.layers * w.kv_heads * (w.n_tokens + 1) * w.head_dim * 2
+            if need + margin > free:
+                rec[kind] = {"fits": False, "cache_gb": round(need / 1e9, 1)}
+                continue
+            run = RQDecode(w) if kind == "rq" else BF16Decode(w)
+            run.step()
+            g = graphed(run.step, torch)
+            for _ in range(args.warmup):
+                g.replay()
+            ms, _ = time_steps(g.replay, args.steps, torch)
+            rec[kind] = {"fits": True, "cache_gb": round(need / 1e9, 1), "ms_per_step": round(ms, 4),
+                         "tokens_per_s": round(b / (ms * 1e-3), 1),
+                         "hbm_gbps": round(run.step_bytes() / (ms * 1e-3) / 1e9, 1)}
+            del g, run
+        print(json.dumps(rec), flush=True)
+        log(f"[sweep] batch {b}: " + ", ".join(
+            f"{k} " + (f"{rec[k]['tokens_per_s']} tok/s ({rec[k]['cache_gb']} GB)" if rec[k]["fits"]
+                       else f"does not fit ({rec[k]['cache_gb']} GB)") for k in ("rq", "bf16")))
+        if not rec["rq"]["fits"] and not rec["bf16"]["fits"]:
+            break
+        b *= 2
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +252,9 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph of the step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="batch-capacity sweep (batch 1, 2, 4, ... while caches fit) instead of the "
+                         "single benchmark line")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run a 1 GiB device copy and a 1 GiB read (known byte counts) "
                          "to calibrate FETCH_SIZE / WRITE_SIZE counters")
@@ -239,6 +282,10 @@ def main():
         rq.read_probe(src, sink)             # reads exactly 1 GiB
         torch.cuda.synchronize()
         print(json.dumps({"calibration_bytes": n}), flush=True)
+        return
+
+    if args.sweep:
+        capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
         return
 
     w = WORKLOADS[args.config]
