@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 MODE_RESIDUAL = 0
 MODE_DIRECT = 1
+MODE_CHAINED = 2
 ALPHA_LS = 0
 ALPHA_NORM_RATIO = 1
 ALPHA_ONE = 2

@@ -30,6 +30,13 @@
  *      the dequantized residual: alpha = <y,yhat>/<yhat,yhat> ([abstract]:
  *      "least-square scaling"; [ai4s p2]: "BF16 least-squares coefficients
  *      stored for residuals"); 0 when yhat = 0.
+ *   R11 The chained ("previous-loop") reference of the ablation ([ai4s p3]:
+ *      chained reconstruction grows with the distance from the anchor): loop
+ *      l < a of a group takes its residual against the reconstruction of loop
+ *      l+1, the anchor ending the chain, so reconstructing loop j reads the
+ *      anchor and the residuals of loops j..a-1.  Because H is linear, the
+ *      rotated residual is H(x_l - deq(A)) minus the sum of alpha_i yhat_i
+ *      over i = a-1 down to l+1, and it is computed in that form.
  */
 #include "rq_oracle.h"
 
@@ -294,12 +301,13 @@ static int params_ok(const rqo_params* p) {
   if (!p || p->d <= 0 || p->g <= 0 || p->d % p->g || p->P <= 0 || p->d > 4096) return 0;
   if (p->anchor_bits < 1 || p->anchor_bits > 8) return 0;
   if (p->residual_bits < 1 || p->residual_bits > 8) return 0;
-  if (p->mode != RQO_MODE_RESIDUAL && p->mode != RQO_MODE_DIRECT) return 0;
+  if (p->mode != RQO_MODE_RESIDUAL && p->mode != RQO_MODE_DIRECT && p->mode != RQO_MODE_CHAINED)
+    return 0;
   return 1;
 }
 
 static int uses_rotation(const rqo_params* p) {
-  return p->mode == RQO_MODE_RESIDUAL && p->rotate;
+  return p->mode != RQO_MODE_DIRECT && p->rotate;
 }
 
 /* Rotation of a parameter set: initialized only when residuals are rotated. */
@@ -330,6 +338,47 @@ static int encode_group_r(const rqo_params* p, const double* x, const rot_t* R,
   rqo_quant_vector(x + a * d, d, g, p->anchor_bits, codes + a * d, s8 + a * ng, z8 + a * ng);
   rqo_dequant_vector(codes + a * d, s8 + a * ng, z8 + a * ng, d, g, A);
   alpha[a] = 0;
+
+  if (p->mode == RQO_MODE_CHAINED) {
+    /* reading R11: from the loop next to the anchor outwards; corr holds
+     * sum alpha_i yhat_i over the loops already stored, largest i first */
+    double* corr = (double*)calloc((size_t)d, sizeof(double));
+    if (!corr) {
+      free(A);
+      return -2;
+    }
+    for (int l = P - 2; l >= 0; --l) {
+      for (int i = 0; i < d; ++i) r[i] = x[l * d + i] - A[i];
+      if (p->rotate)
+        rot_apply(R, r, y);
+      else
+        memcpy(y, r, sizeof(double) * d);
+      for (int i = 0; i < d; ++i) y[i] -= corr[i];
+      rqo_quant_vector(y, d, g, p->residual_bits, codes + l * d, s8 + l * ng, z8 + l * ng);
+      rqo_dequant_vector(codes + l * d, s8 + l * ng, z8 + l * ng, d, g, yh);
+      double num = 0.0, den = 0.0, yy = 0.0;
+      for (int i = 0; i < d; ++i) {
+        num += y[i] * yh[i];
+        den += yh[i] * yh[i];
+        yy += y[i] * y[i];
+      }
+      double al;
+      if (p->alpha_mode == RQO_ALPHA_ONE)
+        al = 1.0;
+      else if (den <= 0.0)
+        al = 0.0;
+      else if (p->alpha_mode == RQO_ALPHA_NORM_RATIO)
+        al = sqrt(yy) / sqrt(den);
+      else
+        al = num / den;
+      alpha[l] = rqo_bf16_encode(al);
+      const double ab = rqo_bf16_decode(alpha[l]);
+      for (int i = 0; i < d; ++i) corr[i] += ab * yh[i];
+    }
+    free(corr);
+    free(A);
+    return 0;
+  }
 
   for (int l = 0; l < P - 1; ++l) {
     if (p->mode == RQO_MODE_DIRECT) {
@@ -387,11 +436,29 @@ static int reconstruct_group_r(const rqo_params* p, const uint8_t* codes, const 
     rqo_dequant_vector(codes + j * d, s8 + j * ng, z8 + j * ng, d, g, out);
     return 0;
   }
-  double* A = (double*)malloc(sizeof(double) * d * 3);
+  double* A = (double*)malloc(sizeof(double) * d * 4);
   if (!A) return -2;
   double* yh = A + d;
   double* rh = A + 2 * d;
   rqo_dequant_vector(codes + a * d, s8 + a * ng, z8 + a * ng, d, g, A);
+  if (p->mode == RQO_MODE_CHAINED) {
+    /* reading R11: deq(anchor) + H^T sum_{i = a-1 .. j} alpha_i yhat_i, the
+     * anchor and the residuals of loops j..a-1 (distance + 1 reads) */
+    double* sum = A + 3 * d;
+    memset(sum, 0, sizeof(double) * d);
+    for (int i = a - 1; i >= j; --i) {
+      rqo_dequant_vector(codes + i * d, s8 + i * ng, z8 + i * ng, d, g, yh);
+      const double al = rqo_bf16_decode(alpha[i]);
+      for (int e = 0; e < d; ++e) sum[e] += al * yh[e];
+    }
+    if (p->rotate)
+      rot_apply_t(R, sum, rh);
+    else
+      memcpy(rh, sum, sizeof(double) * d);
+    for (int e = 0; e < d; ++e) out[e] = A[e] + rh[e];
+    free(A);
+    return 0;
+  }
   rqo_dequant_vector(codes + j * d, s8 + j * ng, z8 + j * ng, d, g, yh);
   if (p->rotate)
     rot_apply_t(R, yh, rh);
@@ -567,8 +634,11 @@ int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
     if (!rc) rc = rqo_attention_dense(n, d, q, Kh, Vh, scale, out);
   } else if (rc == 0) {
     const int j = loop % P, a = P - 1;
-    const int two = (p->mode == RQO_MODE_RESIDUAL && j != a);
+    const int two = (p->mode != RQO_MODE_DIRECT && j != a);
     const int own = (p->mode == RQO_MODE_DIRECT) ? loop : (loop - j + a); /* first plane */
+    /* residual planes read for this loop: its own (residual mode) or those of
+     * loops j..a-1 of the group (chained mode, reading R11) */
+    const int r_last = (p->mode == RQO_MODE_CHAINED) ? loop - j + a - 1 : loop;
     if (two && p->rotate)
       rot_apply(&RK, q, u);
     else
@@ -587,17 +657,18 @@ int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
         la += rqo_fp8_decode(ks[vA * ng + gi]) * sqc + rqo_fp8_decode(kz[vA * ng + gi]) * sq;
       }
       double lr = 0.0;
-      if (two) {
-        size_t vR = (size_t)loop * N + t;
+      for (int rl = loop; two && rl <= r_last; ++rl) {
+        size_t vR = (size_t)rl * N + t;
+        double lp = 0.0;
         for (int gi = 0; gi < ng; ++gi) {
           double su = 0.0, suc = 0.0;
           for (int i = gi * g; i < (gi + 1) * g; ++i) {
             su += u[i];
             suc += u[i] * kc[vR * d + i];
           }
-          lr += rqo_fp8_decode(ks[vR * ng + gi]) * suc + rqo_fp8_decode(kz[vR * ng + gi]) * su;
+          lp += rqo_fp8_decode(ks[vR * ng + gi]) * suc + rqo_fp8_decode(kz[vR * ng + gi]) * su;
         }
-        lr *= rqo_bf16_decode(ka[vR]);
+        lr += rqo_bf16_decode(ka[vR]) * lp;
       }
       lg[t] = scale * (la + lr);
       if (lg[t] > m) m = lg[t];
@@ -610,8 +681,8 @@ int rqo_attention_slice(const rqo_params* p, int L, int N, int n, int loop,
       for (int i = 0; i < d; ++i)
         accA[i] += w * (rqo_fp8_decode(vs[vA * ng + i / g]) * vc[vA * d + i] +
                         rqo_fp8_decode(vz[vA * ng + i / g]));
-      if (two) {
-        size_t vR = (size_t)loop * N + t;
+      for (int rl = loop; two && rl <= r_last; ++rl) {
+        size_t vR = (size_t)rl * N + t;
         double al = rqo_bf16_decode(va[vR]);
         for (int i = 0; i < d; ++i)
           accR[i] += w * al *

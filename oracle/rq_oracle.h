@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-enum { RQO_MODE_RESIDUAL = 0, RQO_MODE_DIRECT = 1 };
+enum { RQO_MODE_RESIDUAL = 0, RQO_MODE_DIRECT = 1, RQO_MODE_CHAINED = 2 };
 enum { RQO_ALPHA_LS = 0, RQO_ALPHA_NORM_RATIO = 1, RQO_ALPHA_ONE = 2 };
 
 typedef struct {
@@ -41,8 +41,8 @@ typedef struct {
   int P;              /* loops per group; the anchor is the last loop of a group */
   int anchor_bits;    /* bits of the anchor (or, in direct mode, of the anchor-position loop) */
   int residual_bits;  /* bits of every other loop */
-  int mode;           /* RQO_MODE_RESIDUAL or RQO_MODE_DIRECT */
-  int alpha_mode;     /* RQO_ALPHA_* (residual mode only) */
+  int mode;           /* RQO_MODE_RESIDUAL, RQO_MODE_DIRECT or RQO_MODE_CHAINED */
+  int alpha_mode;     /* RQO_ALPHA_* (residual and chained modes) */
   int rotate;         /* 1: rotate residuals with H; 0: identity */
 } rqo_params;
 
