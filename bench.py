@@ -89,7 +89,7 @@ def dominant_calls(run):
     w = run.w
     P = w.loops_per_group
     return [(loop, layer) for loop in range(w.loops) for layer in range(w.layers)
-            if (loop % P != P - 1) == (w.mode == 0)]
+            if (loop % P != P - 1) == (w.mode != 1)]
 
 
 def dominant_kernel_ms(run, steps: int, torch, use_graph: bool):
@@ -140,7 +140,7 @@ def cpu_baseline(run, budget_s: float = 12.0):
     cores = min(16, os.cpu_count() or 1)
     p = O.Params(d=w.head_dim, P=w.loops_per_group, anchor_bits=w.anchor_bits,
                  residual_bits=w.residual_bits, mode=w.mode, alpha_mode=w.alpha_mode,
-                 rotate=1 if (w.rotation == 1 and w.mode == 0) else 0)
+                 rotate=1 if (w.rotation == 1 and w.mode != 1) else 0)
     signs = rotation_signs(w).numpy()
 
     def bits(t):
@@ -310,13 +310,13 @@ def main():
     log(f"[bench] {ms:.3f} ms/step, {tok_s:.1f} tokens/s, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
 
     dom_ms, n_launch = dominant_kernel_ms(run, args.steps, torch, use_graph)
-    P = w.loops_per_group
-    dom_loop = 0 if w.mode == 0 else P - 1
-    dom_bytes = run.call_bytes(dom_loop)
+    calls = dominant_calls(run)
+    # bytes per dominant call (chained mode: the calls read 1 to P-1 residual planes)
+    dom_bytes = sum(run.call_bytes(loop) for loop, _ in calls) // len(calls)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    two = w.mode == 0
-    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0}> + "
-             f"combine_kernel<{w.head_dim},{str(two).lower()}>")
+    two = w.mode != 1
+    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0}"
+             f"{',NR' if w.mode == 2 else ''}> + combine_kernel<{w.head_dim},{str(two).lower()}>")
     log(f"[bench] dominant call ({kname}): {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
         f"{achieved:.0f} GB/s")
 
@@ -366,7 +366,7 @@ def main():
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
                    "context_tokens": w.n_tokens, "anchor_bits": w.anchor_bits,
                    "residual_bits": w.residual_bits, "group": 16,
-                   "mode": "residual" if w.mode == 0 else "direct",
+                   "mode": {0: "residual", 1: "direct", 2: "chained"}[w.mode],
                    "launch": "hip graph of one step" if use_graph else "eager"},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": step_bytes,

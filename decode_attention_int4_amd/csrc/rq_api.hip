@@ -23,6 +23,7 @@ int bf16_tile_tokens();
 // n_tokens, so a workspace sized for n serves any smaller n.
 static constexpr int32_t kDecodeTargetTwo = 768;
 static constexpr int32_t kDecodeTargetOne = 1024;
+static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
 static constexpr int32_t kDecodeTarget =
     kDecodeTargetTwo > kDecodeTargetOne ? kDecodeTargetTwo : kDecodeTargetOne;  // workspace bound
 static constexpr int32_t kBf16Target = 512;
@@ -64,7 +65,12 @@ rq_status check_desc(const rq_cache_desc* d) {
   if (d->loops % d->loops_per_group != 0 || d->loops > 64) return RQ_ERR_UNSUPPORTED;
   if ((d->anchor_bits != 2 && d->anchor_bits != 4) || (d->residual_bits != 2 && d->residual_bits != 4))
     return RQ_ERR_UNSUPPORTED;
-  if (d->mode != RQ_MODE_RESIDUAL && d->mode != RQ_MODE_DIRECT) return RQ_ERR_UNSUPPORTED;
+  if (d->mode != RQ_MODE_RESIDUAL && d->mode != RQ_MODE_DIRECT && d->mode != RQ_MODE_CHAINED)
+    return RQ_ERR_UNSUPPORTED;
+  // chained mode: the decode kernels read up to three residual planes
+  if (d->mode == RQ_MODE_CHAINED &&
+      (d->loops_per_group > 4 || d->anchor_bits != 4 || d->residual_bits != 2))
+    return RQ_ERR_UNSUPPORTED;
   if (d->alpha_mode != RQ_ALPHA_LS && d->alpha_mode != RQ_ALPHA_NORM_RATIO && d->alpha_mode != RQ_ALPHA_ONE)
     return RQ_ERR_UNSUPPORTED;
   if (d->rotation != RQ_ROT_NONE && d->rotation != RQ_ROT_HADAMARD) return RQ_ERR_UNSUPPORTED;
@@ -72,11 +78,14 @@ rq_status check_desc(const rq_cache_desc* d) {
   const double total = 2.0 * d->batch * d->loops * (double)d->layers * d->kv_heads *
                        (double)d->max_tokens * (d->head_dim * 0.5 + 2 * d->head_dim / 16.0 + 2.0);
   if (total > 9.0e18) return RQ_ERR_UNSUPPORTED;
+  // the decode kernels address one slot with 32-bit buffer offsets
+  const double slot = (double)d->max_tokens * (d->head_dim * 0.5 + 2 * d->head_dim / 16.0 + 2.0);
+  if (slot > 2.0e9) return RQ_ERR_UNSUPPORTED;
   return RQ_OK;
 }
 
 bool needs_signs(const rq_cache_desc* d) {
-  return d->mode == RQ_MODE_RESIDUAL && d->rotation == RQ_ROT_HADAMARD;
+  return d->mode != RQ_MODE_DIRECT && d->rotation == RQ_ROT_HADAMARD;
 }
 
 }  // namespace
@@ -218,10 +227,12 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
-  const bool two = desc->mode == RQ_MODE_RESIDUAL && loop % desc->loops_per_group !=
-                                                         desc->loops_per_group - 1;
-  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim),
-                                             two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne);
+  const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
+  const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
+  const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
+  const rq::SplitPlan plan = rq::plan_splits(
+      bh, n_tokens, rq::decode_tile_tokens(desc->head_dim),
+      chain ? rq::kDecodeTargetChain : two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);

@@ -161,12 +161,12 @@ __host__ __device__ constexpr int span_of(int bytes, int row) {
   return (bytes + 64 * gran_of(bytes, row) - 1) / (64 * gran_of(bytes, row)) * 64 * gran_of(bytes, row);
 }
 
-template <int D, int B1, int B2>
+template <int D, int B1, int B2, int NR = 1>
 struct Stage {
   using LY = Lay<D>;
   static constexpr int TPW = LY::TPW;
   static constexpr int R1 = D * B1 / 8;                 // code bytes per token, first plane
-  static constexpr int R2 = D * (B2 ? B2 : 2) / 8;      // second plane
+  static constexpr int R2 = D * (B2 ? B2 : 2) / 8;      // residual planes
   static constexpr int RS = 2 * LY::NG;                 // sz bytes per token
   static constexpr int C1 = TPW * R1, C2 = TPW * R2, SZ = TPW * RS;
   // alpha: a 2-byte DMA still advances 4 bytes per lane in LDS (token i at 4 i)
@@ -175,16 +175,21 @@ struct Stage {
   static constexpr int k1s = k1c + span_of(C1, R1);
   static constexpr int v1c = k1s + span_of(SZ, RS);
   static constexpr int v1s = v1c + span_of(C1, R1);
-  static constexpr int k2c = v1s + span_of(SZ, RS);
-  static constexpr int k2s = k2c + (B2 ? span_of(C2, R2) : 0);
-  static constexpr int v2c = k2s + (B2 ? span_of(SZ, RS) : 0);
-  static constexpr int v2s = v2c + (B2 ? span_of(C2, R2) : 0);
-  static constexpr int ka = v2s + (B2 ? span_of(SZ, RS) : 0);
-  static constexpr int va = ka + (B2 ? AL : 0);
-  static constexpr int BYTES = va + (B2 ? AL : 0);
+  // residual plane r (r < NR) occupies [res(r), res(r) + RSET): K codes, K sz,
+  // V codes, V sz, K alpha, V alpha
+  static constexpr int RES0 = v1s + span_of(SZ, RS);
+  static constexpr int k2c = 0;
+  static constexpr int k2s = k2c + span_of(C2, R2);
+  static constexpr int v2c = k2s + span_of(SZ, RS);
+  static constexpr int v2s = v2c + span_of(C2, R2);
+  static constexpr int ka = v2s + span_of(SZ, RS);
+  static constexpr int va = ka + AL;
+  static constexpr int RSET = va + AL;
+  static constexpr int res(int r) { return RES0 + r * RSET; }
+  static constexpr int BYTES = RES0 + (B2 ? NR * RSET : 0);
   static constexpr int n_of(int bytes, int row) { return span_of(bytes, row) / (64 * gran_of(bytes, row)); }
   static constexpr int N_DMA = 2 * (n_of(C1, R1) + n_of(SZ, RS)) +
-                               (B2 ? 2 * (n_of(C2, R2) + n_of(SZ, RS) + 1) : 0);
+                               (B2 ? NR * 2 * (n_of(C2, R2) + n_of(SZ, RS) + 1) : 0);
   // ring depth (two measured faster than three for both kernel kinds)
   static constexpr int COUNT = 2;
   static_assert((COUNT - 1) * N_DMA < 64, "pending DMA count must fit vmcnt");
@@ -462,7 +467,9 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
   if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
 }
 
-template <int D, int B1, int B2>
+// NR > 1 (chained mode): loop a.loop reads the residual planes of loops
+// a.loop .. a.loop + NR - 1, all accumulated into the one residual sum.
+template <int D, int B1, int B2, int NR>
 __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   using LY = Lay<D>;
   constexpr int NG = LY::NG, LPP = LY::LPP, TPW = LY::TPW;
@@ -471,7 +478,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   constexpr int CB1 = 16 * B1 / 8, CB2 = 16 * B2E / 8;  // code bytes per lane and token
   const Geometry& g = a.g;
 
-  using ST = Stage<D, B1, B2>;
+  using ST = Stage<D, B1, B2, NR>;
   constexpr int kStaging = NW * ST::COUNT * ST::BYTES;
   constexpr int kRow = (TWO ? 2 * D : D) + 1;              // accA | accR | l
   constexpr int kEpilogue = NW * LY::PAIRS * kRow * 4;
@@ -507,8 +514,12 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
   const rsrc_t rk1 = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, loop1, kvh), sb1);
   const rsrc_t rv1 = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, loop1, kvh), sb1);
-  const rsrc_t rk2 = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, a.loop, kvh), sb2);
-  const rsrc_t rv2 = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, a.loop, kvh), sb2);
+  rsrc_t rk2[NR], rv2[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    rk2[r] = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, a.loop + r, kvh), sb2);
+    rv2[r] = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, a.loop + r, kvh), sb2);
+  }
   const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
   const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
 
@@ -523,12 +534,16 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     dma_piece<ST::C1, ST::R1, F>(rv1, tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
     dma_piece<ST::SZ, ST::RS, F>(rv1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
     if constexpr (TWO) {
-      dma_piece<ST::C2, ST::R2, F>(rk2, tb * ST::R2, vt * ST::R2, st + ST::k2c, lane);
-      dma_piece<ST::SZ, ST::RS, F>(rk2, s2rel + tb * ST::RS, vt * ST::RS, st + ST::k2s, lane);
-      dma_piece<ST::C2, ST::R2, F>(rv2, tb * ST::R2, vt * ST::R2, st + ST::v2c, lane);
-      dma_piece<ST::SZ, ST::RS, F>(rv2, s2rel + tb * ST::RS, vt * ST::RS, st + ST::v2s, lane);
-      dma_alpha(rk2, arel + tb * 2, F ? TPW : vt, st + ST::ka, lane);
-      dma_alpha(rv2, arel + tb * 2, F ? TPW : vt, st + ST::va, lane);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        lds_u8* rs = st + ST::res(r);
+        dma_piece<ST::C2, ST::R2, F>(rk2[r], tb * ST::R2, vt * ST::R2, rs + ST::k2c, lane);
+        dma_piece<ST::SZ, ST::RS, F>(rk2[r], s2rel + tb * ST::RS, vt * ST::RS, rs + ST::k2s, lane);
+        dma_piece<ST::C2, ST::R2, F>(rv2[r], tb * ST::R2, vt * ST::R2, rs + ST::v2c, lane);
+        dma_piece<ST::SZ, ST::RS, F>(rv2[r], s2rel + tb * ST::RS, vt * ST::RS, rs + ST::v2s, lane);
+        dma_alpha(rk2[r], arel + tb * 2, F ? TPW : vt, rs + ST::ka, lane);
+        dma_alpha(rv2[r], arel + tb * 2, F ? TPW : vt, rs + ST::va, lane);
+      }
     }
   };
   auto issue = [&](int tile) __attribute__((always_inline)) {
@@ -658,13 +673,6 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     // registers are not live across the logit computation
     PairPlane<B1> k1;
     lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
-    PairPlane<B2E> k2;
-    uint32_t ka0 = 0, ka1 = 0;
-    if constexpr (TWO) {
-      lds_pair<B2E>(k2, st + ST::k2c + o2c, st + ST::k2s + osz, ST::R2, ST::RS);
-      ka0 = lds_u16(st + ST::ka + oal);
-      ka1 = lds_u16(st + ST::ka + oal + 4);
-    }
 
     // ---- logits of the pair
     asm volatile("" ::: "memory");  // keep the pair reads inside the loop
@@ -703,12 +711,19 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
       part1 = fmaf(s1.x * key_dot<B1>(k1.c1, qp, magic), ipq, s1.y * qsum);
     }
     if constexpr (TWO) {
-      f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
-      if (!active) s0 = s1 = (f2){0.f, 0.f};
-      const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
-      const float r1 = fmaf(s1.x * key_dot2<B2E>(k2.c1, uh, ul, magic), ipu, s1.y * usum);
-      part0 = fmaf(bf16_to_f32(ka0), r0, part0);
-      part1 = fmaf(bf16_to_f32(ka1), r1, part1);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const lds_u8* rs = st + ST::res(r);
+        PairPlane<B2E> k2;
+        lds_pair<B2E>(k2, rs + ST::k2c + o2c, rs + ST::k2s + osz, ST::R2, ST::RS);
+        const uint32_t ka0 = lds_u16(rs + ST::ka + oal), ka1 = lds_u16(rs + ST::ka + oal + 4);
+        f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
+        if (!active) s0 = s1 = (f2){0.f, 0.f};
+        const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
+        const float r1 = fmaf(s1.x * key_dot2<B2E>(k2.c1, uh, ul, magic), ipu, s1.y * usum);
+        part0 = fmaf(bf16_to_f32(ka0), r0, part0);
+        part1 = fmaf(bf16_to_f32(ka1), r1, part1);
+      }
     }
     const float lg0 = ok0 ? pair_sum<LPP>(part0) * qs : kEmpty;
     const float lg1 = ok1 ? pair_sum<LPP>(part1) * qs : kEmpty;
@@ -737,13 +752,6 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     // ---- values
     PairPlane<B1> v1;
     lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, ST::R1, ST::RS);
-    PairPlane<B2E> v2;
-    uint32_t va0 = 0, va1 = 0;
-    if constexpr (TWO) {
-      lds_pair<B2E>(v2, st + ST::v2c + o2c, st + ST::v2s + osz, ST::R2, ST::RS);
-      va0 = lds_u16(st + ST::va + oal);
-      va1 = lds_u16(st + ST::va + oal + 4);
-    }
     {
       // first plane: fp16 high + low weights, so the weights are exact to ~2^-22
       f2 s0 = sz_pair(v1.sz0), s1 = sz_pair(v1.sz1);
@@ -757,17 +765,24 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
       value_acc<B1, true>(v1, wh, wl, accA, magic);
     }
     if constexpr (TWO) {
-      // residual plane: single fp16 weights against codes centred on c0 (the
+      // residual planes: single fp16 weights against codes centred on c0 (the
       // centre is added back exactly through the offset sum), which halves the
       // weight-rounding error of this smaller term
       constexpr float c0 = (float)((1 << B2E) - 1) * 0.5f;
-      f2 s0 = sz_pair(v2.sz0), s1 = sz_pair(v2.sz1);
-      if (!active) s0 = s1 = (f2){0.f, 0.f};
-      const float pa0 = p0 * bf16_to_f32(va0), pa1 = p1 * bf16_to_f32(va1);
-      const h2 wr = (h2){(_Float16)(pa0 * s0.x * kWR), (_Float16)(pa1 * s1.x * kWR)};
-      WR = __builtin_amdgcn_fdot2(wr, ones, WR, false);
-      zR = fmaf(pa0, fmaf(s0.x, c0, s0.y), fmaf(pa1, fmaf(s1.x, c0, s1.y), zR));
-      value_acc<B2E, false>(v2, wr, wr, accR, magic);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const lds_u8* rs = st + ST::res(r);
+        PairPlane<B2E> v2;
+        lds_pair<B2E>(v2, rs + ST::v2c + o2c, rs + ST::v2s + osz, ST::R2, ST::RS);
+        const uint32_t va0 = lds_u16(rs + ST::va + oal), va1 = lds_u16(rs + ST::va + oal + 4);
+        f2 s0 = sz_pair(v2.sz0), s1 = sz_pair(v2.sz1);
+        if (!active) s0 = s1 = (f2){0.f, 0.f};
+        const float pa0 = p0 * bf16_to_f32(va0), pa1 = p1 * bf16_to_f32(va1);
+        const h2 wr = (h2){(_Float16)(pa0 * s0.x * kWR), (_Float16)(pa1 * s1.x * kWR)};
+        WR = __builtin_amdgcn_fdot2(wr, ones, WR, false);
+        zR = fmaf(pa0, fmaf(s0.x, c0, s0.y), fmaf(pa1, fmaf(s1.x, c0, s1.y), zR));
+        value_acc<B2E, false>(v2, wr, wr, accR, magic);
+      }
     }
   }
   __syncthreads();  // every wave is done with its ring before the epilogue reuses it
@@ -856,9 +871,9 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
 }
 
-template <int D, int B1, int B2>
+template <int D, int B1, int B2, int NR = 1>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, B1, B2>), dim3(a.splits, a.g.batch * a.q_heads), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR>), dim3(a.splits, a.g.batch * a.q_heads), dim3(NW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D, B2 != 0>), dim3(a.g.batch * a.q_heads), dim3(64), 0, s, a);
@@ -874,6 +889,12 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     return bits == 4 ? launch_t<D, 4, 0>(a, s) : launch_t<D, 2, 0>(a, s);
   }
   const int ab = g.anchor_bits, rb = g.residual_bits;
+  if (g.mode == RQ_MODE_CHAINED) {
+    // loop j reads the residual planes of loops j .. anchor - 1 (4/2 bits only)
+    const int nr = g.P - 1 - a.loop % g.P;
+    if (nr == 3) return launch_t<D, 4, 2, 3>(a, s);
+    if (nr == 2) return launch_t<D, 4, 2, 2>(a, s);
+  }
   if (ab == 4 && rb == 2) return launch_t<D, 4, 2>(a, s);
   if (ab == 4 && rb == 4) return launch_t<D, 4, 4>(a, s);
   if (ab == 2 && rb == 2) return launch_t<D, 2, 2>(a, s);

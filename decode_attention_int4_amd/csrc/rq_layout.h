@@ -39,7 +39,7 @@ struct Geometry {
 
   RQ_HD bool is_anchor(int loop) const { return loop % P == P - 1; }
   RQ_HD int bits_of(int loop) const { return is_anchor(loop) ? anchor_bits : residual_bits; }
-  RQ_HD bool has_alpha(int loop) const { return mode == RQ_MODE_RESIDUAL && !is_anchor(loop); }
+  RQ_HD bool has_alpha(int loop) const { return mode != RQ_MODE_DIRECT && !is_anchor(loop); }
 
   // Byte offset of the codes sub-plane of a slot.
   RQ_HD uint64_t slot_offset(int kv, int b, int layer, int loop, int head) const {
@@ -72,7 +72,7 @@ inline Geometry make_geometry(const rq_cache_desc& c) {
   g.codes_bytes[0] = align_up(T * (uint64_t)c.head_dim * c.anchor_bits / 8, kAlign);
   g.codes_bytes[1] = align_up(T * (uint64_t)c.head_dim * c.residual_bits / 8, kAlign);
   g.sz_bytes = align_up(T * 2u * (uint64_t)g.ng, kAlign);
-  g.alpha_bytes = (c.mode == RQ_MODE_RESIDUAL) ? align_up(T * 2u, kAlign) : 0;
+  g.alpha_bytes = (c.mode != RQ_MODE_DIRECT) ? align_up(T * 2u, kAlign) : 0;
   g.slot_bytes[0] = g.codes_bytes[0] + g.sz_bytes;
   g.slot_bytes[1] = g.codes_bytes[1] + g.sz_bytes + g.alpha_bytes;
   g.group_bytes = g.slot_bytes[0] + (uint64_t)(c.loops_per_group - 1) * g.slot_bytes[1];

@@ -171,8 +171,14 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
                          base + g.sz_rel(aloop) + (uint64_t)pos * (2 * D / 16), A, lane);
     }
 
-    // ---- other loops of the group
-    for (int j = 0; j < g.P - 1; ++j) {
+    // ---- other loops of the group.  Chained mode walks from the loop next to
+    // the anchor outwards: corr = sum alpha_i yhat_i over the loops already
+    // stored, so y = H (x_l - deq(A)) - corr is the rotated residual against
+    // the reconstruction of loop l + 1
+    const bool chained = g.mode == RQ_MODE_CHAINED;
+    double corr0 = 0.0, corr1 = 0.0;
+    for (int jj = 0; jj < g.P - 1; ++jj) {
+      const int j = chained ? g.P - 2 - jj : jj;
       const int loop = k * g.P + j;
       load(loop, x0, x1);
       uint8_t* base = a.cache + g.slot_offset(kv, b, layer, loop, head);
@@ -192,6 +198,10 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
         y0 *= sc0;
         y1 = v1ok ? y1 * sc1 : 0.0;
       }
+      if (chained) {
+        y0 -= corr0;
+        y1 = v1ok ? y1 - corr1 : 0.0;
+      }
       const QuantResult R = quant_vec<D, RB>(y0, y1);
       store_codes<D, RB>(row, sz_row, R, lane);
       const double yh1 = v1ok ? R.deq1 : 0.0;
@@ -209,6 +219,11 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
         al = f64_to_bf16(num / den);
       if (lane == 0)
         reinterpret_cast<uint16_t*>(base + g.alpha_rel(loop))[pos] = (uint16_t)al;
+      if (chained) {
+        const double ab = (double)bf16_to_f32((uint16_t)al);
+        corr0 += ab * R.deq0;
+        corr1 = v1ok ? corr1 + ab * R.deq1 : 0.0;
+      }
     }
   }
 }

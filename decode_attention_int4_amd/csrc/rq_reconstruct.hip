@@ -75,18 +75,24 @@ __global__ void __launch_bounds__(256) reconstruct_kernel(ReconArgs a) {
     float x0 = deq_elem(as, g.sz_rel(aloop), abits, D, t, lane);
     float x1 = v1ok ? deq_elem(as, g.sz_rel(aloop), abits, D, t, lane + 64) : 0.f;
     if (!direct && !anchor) {
-      const uint8_t* rs = a.cache + g.slot_offset(kv, b, layer, loop, head);
-      float y0 = deq_elem(rs, g.sz_rel(loop), g.residual_bits, D, t, lane);
-      float y1 = v1ok ? deq_elem(rs, g.sz_rel(loop), g.residual_bits, D, t, lane + 64) : 0.f;
+      // sum alpha_i yhat_i over the residual planes this loop reads (its own;
+      // chained mode: loops up to the anchor), then H^T once
+      const int last = g.mode == RQ_MODE_CHAINED ? aloop - 1 : loop;
+      float y0 = 0.f, y1 = 0.f;
+      for (int rl = last; rl >= loop; --rl) {
+        const uint8_t* rs = a.cache + g.slot_offset(kv, b, layer, rl, head);
+        const float al = bf16_to_f32(reinterpret_cast<const uint16_t*>(rs + g.alpha_rel(rl))[t]);
+        y0 = fmaf(al, deq_elem(rs, g.sz_rel(rl), g.residual_bits, D, t, lane), y0);
+        if (v1ok) y1 = fmaf(al, deq_elem(rs, g.sz_rel(rl), g.residual_bits, D, t, lane + 64), y1);
+      }
       if (g.rotation == RQ_ROT_HADAMARD) {
         wht_f32<D>(y0, y1, lane);
         const int8_t* sg = a.signs + ((uint64_t)kv * g.layers + layer) * D;
         y0 *= sc0 * (float)sg[lane];
         if (v1ok) y1 *= sc1 * (float)sg[lane + 64];
       }
-      const float al = bf16_to_f32(reinterpret_cast<const uint16_t*>(rs + g.alpha_rel(loop))[t]);
-      x0 = fmaf(al, y0, x0);
-      x1 = fmaf(al, y1, x1);
+      x0 += y0;
+      x1 += y1;
     }
     const uint64_t o = item * D;
     if (a.out_bf16) {

@@ -21,7 +21,7 @@ RQ_OK = 0
 STATUS_NAMES = {0: "RQ_OK", 1: "RQ_ERR_INVALID_ARG", 2: "RQ_ERR_UNSUPPORTED",
                 3: "RQ_ERR_CAPACITY", 4: "RQ_ERR_WORKSPACE", 5: "RQ_ERR_ALIGNMENT",
                 6: "RQ_ERR_LAUNCH"}
-MODE_RESIDUAL, MODE_DIRECT = 0, 1
+MODE_RESIDUAL, MODE_DIRECT, MODE_CHAINED = 0, 1, 2
 ALPHA_LS, ALPHA_NORM_RATIO, ALPHA_ONE = 0, 1, 2
 ROT_NONE, ROT_HADAMARD = 0, 1
 OUT_F32, OUT_BF16 = 0, 1

@@ -41,7 +41,7 @@ class Workload:
     loops_per_group: int = 4
     sigmas: tuple = (0.3, 0.2, 0.1)
     seed: int = 0
-    mode: int = 0                # 0 residual, 1 direct
+    mode: int = 0                # 0 residual, 1 direct, 2 chained
     anchor_bits: int = 4
     residual_bits: int = 2
     alpha_mode: int = 0          # 0 least squares, 1 norm ratio, 2 fixed 1
@@ -75,6 +75,9 @@ WORKLOADS = {
     "ouro16k_b4_direct": Workload("ouro16k_b4_direct", batch=4, loops=4, layers=24,
                                   kv_heads=16, q_heads=16, head_dim=128, n_tokens=16384,
                                   mode=1),
+    # the ablation's chained (previous-loop) reference on the 8k/batch 4 shapes
+    "ouro8k_b4_chained": Workload("ouro8k_b4_chained", batch=4, loops=4, layers=24, kv_heads=16,
+                                  q_heads=16, head_dim=128, n_tokens=8192, mode=2),
     # Huginn-3.5B-like looped core: 4 layers x 32 loops (8 groups of 4), 55 x 96, 8k, b2.
     "huginn8k_b2": Workload("huginn8k_b2", batch=2, loops=32, layers=4, kv_heads=55,
                             q_heads=55, head_dim=96, n_tokens=8192,

@@ -96,7 +96,11 @@ class RQDecode:
             bits = w.anchor_bits if anchor else w.residual_bits
             per_token = d * bits // 8 + 2 * ng
         else:
-            per_token = (d * w.anchor_bits // 8 + 2 * ng) + (d * w.residual_bits // 8 + 2 * ng + 2)
+            # the anchor plus one residual plane (chained mode: one per loop up
+            # to the anchor, i.e. distance + 1 reads)
+            planes = (P - 1 - loop % P) if w.mode == rq.MODE_CHAINED else 1
+            per_token = (d * w.anchor_bits // 8 + 2 * ng) + \
+                planes * (d * w.residual_bits // 8 + 2 * ng + 2)
         return 2 * per_token * w.batch * w.kv_heads * self.N
 
     def step_bytes(self) -> int:

@@ -34,9 +34,21 @@
  *
  * Cache descriptor and supported values:
  *   head_dim 64, 96 or 128; group_size 16; loops % loops_per_group == 0;
- *   anchor_bits and residual_bits each 2 or 4; mode RESIDUAL or DIRECT;
+ *   anchor_bits and residual_bits each 2 or 4; mode RESIDUAL, DIRECT or
+ *   CHAINED (CHAINED: anchor 4 bits, residuals 2 bits, loops_per_group <= 4);
  *   alpha_mode LS, NORM_RATIO or ONE; rotation HADAMARD or NONE;
- *   1 <= batch, layers, kv_heads; 1 <= loops <= 64; 1 <= max_tokens.
+ *   1 <= batch, layers, kv_heads; 1 <= loops <= 64; 1 <= max_tokens, and one
+ *   slot (below) at most 2e9 bytes.
+ *
+ * Modes.  RESIDUAL is the method: every non-anchor loop stores its residual
+ * against the dequantized anchor, so any loop is rebuilt from two reads.
+ * DIRECT stores every loop on its own (the comparison without residuals).
+ * CHAINED is the ablation's previous-loop reference (ai4snews para. 3):
+ * loop l < anchor stores its residual against the reconstruction of loop
+ * l + 1, the anchor ending the chain, so loop j is rebuilt from the anchor and
+ * the residuals of loops j .. anchor - 1 (distance + 1 reads); its rotated
+ * residual is computed as H (x_l - deq(anchor)) - sum alpha_i yhat_i over
+ * i = anchor-1 down to l+1.
  *
  * Byte layout of a cache buffer (little endian).  A "slot" holds one
  * (kv, batch row, layer, loop, kv head) stream of max_tokens tokens, where
@@ -51,8 +63,9 @@
  *                                   at bit (i*bits) % 8 (low bits first)
  *     sz    [max_tokens][2*d/16]    byte 2g = FP8 e4m3fn scale of group g,
  *                                   byte 2g+1 = FP8 e4m3fn offset of group g
- *     alpha [max_tokens] uint16     BF16 coefficient (residual loops of
- *                                   RESIDUAL mode only; absent otherwise)
+ *     alpha [max_tokens] uint16     BF16 coefficient (non-anchor loops of
+ *                                   RESIDUAL and CHAINED modes; absent
+ *                                   otherwise)
  * A dequantized group value is scale * code + offset.  Slot sizes and
  * offsets are given by rq_cache_slot(); the total by rq_cache_bytes().
  */
@@ -76,7 +89,7 @@ typedef enum {
   RQ_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch */
 } rq_status;
 
-enum { RQ_MODE_RESIDUAL = 0, RQ_MODE_DIRECT = 1 };
+enum { RQ_MODE_RESIDUAL = 0, RQ_MODE_DIRECT = 1, RQ_MODE_CHAINED = 2 };
 enum { RQ_ALPHA_LS = 0, RQ_ALPHA_NORM_RATIO = 1, RQ_ALPHA_ONE = 2 };
 enum { RQ_ROT_NONE = 0, RQ_ROT_HADAMARD = 1 };
 enum { RQ_OUT_F32 = 0, RQ_OUT_BF16 = 1 };

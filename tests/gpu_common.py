@@ -29,7 +29,7 @@ def say(*a):
 def params(w: Workload) -> O.Params:
     return O.Params(d=w.head_dim, g=16, P=w.loops_per_group, anchor_bits=w.anchor_bits,
                     residual_bits=w.residual_bits, mode=w.mode, alpha_mode=w.alpha_mode,
-                    rotate=1 if (w.rotation == 1 and w.mode == 0) else 0)
+                    rotate=1 if (w.rotation == 1 and w.mode != 1) else 0)
 
 
 def rotations(w: Workload, layer: int):

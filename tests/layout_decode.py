@@ -43,13 +43,13 @@ class Geom:
         return self.anchor_bits if self.is_anchor(loop) else self.residual_bits
 
     def has_alpha(self, loop):
-        return self.mode == 0 and not self.is_anchor(loop)
+        return self.mode != 1 and not self.is_anchor(loop)
 
     def sub_sizes(self, loop):
         T = self.max_tokens
         codes = _align(T * self.d * self.bits(loop) // 8)
         sz = _align(T * 2 * (self.d // 16))
-        alpha = _align(T * 2) if self.mode == 0 else 0
+        alpha = _align(T * 2) if self.mode != 1 else 0
         return codes, sz, alpha
 
     def slot_bytes(self, loop):

@@ -68,23 +68,26 @@ def test_geometry_matches_documented_layout(desc):
         assert s.slot_bytes == g.slot_bytes(loop)
 
 
-@pytest.mark.parametrize("mode,ab,rb", [(0, 4, 2), (1, 4, 2), (0, 4, 4), (0, 2, 2)])
+@pytest.mark.parametrize("mode,ab,rb", [(0, 4, 2), (1, 4, 2), (0, 4, 4), (0, 2, 2), (2, 4, 2)])
 @pytest.mark.parametrize("d", [64, 96, 128])
 def test_cache_bytes_equal_accounting(mode, ab, rb, d):
     """With max_tokens a multiple of 256 nothing is padded, so the buffer holds
     exactly bits_per_element * elements / 8 bytes."""
     desc = rq.make_desc(2, 8, 3, 5, 512, d, anchor_bits=ab, residual_bits=rb, mode=mode)
     elements = 2 * 2 * 8 * 3 * 5 * 512 * d
-    bits = O.bits_per_element(ab, rb, 16, d, 4, with_alpha=(mode == 0))
+    bits = O.bits_per_element(ab, rb, 16, d, 4, with_alpha=(mode != 1))
     assert rq.cache_bytes(desc) * 8 == bits * elements
 
 
 def test_unsupported_descriptors():
     base = dict(batch=1, loops=4, layers=1, kv_heads=2, max_tokens=16, head_dim=64)
     assert rq.validate_desc(rq.make_desc(**base)) == 0
+    assert rq.validate_desc(rq.make_desc(**base, mode=2)) == 0
     bad = [dict(head_dim=80), dict(head_dim=256), dict(group_size=32), dict(loops=6),
-           dict(anchor_bits=3), dict(residual_bits=8), dict(mode=2), dict(alpha_mode=5),
-           dict(rotation=2), dict(loops=128, loops_per_group=4)]
+           dict(anchor_bits=3), dict(residual_bits=8), dict(mode=3), dict(alpha_mode=5),
+           dict(rotation=2), dict(loops=128, loops_per_group=4),
+           dict(mode=2, loops=8, loops_per_group=8), dict(mode=2, residual_bits=4),
+           dict(max_tokens=60_000_000)]
     for kw in bad:
         args = {**base}
         extra = {k: v for k, v in kw.items() if k not in base}

@@ -172,6 +172,8 @@ VARIANTS = {
     "norm_ratio": dict(alpha_mode=1),
     "alpha_one": dict(alpha_mode=2),
     "no_rotation": dict(rotation=0),
+    "chained": dict(mode=2),
+    "chained_no_rotation": dict(mode=2, rotation=0),
 }
 
 
