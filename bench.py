@@ -315,8 +315,9 @@ def main():
     dom_bytes = sum(run.call_bytes(loop) for loop, _ in calls) // len(calls)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     two = w.mode != 1
-    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0}"
-             f"{',NR' if w.mode == 2 else ''}> + combine_kernel<{w.head_dim},{str(two).lower()}>")
+    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
+             f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()}>"
+             f" + combine_kernel<{w.head_dim},{str(two).lower()}>")
     log(f"[bench] dominant call ({kname}): {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
         f"{achieved:.0f} GB/s")
 
@@ -367,6 +368,8 @@ def main():
                    "context_tokens": w.n_tokens, "anchor_bits": w.anchor_bits,
                    "residual_bits": w.residual_bits, "group": 16,
                    "mode": {0: "residual", 1: "direct", 2: "chained"}[w.mode],
+                   "cache": (f"paged, {w.page_tokens}-token blocks in random pool order"
+                             if w.page_tokens else "contiguous"),
                    "launch": "hip graph of one step" if use_graph else "eager"},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": step_bytes,

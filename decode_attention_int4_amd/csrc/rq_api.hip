@@ -12,6 +12,7 @@
 
 namespace rq {
 int decode_tile_tokens(int d);
+int decode_wave_tokens(int d);
 int bf16_tile_tokens();
 
 // Split-K planning.  Small batch*heads products are split along the tokens
@@ -88,6 +89,33 @@ bool needs_signs(const rq_cache_desc* d) {
   return d->mode != RQ_MODE_DIRECT && d->rotation == RQ_ROT_HADAMARD;
 }
 
+// A pool descriptor of a paged cache: blocks of max_tokens tokens, a power of
+// two no smaller than one wave tile of the decode kernel (so no tile straddles
+// two blocks).  Returns log2 of the block size, or -1.
+int paged_block_shift(const rq_cache_desc* pool) {
+  const int bt = pool->max_tokens;
+  if (bt < rq::decode_wave_tokens(pool->head_dim) || (bt & (bt - 1)) != 0) return -1;
+  int sh = 0;
+  while ((1 << sh) < bt) ++sh;
+  return sh;
+}
+
+// Shared checks of the paged entry points; fills `pg`.
+rq_status check_paged(const rq_cache_desc* pool, int32_t n_seqs, const int32_t* block_table,
+                      int32_t max_blocks, rq::Paging& pg) {
+  rq_status st = check_desc(pool);
+  if (st != RQ_OK) return st;
+  const int sh = paged_block_shift(pool);
+  if (sh < 0) return RQ_ERR_UNSUPPORTED;
+  if (n_seqs <= 0 || max_blocks <= 0 || !block_table) return RQ_ERR_INVALID_ARG;
+  if (((int64_t)max_blocks << sh) > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (!aligned(block_table, 4)) return RQ_ERR_ALIGNMENT;
+  pg.table = block_table;
+  pg.max_blocks = max_blocks;
+  pg.block_shift = sh;
+  return RQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,7 +164,8 @@ rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, in
 
 static rq_status quantize_append_impl(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
                                       int32_t n_tokens, const int32_t* positions, int32_t t_new,
-                                      const int8_t* signs, void* stream) {
+                                      const int8_t* signs, void* stream, int32_t rows,
+                                      rq::Paging pg) {
   if (t_new == 0) return RQ_OK;
   if (!cache || !kv_bf16 || (needs_signs(desc) && !signs)) return RQ_ERR_INVALID_ARG;
   if (!aligned(cache, 256) || !aligned(kv_bf16, 4) || !aligned(positions, 4)) return RQ_ERR_ALIGNMENT;
@@ -148,7 +177,9 @@ static rq_status quantize_append_impl(const rq_cache_desc* desc, void* cache, co
   a.n_tokens = n_tokens;
   a.t_new = t_new;
   a.positions = positions;
-  a.items = 2ull * desc->batch * desc->layers * desc->kv_heads *
+  a.rows = rows;
+  a.paging = pg;
+  a.items = 2ull * rows * desc->layers * desc->kv_heads *
             (uint64_t)(desc->loops / desc->loops_per_group) * (uint64_t)t_new;
   return rq::launch_quant_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK
                                                                                       : RQ_ERR_LAUNCH;
@@ -160,7 +191,8 @@ rq_status rq_quantize_append(const rq_cache_desc* desc, void* cache, const uint1
   if (st != RQ_OK) return st;
   if (n_tokens < 0 || t_new < 0) return RQ_ERR_INVALID_ARG;
   if ((int64_t)n_tokens + t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
-  return quantize_append_impl(desc, cache, kv_bf16, n_tokens, nullptr, t_new, signs, stream);
+  return quantize_append_impl(desc, cache, kv_bf16, n_tokens, nullptr, t_new, signs, stream,
+                              desc->batch, rq::Paging{});
 }
 
 rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache, const uint16_t* kv_bf16,
@@ -171,7 +203,21 @@ rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache, cons
   if (t_new < 0) return RQ_ERR_INVALID_ARG;
   if (t_new > desc->max_tokens) return RQ_ERR_CAPACITY;
   if (t_new > 0 && !positions) return RQ_ERR_INVALID_ARG;
-  return quantize_append_impl(desc, cache, kv_bf16, 0, positions, t_new, signs, stream);
+  return quantize_append_impl(desc, cache, kv_bf16, 0, positions, t_new, signs, stream, desc->batch,
+                              rq::Paging{});
+}
+
+rq_status rq_paged_quantize_append(const rq_cache_desc* pool, void* cache, const uint16_t* kv_bf16,
+                                   int32_t n_seqs, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const int32_t* positions,
+                                   int32_t t_new, const int8_t* signs, void* stream) {
+  rq::Paging pg{};
+  rq_status st = check_paged(pool, n_seqs, block_table, max_blocks_per_seq, pg);
+  if (st != RQ_OK) return st;
+  if (t_new < 0) return RQ_ERR_INVALID_ARG;
+  if ((int64_t)t_new > ((int64_t)max_blocks_per_seq << pg.block_shift)) return RQ_ERR_CAPACITY;
+  if (t_new > 0 && !positions) return RQ_ERR_INVALID_ARG;
+  return quantize_append_impl(pool, cache, kv_bf16, 0, positions, t_new, signs, stream, n_seqs, pg);
 }
 
 rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int8_t* signs,
@@ -198,27 +244,39 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
                                                                                     : RQ_ERR_LAUNCH;
 }
 
-uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
-  if (check_desc(desc) != RQ_OK || q_heads <= 0) return 0;
-  const int32_t bh = desc->batch * q_heads;
+static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q_heads,
+                              int32_t max_n_tokens) {
+  if (check_desc(desc) != RQ_OK || q_heads <= 0 || rows <= 0) return 0;
+  const int32_t bh = rows * q_heads;
   const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim),
                                          rq::kDecodeTarget);
   return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
+}
+
+uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
+  return check_desc(desc) == RQ_OK ? workspace_for(desc, desc->batch, q_heads, max_n_tokens) : 0;
+}
+
+uint64_t rq_paged_decode_workspace_bytes(const rq_cache_desc* pool, int32_t q_heads, int32_t n_seqs,
+                                         int32_t max_n_tokens) {
+  return workspace_for(pool, n_seqs, q_heads, max_n_tokens);
 }
 
 static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* cache,
                                        const int8_t* signs, int32_t loop, int32_t layer,
                                        const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
                                        const int32_t* lengths, float softmax_scale, void* workspace,
-                                       uint64_t workspace_bytes, float* out, void* stream) {
+                                       uint64_t workspace_bytes, float* out, void* stream,
+                                       int32_t rows, rq::Paging pg) {
   rq_status st = check_desc(desc);
   if (st != RQ_OK) return st;
   if (loop < 0 || loop >= desc->loops || layer < 0 || layer >= desc->layers || q_heads <= 0 ||
       n_tokens < 0)
     return RQ_ERR_INVALID_ARG;
   if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
-  if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
-  const uint64_t need = rq_decode_workspace_bytes(desc, q_heads, n_tokens);
+  const int64_t cap = pg.table ? ((int64_t)pg.max_blocks << pg.block_shift) : desc->max_tokens;
+  if (n_tokens > cap) return RQ_ERR_CAPACITY;
+  const uint64_t need = workspace_for(desc, rows, q_heads, n_tokens);
   if (!cache || !q_bf16 || !out || (needs_signs(desc) && !signs) || (need && !workspace))
     return RQ_ERR_INVALID_ARG;
   if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q_bf16, 4) || !aligned(out, 4) ||
@@ -226,7 +284,7 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
     return RQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
-  const int32_t bh = desc->batch * q_heads;
+  const int32_t bh = rows * q_heads;
   const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
   const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
   const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
@@ -241,6 +299,8 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   a.out = out;
   a.partials = static_cast<float*>(workspace);
   a.lengths = lengths;
+  a.rows = rows;
+  a.paging = pg;
   a.loop = loop;
   a.layer = layer;
   a.q_heads = q_heads;
@@ -257,7 +317,8 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
                               int32_t n_tokens, float softmax_scale, void* workspace,
                               uint64_t workspace_bytes, float* out, void* stream) {
   return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, n_tokens, nullptr,
-                               softmax_scale, workspace, workspace_bytes, out, stream);
+                               softmax_scale, workspace, workspace_bytes, out, stream, desc->batch,
+                               rq::Paging{});
 }
 
 rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cache,
@@ -267,7 +328,24 @@ rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cach
                                      uint64_t workspace_bytes, float* out, void* stream) {
   if (!lengths) return RQ_ERR_INVALID_ARG;
   return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, max_n_tokens,
-                               lengths, softmax_scale, workspace, workspace_bytes, out, stream);
+                               lengths, softmax_scale, workspace, workspace_bytes, out, stream,
+                               desc->batch, rq::Paging{});
+}
+
+rq_status rq_paged_decode_attention(const rq_cache_desc* pool, const void* cache,
+                                    const int8_t* signs, int32_t loop, int32_t layer,
+                                    const uint16_t* q_bf16, int32_t q_heads, int32_t n_seqs,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* lengths, int32_t max_n_tokens,
+                                    float softmax_scale, void* workspace, uint64_t workspace_bytes,
+                                    float* out, void* stream) {
+  rq::Paging pg{};
+  rq_status st = check_paged(pool, n_seqs, block_table, max_blocks_per_seq, pg);
+  if (st != RQ_OK) return st;
+  if (!lengths) return RQ_ERR_INVALID_ARG;
+  return decode_attention_impl(pool, cache, signs, loop, layer, q_bf16, q_heads, max_n_tokens,
+                               lengths, softmax_scale, workspace, workspace_bytes, out, stream,
+                               n_seqs, pg);
 }
 
 uint64_t rq_bf16_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,

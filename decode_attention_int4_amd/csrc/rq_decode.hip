@@ -469,7 +469,11 @@ __global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
 
 // NR > 1 (chained mode): loop a.loop reads the residual planes of loops
 // a.loop .. a.loop + NR - 1, all accumulated into the one residual sum.
-template <int D, int B1, int B2, int NR>
+// PAGED: row b's tokens live in the pool blocks its block-table row names; a
+// wave tile (TPW tokens, block sizes are powers of two >= TPW) never straddles
+// two blocks, so the tile's buffer resources are rebuilt from its block's
+// slots, with the block id read through the scalar cache.
+template <int D, int B1, int B2, int NR, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   using LY = Lay<D>;
   constexpr int NG = LY::NG, LPP = LY::LPP, TPW = LY::TPW;
@@ -508,18 +512,35 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(n_row, t_begin + a.tokens_per_split);
 
-  // ---- one buffer resource per slot (codes | sz | alpha of one stream)
+  // ---- one buffer resource per slot (codes | sz | alpha of one stream); a
+  // paged call rebuilds them per tile at its block's offset from block 0
   const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
   const uint32_t sb1 = (uint32_t)g.slot_bytes[g.is_anchor(loop1) ? 0 : 1];
   const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
-  const rsrc_t rk1 = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, loop1, kvh), sb1);
-  const rsrc_t rv1 = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, loop1, kvh), sb1);
-  rsrc_t rk2[NR], rv2[NR];
+  const int brow = PAGED ? 0 : b;
+  const uint8_t* bk1 = a.cache + g.slot_offset(0, brow, a.layer, loop1, kvh);
+  const uint8_t* bv1 = a.cache + g.slot_offset(1, brow, a.layer, loop1, kvh);
+  const uint8_t *bk2[NR], *bv2[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    rk2[r] = make_rsrc(a.cache + g.slot_offset(0, b, a.layer, a.loop + r, kvh), sb2);
-    rv2[r] = make_rsrc(a.cache + g.slot_offset(1, b, a.layer, a.loop + r, kvh), sb2);
+    bk2[r] = a.cache + g.slot_offset(0, brow, a.layer, a.loop + r, kvh);
+    bv2[r] = a.cache + g.slot_offset(1, brow, a.layer, a.loop + r, kvh);
   }
+  rsrc_t rk1, rv1, rk2[NR], rv2[NR];
+  auto point_at = [&](uint64_t delta) __attribute__((always_inline)) {
+    rk1 = make_rsrc(bk1 + delta, sb1);
+    rv1 = make_rsrc(bv1 + delta, sb1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      rk2[r] = make_rsrc(bk2[r] + delta, sb2);
+      rv2[r] = make_rsrc(bv2[r] + delta, sb2);
+    }
+  };
+  if constexpr (!PAGED) point_at(0);
+  // block-table row of this sequence, read through the scalar cache
+  typedef const __attribute__((address_space(4))) int32_t c_i32;
+  const c_i32* btab = (const c_i32*)(a.paging.table + (uint64_t)b * a.paging.max_blocks);
+  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;  // one pool block
   const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
   const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
 
@@ -547,9 +568,16 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     }
   };
   auto issue = [&](int tile) __attribute__((always_inline)) {
-    const uint32_t tb = (uint32_t)(first + tile * NW * TPW);
+    uint32_t tb = (uint32_t)(first + tile * NW * TPW);
     lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
     const int vt = t_end - (int)tb;  // in-range tokens of this tile (>= 1)
+    if constexpr (PAGED) {
+      // ids outside the pool are clamped into it: garbage in, but no read
+      // outside the cache
+      const int blk = min(max(btab[tb >> a.paging.block_shift], 0), g.batch - 1);
+      point_at((uint64_t)blk * bstride);
+      tb &= (1u << a.paging.block_shift) - 1u;
+    }
     if (vt >= TPW)
       issue_t(std::integral_constant<bool, true>{}, tb, st, TPW);
     else
@@ -873,10 +901,14 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
 
 template <int D, int B1, int B2, int NR = 1>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR>), dim3(a.splits, a.g.batch * a.q_heads), dim3(NW * 64), 0, s, a);
+  const dim3 grid(a.splits, a.rows * a.q_heads);
+  if (a.paging.table)
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true>), grid, dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false>), grid, dim3(NW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D, B2 != 0>), dim3(a.g.batch * a.q_heads), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<D, B2 != 0>), dim3(a.rows * a.q_heads), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -902,6 +934,14 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int decode_wave_tokens(int d) {
+  switch (d) {
+    case 64: return Lay<64>::TPW;
+    case 96: return Lay<96>::TPW;
+    default: return Lay<128>::TPW;
+  }
+}
 
 int decode_tile_tokens(int d) {
   switch (d) {

@@ -8,14 +8,25 @@
 
 namespace rq {
 
+// Paged cache (vLLM-style block tables): the descriptor describes a pool whose
+// "batch" rows are physical blocks of max_tokens = 2^block_shift tokens, and
+// row r's logical token t lives at token t & (2^block_shift - 1) of block
+// table[r * max_blocks + (t >> block_shift)].  table == null: not paged.
+struct Paging {
+  const int32_t* table;
+  int32_t max_blocks, block_shift;
+};
+
 struct QuantArgs {
   Geometry g;
   uint8_t* cache;
   const uint16_t* kv;     // [2][B][L][layers][H][t_new][d] BF16
   const int8_t* signs;    // [2][layers][d]
   int32_t n_tokens, t_new;
-  const int32_t* positions;  // [B] first position per batch row, or null (all at n_tokens)
-  uint64_t items;         // 2*B*layers*H*(L/P)*t_new
+  const int32_t* positions;  // [rows] first position per row, or null (all at n_tokens)
+  uint64_t items;         // 2*rows*layers*H*(L/P)*t_new
+  int32_t rows;           // batch rows of kv (the descriptor's batch unless paged)
+  Paging paging;
 };
 hipError_t launch_quant_append(const QuantArgs& a, hipStream_t s);
 
@@ -39,7 +50,9 @@ struct DecodeArgs {
   const uint16_t* q;      // [B][Hq][d]
   float* out;             // [B][Hq][d]
   float* partials;        // [B*Hq][splits][2 + 2d]
-  const int32_t* lengths;  // [B] tokens per batch row (clamped to n_tokens), or null
+  const int32_t* lengths;  // [rows] tokens per row (clamped to n_tokens), or null
+  int32_t rows;           // query rows (the descriptor's batch unless paged)
+  Paging paging;
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;
   float qscale;           // softmax scale * log2(e)

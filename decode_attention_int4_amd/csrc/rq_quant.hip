@@ -139,10 +139,22 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
     c /= g.kv_heads;
     const int layer = (int)(c % g.layers);
     c /= g.layers;
-    const int b = (int)(c % g.batch);
-    const int kv = (int)(c / g.batch);
+    const int b = (int)(c % a.rows);
+    const int kv = (int)(c / a.rows);
     int pos = a.n_tokens + t;
-    if (a.positions) {
+    int slot_row = b;  // row of the cache geometry: the batch row, or a pool block
+    if (a.paging.table) {
+      // paged: the logical position picks the block from the row's table; a
+      // row whose range does not fit its table, or a token whose block id is
+      // outside the pool, is skipped (all wave-uniform)
+      const int cap = a.paging.max_blocks << a.paging.block_shift;
+      const int p0 = a.positions[b];
+      if (p0 < 0 || p0 > cap - a.t_new) continue;
+      const int lp = p0 + t;
+      slot_row = a.paging.table[(uint64_t)b * a.paging.max_blocks + (lp >> a.paging.block_shift)];
+      if (slot_row < 0 || slot_row >= g.batch) continue;
+      pos = lp & ((1 << a.paging.block_shift) - 1);
+    } else if (a.positions) {
       // per-row positions come from device memory: a row whose range does not
       // fit the cache is skipped (the whole wave agrees, b is wave-uniform)
       const int p0 = a.positions[b];
@@ -151,7 +163,7 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
     }
 
     auto src = [&](int loop) {
-      return a.kv + ((((uint64_t)(kv * g.batch + b) * g.loops + loop) * g.layers + layer) *
+      return a.kv + ((((uint64_t)(kv * a.rows + b) * g.loops + loop) * g.layers + layer) *
                          g.kv_heads + head) * (uint64_t)a.t_new * D + (uint64_t)t * D;
     };
     auto load = [&](int loop, double& x0, double& x1) {
@@ -166,7 +178,7 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
     load(aloop, x0, x1);
     const QuantResult A = quant_vec<D, AB>(x0, x1);
     {
-      uint8_t* base = a.cache + g.slot_offset(kv, b, layer, aloop, head);
+      uint8_t* base = a.cache + g.slot_offset(kv, slot_row, layer, aloop, head);
       store_codes<D, AB>(base + (uint64_t)pos * (D * AB / 8),
                          base + g.sz_rel(aloop) + (uint64_t)pos * (2 * D / 16), A, lane);
     }
@@ -181,7 +193,7 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
       const int j = chained ? g.P - 2 - jj : jj;
       const int loop = k * g.P + j;
       load(loop, x0, x1);
-      uint8_t* base = a.cache + g.slot_offset(kv, b, layer, loop, head);
+      uint8_t* base = a.cache + g.slot_offset(kv, slot_row, layer, loop, head);
       uint8_t* row = base + (uint64_t)pos * (D * RB / 8);
       uint8_t* sz_row = base + g.sz_rel(loop) + (uint64_t)pos * (2 * D / 16);
       if (g.mode == RQ_MODE_DIRECT) {

@@ -33,6 +33,7 @@ EXPORTS = (
     "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ragged",
     "rq_bf16_decode_workspace_bytes", "rq_bf16_decode_attention",
     "rq_read_probe_sink_words", "rq_read_probe",
+    "rq_paged_decode_workspace_bytes", "rq_paged_quantize_append", "rq_paged_decode_attention",
 )
 
 
@@ -97,11 +98,18 @@ def lib() -> ctypes.CDLL:
         L.rq_bf16_decode_workspace_bytes.restype = _u64
         L.rq_bf16_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
                                                ctypes.c_float, _vp, _u64, _vp, _vp]
+        L.rq_paged_decode_workspace_bytes.argtypes = [D, _i32, _i32, _i32]
+        L.rq_paged_decode_workspace_bytes.restype = _u64
+        L.rq_paged_quantize_append.argtypes = [D, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp]
+        L.rq_paged_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp,
+                                                _i32, _vp, _i32, ctypes.c_float, _vp, _u64, _vp,
+                                                _vp]
         L.rq_read_probe_sink_words.restype = ctypes.c_uint32
         L.rq_read_probe.argtypes = [_vp, _u64, _vp, _vp]
         for name in ("rq_validate_desc", "rq_cache_bytes", "rq_cache_slot", "rq_quantize_append",
                      "rq_quantize_append_ragged", "rq_reconstruct", "rq_decode_attention",
-                     "rq_decode_attention_ragged", "rq_bf16_decode_attention", "rq_read_probe"):
+                     "rq_decode_attention_ragged", "rq_bf16_decode_attention", "rq_read_probe",
+                     "rq_paged_quantize_append", "rq_paged_decode_attention"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -269,6 +277,68 @@ def decode_attention_ragged(desc: CacheDesc, cache: torch.Tensor, signs: Optiona
         max_n_tokens, float(softmax_scale), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.float32, "out"), _stream(stream)),
         "rq_decode_attention_ragged")
+    return out
+
+
+def paged_decode_workspace_bytes(pool: CacheDesc, q_heads: int, n_seqs: int,
+                                 max_n_tokens: int) -> int:
+    return int(lib().rq_paged_decode_workspace_bytes(ctypes.byref(pool), q_heads, n_seqs,
+                                                     max_n_tokens))
+
+
+def _table(block_table: torch.Tensor, n_seqs: int):
+    if block_table.dim() != 2 or block_table.shape[0] != n_seqs:
+        raise ValueError(f"block_table shape {tuple(block_table.shape)} is not [n_seqs, max_blocks]")
+    return _dev(block_table, torch.int32, "block_table"), block_table.shape[1]
+
+
+def paged_quantize_append(pool: CacheDesc, cache: torch.Tensor, kv_bf16: torch.Tensor,
+                          block_table: torch.Tensor, positions: torch.Tensor,
+                          signs: Optional[torch.Tensor], stream=None) -> None:
+    """Paged cache: pool.batch = blocks in the pool, pool.max_tokens = tokens per block.
+    kv_bf16: [2, n_seqs, loops, layers, kv_heads, t_new, d] BF16; sequence s is
+    appended at logical positions[s] through block_table[s] (device int32
+    [n_seqs, max_blocks_per_seq])."""
+    n = kv_bf16.shape[1]
+    if kv_bf16.dim() != 7 or kv_bf16.shape[0] != 2 or \
+            tuple(kv_bf16.shape[2:5]) != (pool.loops, pool.layers, pool.kv_heads) or \
+            kv_bf16.shape[6] != pool.head_dim:
+        raise ValueError(f"kv_bf16 shape {tuple(kv_bf16.shape)} does not match {pool}")
+    if tuple(positions.shape) != (n,):
+        raise ValueError(f"positions shape {tuple(positions.shape)} != ({n},)")
+    if cache.numel() < cache_bytes(pool):
+        raise ValueError("cache tensor smaller than rq_cache_bytes()")
+    tab, mb = _table(block_table, n)
+    s = _dev(signs, torch.int8, "signs") if signs is not None else None
+    _check(lib().rq_paged_quantize_append(
+        ctypes.byref(pool), _dev(cache, torch.uint8, "cache"),
+        _dev(kv_bf16, torch.bfloat16, "kv_bf16"), n, tab, mb,
+        _dev(positions, torch.int32, "positions"), kv_bf16.shape[5], s, _stream(stream)),
+        "rq_paged_quantize_append")
+
+
+def paged_decode_attention(pool: CacheDesc, cache: torch.Tensor, signs: Optional[torch.Tensor],
+                           loop: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                           lengths: torch.Tensor, max_n_tokens: int, softmax_scale: float,
+                           workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """q: [n_seqs, q_heads, d] BF16, block_table: device int32 [n_seqs, max_blocks],
+    lengths: device int32 [n_seqs] -> out [n_seqs, q_heads, d] fp32."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match {pool}")
+    n = q.shape[0]
+    if tuple(lengths.shape) != (n,):
+        raise ValueError(f"lengths shape {tuple(lengths.shape)} != ({n},)")
+    tab, mb = _table(block_table, n)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    s = _dev(signs, torch.int8, "signs") if signs is not None else None
+    _check(lib().rq_paged_decode_attention(
+        ctypes.byref(pool), _dev(cache, torch.uint8, "cache"), s, loop, layer,
+        _dev(q, torch.bfloat16, "q"), q.shape[1], n, tab, mb,
+        _dev(lengths, torch.int32, "lengths"), max_n_tokens, float(softmax_scale),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _dev(out, torch.float32, "out"), _stream(stream)), "rq_paged_decode_attention")
     return out
 
 

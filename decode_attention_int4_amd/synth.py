@@ -49,6 +49,7 @@ class Workload:
     outlier_channels: int = 2
     outlier_factor: float = 10.0
     lognormal_sigma: float = 0.5
+    page_tokens: int = 0         # > 0: paged cache of blocks this size, scattered over the pool
 
     @property
     def softmax_scale(self) -> float:
@@ -78,6 +79,9 @@ WORKLOADS = {
     # the ablation's chained (previous-loop) reference on the 8k/batch 4 shapes
     "ouro8k_b4_chained": Workload("ouro8k_b4_chained", batch=4, loops=4, layers=24, kv_heads=16,
                                   q_heads=16, head_dim=128, n_tokens=8192, mode=2),
+    # the 8k/batch 4 shapes in a paged cache: blocks of 16 tokens in random pool order
+    "ouro8k_b4_paged16": Workload("ouro8k_b4_paged16", batch=4, loops=4, layers=24, kv_heads=16,
+                                  q_heads=16, head_dim=128, n_tokens=8192, page_tokens=16),
     # Huginn-3.5B-like looped core: 4 layers x 32 loops (8 groups of 4), 55 x 96, 8k, b2.
     "huginn8k_b2": Workload("huginn8k_b2", batch=2, loops=32, layers=4, kv_heads=55,
                             q_heads=55, head_dim=96, n_tokens=8192,

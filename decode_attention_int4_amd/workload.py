@@ -12,6 +12,7 @@ from __future__ import annotations
 
 from typing import Dict, Iterable, Tuple
 
+import numpy as np
 import torch
 
 from . import rq
@@ -38,14 +39,30 @@ def desc_for(w: Workload, max_tokens: int) -> rq.CacheDesc:
 
 
 class RQDecode:
-    """A filled ResidualQuant cache plus everything one decode step needs."""
+    """A filled ResidualQuant cache plus everything one decode step needs.
+
+    With w.page_tokens > 0 the cache is a paged pool: every batch row owns
+    enough blocks for its tokens, drawn in random order from the pool the
+    way a serving allocator hands out freed blocks."""
 
     def __init__(self, w: Workload, device="cuda", keep: Iterable[SliceKey] = (),
                  chunk_tokens: int | None = None, extra_tokens: int = 1):
         self.w = w
         self.N = w.n_tokens
-        self.desc = desc_for(w, w.n_tokens + extra_tokens)
         self.device = device
+        self.paged = w.page_tokens > 0
+        self._positions: Dict[int, torch.Tensor] = {}   # device start positions of paged appends
+        if self.paged:
+            per_seq = -(-(w.n_tokens + extra_tokens) // w.page_tokens)
+            perm = np.random.default_rng(w.seed + 17).permutation(w.batch * per_seq)
+            self.table = torch.from_numpy(perm.reshape(w.batch, per_seq).astype(np.int32)).to(device)
+            self.lengths = torch.full((w.batch,), self.N, dtype=torch.int32, device=device)
+            self._positions[self.N] = torch.full((w.batch,), self.N, dtype=torch.int32,
+                                                 device=device)
+            self.desc = desc_for(w, w.page_tokens)
+            self.desc.batch = w.batch * per_seq
+        else:
+            self.desc = desc_for(w, w.n_tokens + extra_tokens)
         self.cache = rq.alloc_cache(self.desc, device)
         self.signs = rotation_signs(w).to(device)
         self.lam = channel_scales(w)
@@ -53,8 +70,9 @@ class RQDecode:
         self.fill(keep, chunk_tokens or default_chunk(w))
         self.q = queries(w, device)                       # [loops, layers, B, Hq, d]
         self.new_kv = kv_chunk(w, self.N, self.N + 1, device, self.lam)
-        self.ws = rq.alloc_workspace(rq.decode_workspace_bytes(self.desc, w.q_heads, self.N),
-                                     device)
+        ws = rq.paged_decode_workspace_bytes(self.desc, w.q_heads, w.batch, self.N) if self.paged \
+            else rq.decode_workspace_bytes(self.desc, w.q_heads, self.N)
+        self.ws = rq.alloc_workspace(ws, device)
         self.out = torch.empty(w.loops, w.layers, w.batch, w.q_heads, w.head_dim,
                                dtype=torch.float32, device=device)
 
@@ -64,20 +82,35 @@ class RQDecode:
         for t0 in range(0, self.N, chunk):
             t1 = min(self.N, t0 + chunk)
             x = kv_chunk(self.w, t0, t1, self.device, self.lam)
-            rq.quantize_append(self.desc, self.cache, x, t0, self.signs)
+            self._append(x, t0)
             for (b, layer, head) in keep:
                 parts[(b, layer, head)].append(x[:, b, :, layer, head].cpu())
             del x
         # [2, loops, N, d] BF16 on the host per kept slice
         self.kept = {k: torch.cat(v, dim=2) if v else None for k, v in parts.items()}
 
+    def _append(self, x: torch.Tensor, t0: int, stream=None) -> None:
+        if self.paged:
+            if t0 not in self._positions:
+                self._positions[t0] = torch.full((self.w.batch,), t0, dtype=torch.int32,
+                                                 device=self.device)
+            rq.paged_quantize_append(self.desc, self.cache, x, self.table, self._positions[t0],
+                                     self.signs, stream=stream)
+        else:
+            rq.quantize_append(self.desc, self.cache, x, t0, self.signs, stream=stream)
+
     def attend(self, loop: int, layer: int, stream=None) -> torch.Tensor:
+        if self.paged:
+            return rq.paged_decode_attention(self.desc, self.cache, self.signs, loop, layer,
+                                             self.q[loop, layer], self.table, self.lengths,
+                                             self.N, self.w.softmax_scale, self.ws,
+                                             out=self.out[loop, layer], stream=stream)
         return rq.decode_attention(self.desc, self.cache, self.signs, loop, layer,
                                    self.q[loop, layer], self.N, self.w.softmax_scale, self.ws,
                                    out=self.out[loop, layer], stream=stream)
 
     def append_new(self, stream=None) -> None:
-        rq.quantize_append(self.desc, self.cache, self.new_kv, self.N, self.signs, stream=stream)
+        self._append(self.new_kv, self.N, stream)
 
     def step(self, stream=None) -> None:
         for loop in range(self.w.loops):

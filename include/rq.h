@@ -232,6 +232,65 @@ rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cach
                                      uint64_t workspace_bytes, float* out, void* stream);
 
 /*
+ * Paged cache (the block-table memory manager of a batching inference server;
+ * ai4snews para. 4 places the method inside vLLM).  The cache buffer is a pool
+ * of physical blocks described by an ordinary descriptor `pool` in which
+ *   pool->batch       is the number of blocks in the pool, and
+ *   pool->max_tokens  is the tokens per block: a power of two, at least 16
+ *                     (head_dim 96, 128) or 32 (head_dim 64);
+ * the byte layout above then holds with "batch row" read as "block".  Sequence
+ * s keeps logical token t in block block_table[s * max_blocks_per_seq +
+ * t / block_tokens] at token t % block_tokens; the entries a call reads are
+ * those of the tokens it touches.  Blocks are owned and recycled by the
+ * caller; the results equal those of a contiguous cache holding the same
+ * logical tokens.
+ *   block_table  device int32 [n_seqs][max_blocks_per_seq], 4-byte aligned,
+ *                read on the device.  Capacity per sequence is
+ *                max_blocks_per_seq * block_tokens (at most 2^31 - 1).
+ */
+
+/* Workspace for rq_paged_decode_attention: as rq_decode_workspace_bytes with
+ * n_seqs rows. */
+uint64_t rq_paged_decode_workspace_bytes(const rq_cache_desc* pool, int32_t q_heads,
+                                         int32_t n_seqs, int32_t max_n_tokens);
+
+/*
+ * Quantize-and-append into a paged cache: as rq_quantize_append_ragged for
+ * n_seqs sequences, sequence s written at logical positions [positions[s],
+ * positions[s] + t_new) through its block-table row.
+ *   kv_bf16    device BF16 [2][n_seqs][loops][layers][kv_heads][t_new][d]
+ *   positions  device int32 [n_seqs]; a sequence whose range does not fit its
+ *              capacity is skipped, and so is a token whose block id is
+ *              outside [0, pool->batch) (nothing of it is written).
+ * Errors: RQ_ERR_UNSUPPORTED for a block size outside the supported set;
+ * RQ_ERR_INVALID_ARG when n_seqs or max_blocks_per_seq < 1, block_table is
+ * NULL, or positions is NULL with t_new > 0; RQ_ERR_CAPACITY when t_new
+ * exceeds the capacity per sequence.
+ */
+rq_status rq_paged_quantize_append(const rq_cache_desc* pool, void* cache, const uint16_t* kv_bf16,
+                                   int32_t n_seqs, const int32_t* block_table,
+                                   int32_t max_blocks_per_seq, const int32_t* positions,
+                                   int32_t t_new, const int8_t* signs, void* stream);
+
+/*
+ * Decode attention over a paged cache: as rq_decode_attention_ragged for
+ * n_seqs sequences (q_bf16 [n_seqs][q_heads][d], out fp32 [n_seqs][q_heads][d],
+ * lengths int32 [n_seqs] clamped to [0, max_n_tokens]).  Block ids outside
+ * [0, pool->batch) are clamped into the pool: the output of such a sequence is
+ * then unspecified, but nothing outside the cache buffer is read.
+ * Errors: as rq_paged_quantize_append for the pool and table; RQ_ERR_CAPACITY
+ * when max_n_tokens exceeds the capacity per sequence; otherwise as
+ * rq_decode_attention_ragged (workspace from rq_paged_decode_workspace_bytes).
+ */
+rq_status rq_paged_decode_attention(const rq_cache_desc* pool, const void* cache,
+                                    const int8_t* signs, int32_t loop, int32_t layer,
+                                    const uint16_t* q_bf16, int32_t q_heads, int32_t n_seqs,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* lengths, int32_t max_n_tokens,
+                                    float softmax_scale, void* workspace,
+                                    uint64_t workspace_bytes, float* out, void* stream);
+
+/*
  * Baseline: split-K flash decode over an uncompressed BF16 cache of the same
  * logical shape (the comparison the pages make against BF16 attention,
  * ai4snews para. 4).  k_cache and v_cache are device BF16

@@ -158,6 +158,57 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rq_read_probe(MISALIGNED, 16, FAKE, None) == 5
 
 
+def test_paged_entry_points_reject_bad_arguments_before_launch():
+    L = rq.lib()
+    f = ctypes.c_float(0.125)
+    # block sizes: a power of two, at least one wave tile of the decode kernel
+    for bt, d, ok in ((16, 64, False), (32, 64, True), (16, 128, True), (16, 96, True),
+                      (48, 128, False), (8, 96, False), (1024, 128, True)):
+        p = rq.make_desc(10, 4, 1, 2, bt, d)
+        st = L.rq_paged_decode_attention(ctypes.byref(p), FAKE, FAKE, 0, 0, FAKE, 2, 3, FAKE, 8,
+                                         FAKE, 8 * bt + 1, f, FAKE, 1 << 40, FAKE, None)
+        assert st == (3 if ok else 2), (bt, d)
+        st = L.rq_paged_quantize_append(ctypes.byref(p), FAKE, FAKE, 3, FAKE, 8, FAKE,
+                                        8 * bt + 1, FAKE, None)
+        assert st == (3 if ok else 2), (bt, d)
+    pool = rq.make_desc(40, 4, 1, 2, 32, 64)
+    P = ctypes.byref(pool)
+    ws = rq.paged_decode_workspace_bytes(pool, 2, 3, 256)
+
+    def dec(n_seqs=3, table=FAKE, max_blocks=8, lengths=FAKE, max_n=256, wsb=ws, work=FAKE):
+        return L.rq_paged_decode_attention(P, FAKE, FAKE, 0, 0, FAKE, 2, n_seqs, table,
+                                           max_blocks, lengths, max_n, f, work, wsb, FAKE, None)
+
+    assert dec(table=None) == 1
+    assert dec(n_seqs=0) == 1
+    assert dec(max_blocks=0) == 1
+    assert dec(lengths=None) == 1
+    assert dec(table=ODD) == 5
+    assert dec(max_n=257) == 3           # 8 blocks of 32 tokens
+    assert dec(max_blocks=1 << 27) == 2  # capacity beyond 2^31 - 1 tokens
+    need = rq.paged_decode_workspace_bytes(pool, 2, 3, 8192)
+    assert need > 0
+    assert dec(max_blocks=256, max_n=8192, wsb=need - 4) == 4
+    assert dec(max_blocks=256, max_n=8192, wsb=need, work=None) == 1
+    # the workspace is sized by the sequences, not by the pool's block count
+    assert rq.paged_decode_workspace_bytes(pool, 2, 3, 8192) == \
+        rq.decode_workspace_bytes(rq.make_desc(3, 4, 1, 2, 8192, 64), 2, 8192)
+
+    def app(table=FAKE, positions=FAKE, t_new=1, n_seqs=3, max_blocks=8):
+        return L.rq_paged_quantize_append(P, FAKE, FAKE, n_seqs, table, max_blocks, positions,
+                                          t_new, FAKE, None)
+
+    assert app(positions=None) == 1
+    assert app(positions=None, t_new=0) == 0
+    assert app(t_new=0) == 0
+    assert app(table=None) == 1
+    assert app(n_seqs=0) == 1
+    assert app(t_new=257) == 3
+    assert app(t_new=-1) == 1
+    assert app(positions=ODD) == 5
+    assert app(table=ODD) == 5
+
+
 def test_workspace_bound_is_monotone():
     for d in DESCS:
         for hq in (d.kv_heads, 2 * d.kv_heads):
