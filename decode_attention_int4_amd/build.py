@@ -16,8 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librq.so")
-SOURCES = ["rq_api.hip", "rq_quant.hip", "rq_decode.hip", "rq_bf16.hip", "rq_reconstruct.hip"]
-HEADERS = ["rq_device.h", "rq_kernels.h", "rq_layout.h"]
+SOURCES = ["rq_api.hip", "rq_quant.hip", "rq_decode.hip", "rq_gqa.hip", "rq_bf16.hip",
+           "rq_reconstruct.hip"]
+HEADERS = ["rq_device.h", "rq_kernels.h", "rq_layout.h", "rq_stage.h"]
 ARCH = os.environ.get("RQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

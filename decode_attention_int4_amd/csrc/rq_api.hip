@@ -244,12 +244,27 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
                                                                                     : RQ_ERR_LAUNCH;
 }
 
+// Whether a call runs the grouped-query kernel (one workgroup per KV head);
+// its split plan then counts (batch row, KV head) rows.
+static bool grouped(const rq_cache_desc* desc, int32_t loop, int32_t q_heads) {
+  return q_heads % desc->kv_heads == 0 &&
+         rq::gqa_supported(rq::make_geometry(*desc), loop, q_heads / desc->kv_heads);
+}
+
 static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q_heads,
                               int32_t max_n_tokens) {
   if (check_desc(desc) != RQ_OK || q_heads <= 0 || rows <= 0) return 0;
   const int32_t bh = rows * q_heads;
-  const int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim),
-                                         rq::kDecodeTarget);
+  int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim),
+                                   rq::kDecodeTarget);
+  bool any_grouped = false;
+  for (int32_t loop = 0; loop < desc->loops_per_group; ++loop)
+    any_grouped = any_grouped || grouped(desc, loop, q_heads);
+  if (any_grouped) {
+    const int32_t sg = rq::max_splits_bound(rows * desc->kv_heads, max_n_tokens,
+                                            rq::gqa_tile_tokens(), rq::kDecodeTarget);
+    s = sg > s ? sg : s;
+  }
   return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
@@ -288,9 +303,12 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
   const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
   const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
-  const rq::SplitPlan plan = rq::plan_splits(
-      bh, n_tokens, rq::decode_tile_tokens(desc->head_dim),
-      chain ? rq::kDecodeTargetChain : two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne);
+  const int32_t target =
+      chain ? rq::kDecodeTargetChain : two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne;
+  const rq::SplitPlan plan =
+      grouped(desc, loop, q_heads)
+          ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), target)
+          : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim), target);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);

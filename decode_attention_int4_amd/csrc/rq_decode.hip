@@ -47,21 +47,13 @@
 
 #include "rq_device.h"
 #include "rq_kernels.h"
+#include "rq_stage.h"
 
 #include <type_traits>
 
 namespace rq {
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-constexpr int NW = 4;              // waves per workgroup
-constexpr float kEmpty = -1e30f;   // running max of an empty stream (finite on purpose)
-constexpr float kLazy = 8.f;       // log2-domain headroom before the running max moves
-constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024, 1024)
 // Value weights enter fp16 scaled by these powers of two, so that
 // p (<= 2^8) times an FP8 scale (<= 448), times alpha for residuals, fits.
 constexpr float kWA = 1.f / 16.f, kWR = 1.f / 256.f;
@@ -96,27 +88,10 @@ struct Pairs {
   __host__ __device__ static constexpr float mult(int k) { return (float)(1u << pos(k)); }
 };
 
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return r;
-}
-
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-
 template <int BITS, int K>
 __device__ __forceinline__ h2 pair_of(uint32_t w, uint32_t magic) {
   using PR = Pairs<BITS>;
   return as_h2(and_or(PR::shift(K) ? (w >> PR::shift(K)) : w, PR::mask(K), magic));
-}
-
-// Calls f(integral_constant<K>) for K = 0..N-1 (keeps K a compile-time constant).
-template <int N, int K = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (K < N) {
-    f(std::integral_constant<int, K>{});
-    static_for<N, K + 1>(f);
-  }
 }
 
 // ------------------------------------------------------------ DPP helpers
@@ -196,29 +171,11 @@ struct Stage {
   static_assert(R1 % 4 == 0 && R2 % 4 == 0 && RS % 4 == 0, "token rows are whole dwords");
 };
 
-__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
-  // raw (unstrided) buffer; 0x00020000 is the 32-bit data format that gfx9
-  // requires for untyped buffer loads
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
 // DMA of one plane piece (BYTES of tokens ROW bytes each) from buffer offset
 // `so` into LDS `dst`: lane l of instruction c moves granule c*64 + l.  Lanes
 // past the piece, and in a partial tile lanes past `valid` (the bytes of the
 // in-range tokens), re-read the last granule in range, so nothing outside the
 // range is read and every staged value stays finite.
-// one DMA instruction of G bytes per lane (G a literal for the builtin)
-template <int G>
-__device__ __forceinline__ void dma1(rsrc_t r, lds_u8* dst, int vo, uint32_t so) {
-  if constexpr (G == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, vo, so, 0, 0);
-  else if constexpr (G == 4)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, vo, so, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 2, vo, so, 0, 0);
-}
-
 template <int BYTES, int ROW, bool FULL>
 __device__ __forceinline__ void dma_piece(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
   constexpr int G = gran_of(BYTES, ROW), STEP = 64 * G, N = span_of(BYTES, ROW) / STEP;
@@ -235,22 +192,6 @@ __device__ __forceinline__ void dma_piece(rsrc_t r, uint32_t so, int valid, lds_
   }
 }
 
-// BF16 alphas of a tile, one 2-byte DMA over all lanes (lane l lands at
-// dst + 4 l); lanes past the tile's in-range tokens re-read the last one.
-__device__ __forceinline__ void dma_alpha(rsrc_t r, uint32_t so, int tokens, lds_u8* dst, int lane) {
-  dma1<2>(r, dst, min(lane, tokens - 1) * 2, so);
-}
-
-// s_waitcnt that waits until at most n vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <int BYTES>
 __device__ __forceinline__ void lds_codes(const lds_u8* p, uint32_t* w) {
   typedef __attribute__((address_space(3))) const u32x2 l2;
@@ -263,11 +204,6 @@ __device__ __forceinline__ void lds_codes(const lds_u8* p, uint32_t* w) {
     static_assert(BYTES == 4, "a lane holds 16 codes of 2 or 4 bits");
     w[0] = *reinterpret_cast<l1*>(p);
   }
-}
-
-__device__ __forceinline__ uint32_t lds_u16(const lds_u8* p) {
-  typedef __attribute__((address_space(3))) const uint16_t lh;
-  return *reinterpret_cast<lh*>(p);
 }
 
 // One plane of one token pair as a lane sees it: 16 codes of each token and
@@ -368,45 +304,6 @@ __device__ __forceinline__ void value_acc(const PairPlane<BITS>& pp, h2 wh, h2 w
       });
     }
   }
-}
-
-// Walsh-Hadamard transform of a vector held two elements per lane (l, l+64)
-// by one wave; block diagonal 64+32 when D == 96.  Unscaled.
-template <int D>
-__device__ __forceinline__ void wave_wht(float& y0, float& y1, int lane) {
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float p0 = __shfl_xor(y0, h);
-    y0 = (lane & h) ? (p0 - y0) : (y0 + p0);
-    if constexpr (D == 128) {
-      const float p1 = __shfl_xor(y1, h);
-      y1 = (lane & h) ? (p1 - y1) : (y1 + p1);
-    } else if constexpr (D == 96) {
-      if (h < 32) {
-        const float p1 = __shfl_xor(y1, h);
-        y1 = (lane & h) ? (p1 - y1) : (y1 + p1);
-      }
-    }
-  }
-  if constexpr (D == 128) {
-    const float a = y0, b = y1;
-    y0 = a + b;
-    y1 = a - b;
-  }
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// 2^k with max|v| * 2^k in [2^13, 2^14): fp16 then holds BF16 inputs exactly.
-__device__ __forceinline__ float fp16_prescale(float maxabs) {
-  if (!(maxabs > 0.f)) return 1.f;
-  int e;
-  frexpf(maxabs, &e);
-  return ldexpf(1.f, 14 - e);
 }
 
 // Merges the split partial states (m, l, accA[D], accR[D]) of one (batch row,
@@ -951,7 +848,26 @@ int decode_tile_tokens(int d) {
   }
 }
 
+hipError_t launch_combine(const DecodeArgs& a, bool two, hipStream_t s) {
+  const dim3 grid(a.rows * a.q_heads);
+  switch (a.g.d) {
+    case 64:
+      if (two) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(64), 0, s, a);
+      break;
+    case 96:
+      if (two) hipLaunchKernelGGL((combine_kernel<96, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<96, false>), grid, dim3(64), 0, s, a);
+      break;
+    default:
+      if (two) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (gqa_supported(a.g, a.loop, a.group_ratio)) return launch_gqa(a, s);
   switch (a.g.d) {
     case 64: return launch_d<64>(a, s);
     case 96: return launch_d<96>(a, s);

@@ -1,0 +1,683 @@
+// rq_gqa.hip -- fused decode attention for grouped-query heads on matrix cores.
+//
+// When G = q_heads / kv_heads query heads share one KV head, one workgroup
+// serves all G of them for its token range, so the packed cache is read once
+// per KV head instead of once per query head.  With G heads per cached token
+// the logits and the value sums are dense contractions, and both run on
+// MFMA (v_mfma_f32_16x16x32_f16 for Q K^T, v_mfma_f32_16x16x16_f16 for P V);
+// the per-token quantization scales are folded into the code operand first:
+//
+//   * codes enter fp16 through the magic-number unpack (1024 + c), and one
+//     v_pk_fma_f16 with (s', -1024 s') turns a pair into (s' c_a, s' c_b)
+//     EXACTLY: s' is the FP8 scale times 2^-8 read straight from its bits
+//     (an e4m3 byte shifted left by 7 is an fp16 of value x 2^-8, subnormals
+//     included), and s' c has at most 8 significant bits;
+//   * queries are exact in fp16 after a power-of-two prescale per head; the
+//     rotated query H q is not, so it enters as an fp16 high and low part;
+//   * offsets z multiply per-group query sums, one more small MFMA whose
+//     K slots are (group, high/low part);
+//   * softmax weights enter the P V products as fp16 high + low parts.
+// The logit of a residual loop is q . deq(A) + alpha^K (H q) . deq(R) and
+// the value side keeps sum p deq(A^V) and sum p alpha^V deq(R^V) apart, so
+// H^T is applied once per head at the end (ai4snews summary, paragraphs 3-4).
+//
+// Layouts (lane l, r = l % 16, c = l / 16; checked against the hardware):
+//   16x16xK MFMA:  A[i][k] at lane i + 16 * (k / KP), item k % KP
+//                  B[k][n] at lane n + 16 * (k / KP), item k % KP   (KP = K / 4)
+//                  D[i][n] at lane n + 16 * (i / 4),  item i % 4
+//   Q K^T: M = 16 tokens, N = 16 query heads (G used), K = head_dim elements,
+//          so D holds S^T: lane (head r, tokens 4c..4c+3);
+//   P V:   M = 16 elements of one quantization group, K = 16 tokens,
+//          N = heads, with B = P^T read straight from the S^T layout.
+// A wave streams 16-token tiles through a private two-stage LDS ring filled
+// by buffer_load ... lds DMA.  Code and scale planes are gathered dword by
+// dword into [dword][token] order, so a lane reads the dword it needs of one
+// token (K side) or of four consecutive tokens (V side) without bank
+// conflicts.
+#include <hip/hip_runtime.h>
+
+#include "rq_device.h"
+#include "rq_kernels.h"
+#include "rq_stage.h"
+
+namespace rq {
+namespace {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int TT = 16;  // tokens per wave tile
+// Group sums of prescaled queries reach 16 * 2^14: they enter fp16 scaled by
+// 2^-4 and the offset products are scaled back in fp32.
+constexpr float kZs = 1.f / 16.f;
+
+// 64-lane dword DMAs moving 16 tokens x w dwords
+__host__ __device__ constexpr int gather_dmas(int w) { return (16 * w + 63) / 64; }
+
+template <int D, int B1, int B2>
+struct GStage {
+  static constexpr int NG = D / 16;
+  static constexpr bool TWO = B2 != 0;
+  static constexpr int W1 = D * B1 / 32, W2 = D * (TWO ? B2 : 2) / 32;  // code dwords per token
+  static constexpr int WS = NG / 2;                                     // sz dwords per token
+  static constexpr int RS = 2 * NG;                                     // sz bytes per token
+  // [dword][token] gathers of 16 * W dwords, in whole 64-lane DMA instructions
+  static constexpr int n_gather(int w) { return gather_dmas(w); }
+  static constexpr int span(int w) { return gather_dmas(w) * 256; }
+  static constexpr int k1c = 0;
+  static constexpr int k1s = k1c + span(W1);     // sz rows padded to 16 bytes: 16 tokens
+  static constexpr int v1c = k1s + 256;
+  static constexpr int v1s = v1c + span(W1);
+  static constexpr int k2c = v1s + span(WS);
+  static constexpr int k2s = k2c + (TWO ? span(W2) : 0);
+  static constexpr int v2c = k2s + (TWO ? 256 : 0);
+  static constexpr int v2s = v2c + (TWO ? span(W2) : 0);
+  static constexpr int ka = v2s + (TWO ? span(WS) : 0);
+  static constexpr int va = ka + (TWO ? 256 : 0);
+  static constexpr int BYTES = va + (TWO ? 256 : 0);
+  static constexpr int N_DMA = 2 * n_gather(W1) + 1 + n_gather(WS) +
+                               (TWO ? 2 * n_gather(W2) + 1 + n_gather(WS) + 2 : 0);
+  static constexpr int KM1 = D / 32, KM2 = D / 32;   // K-side MFMAs (32 elements each) per plane
+  static_assert(N_DMA < 64, "pending DMA count must fit vmcnt");
+};
+
+// [dword][token] gather of one plane: DMA lane p (over the instructions)
+// moves dword w = p / 16 of token p % 16; lanes past the plane, and tokens
+// past `valid` in a partial tile, re-read in-range data.
+template <int W, int ROWB, bool FULL>
+__device__ __forceinline__ void dma_gather(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
+#pragma unroll
+  for (int c = 0; c < gather_dmas(W); ++c) {
+    const int p = min(c * 64 + lane, 16 * W - 1);
+    const int w = p >> 4, m = FULL ? (p & 15) : min(p & 15, valid - 1);
+    dma1<4>(r, dst + c * 256, m * ROWB + w * 4, so);
+  }
+}
+
+// Token-major sz rows padded to four dwords: DMA lane p moves dword p % 4
+// (clamped to the row) of token p / 4.
+template <int WS, int ROWB, bool FULL>
+__device__ __forceinline__ void dma_szrows(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
+  const int m = FULL ? (lane >> 2) : min(lane >> 2, valid - 1);
+  dma1<4>(r, dst, m * ROWB + min(lane & 3, WS - 1) * 4, so);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const lds_u8* p) {
+  typedef __attribute__((address_space(3))) const uint32_t l1;
+  return *reinterpret_cast<l1*>(p);
+}
+__device__ __forceinline__ u32x4 lds_u32x4(const lds_u8* p) {
+  typedef __attribute__((address_space(3))) const u32x4 l4;
+  return *reinterpret_cast<l4*>(p);
+}
+
+__device__ __forceinline__ h2 pk_fma(h2 a, h2 b, h2 c) { return __builtin_elementwise_fma(a, b, c); }
+
+// fp16 pair (x0 * 2^-8, x1 * 2^-8) of two FP8 e4m3 bytes held at bits 0-7 and
+// 16-23 of t (other bits zero): the byte's sign moves to bit 15, its
+// exponent and mantissa bits shift left by 7.
+__device__ __forceinline__ h2 fp8pair_h(uint32_t t) {
+  return as_h2(((t & 0x007F007Fu) << 7) | ((t & 0x00800080u) << 8));
+}
+// The same for non-negative bytes (scales).
+__device__ __forceinline__ h2 fp8pair_pos_h(uint32_t t) { return as_h2(t << 7); }
+
+// selector putting byte b of src1 at byte 0 and byte b of src0 at byte 2
+// (bytes 1 and 3 zero) for v_perm_b32(src0, src1, sel)
+__device__ __forceinline__ uint32_t sel2(uint32_t b) { return b | 0x0C00u | ((4u + b) << 16) | 0x0C000000u; }
+// the same byte of one source in both halves
+__device__ __forceinline__ uint32_t sel1(uint32_t b) { return b | 0x0C00u | (b << 16) | 0x0C000000u; }
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Element index of K-side slot `slot` (0..7) of lane group c in MFMA mm:
+// the slots are the fp16 pairs of one code dword in unpack order.
+template <int BITS>
+__host__ __device__ constexpr int kslot_elem(int mm, int c, int slot) {
+  if (BITS == 4) {
+    const int w = 4 * mm + c, k = slot >> 1;
+    return 8 * w + k + 4 * (slot & 1);
+  } else {
+    const int w = 2 * mm + (c >> 1), k = 4 * (c & 1) + (slot >> 1);
+    return 16 * w + k + 8 * (slot & 1);
+  }
+}
+
+// Inverse of kslot_elem: MFMA, lane group and slot of element e.
+template <int BITS>
+__device__ __forceinline__ void kslot_of(int e, int& mm, int& c, int& slot) {
+  if (BITS == 4) {
+    const int w = e >> 3, k8 = e & 7;
+    mm = w >> 2;
+    c = w & 3;
+    slot = 2 * (k8 & 3) + (k8 >> 2);
+  } else {
+    const int w = e >> 4, k16 = e & 15, k = k16 & 7;
+    mm = w >> 1;
+    c = 2 * (w & 1) + (k >> 2);
+    slot = 2 * (k & 3) + (k16 >> 3);
+  }
+}
+
+// K-side A operand of MFMA mm for lane (token r, group c): eight codes of
+// one dword times the FP8 scale s' of their group, exact in fp16.
+template <int BITS>
+__device__ __forceinline__ h8 k_operand(const lds_u8* codes, u32x4 szrow, int mm, int r, int c,
+                                        uint32_t magic) {
+  const int w = BITS == 4 ? 4 * mm + c : 2 * mm + (c >> 1);
+  const uint32_t x = lds_u32(codes + (w * 16 + r) * 4);
+  // the dword's group (w / 2 for 4 bits, w for 2 bits) has its scale in sz
+  // row dword mm, at byte 2 (c >> 1) in both cases
+  const uint32_t sdw = szrow[mm];
+  const uint32_t sb = 2u * (uint32_t)(c >> 1);
+  const h2 sp = fp8pair_pos_h(__builtin_amdgcn_perm(sdw, sdw, sel1(sb)));
+  const h2 op = sp * (h2){(_Float16)-1024.f, (_Float16)-1024.f};
+  h8 a;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const h2 v = pk_fma(as_h2(and_or(x >> (4 * k), 0x000F000Fu, magic)), sp, op);
+      a[2 * k] = v.x;
+      a[2 * k + 1] = v.y;
+    }
+  } else {
+    const uint32_t xs = x >> (8 * (c & 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const h2 v = pk_fma(as_h2(and_or(xs >> (2 * k), 0x00030003u, magic)), sp, op);
+      a[2 * k] = v.x;
+      a[2 * k + 1] = v.y;
+    }
+  }
+  return a;
+}
+
+// K-side offset operand: slot j of lane group c is group 4 (c & 1) + j (high
+// query sums for c < 2, low for c >= 2); z' = z 2^-8 of the lane's token.
+template <int NG>
+__device__ __forceinline__ h4 kz_operand(u32x4 szrow, int c) {
+  const bool hi = c & 1;
+  uint32_t d0 = hi ? szrow[2] : szrow[0], d1 = hi ? szrow[3] : szrow[1];
+  if (NG <= 4 && hi) d0 = 0;          // groups 4-7 do not exist
+  if (NG <= 6 && hi) d1 = 0;          // groups 6-7 do not exist
+  const h2 z01 = fp8pair_h(__builtin_amdgcn_perm(d0, d0, 0x0C030C01u));
+  const h2 z23 = fp8pair_h(__builtin_amdgcn_perm(d1, d1, 0x0C030C01u));
+  return (h4){z01.x, z01.y, z23.x, z23.y};
+}
+
+// V-side A operand for group g: element e (lane row) of tokens 4c..4c+3,
+// times their scales, exact in fp16.
+template <int BITS>
+__device__ __forceinline__ h4 v_operand(const lds_u8* codes, u32x4 sz4, int g, int e, int c,
+                                        uint32_t magic) {
+  const int w = BITS == 4 ? 2 * g + (e >> 3) : g;
+  const u32x4 x = lds_u32x4(codes + (w * 16 + 4 * c) * 4);
+  const uint32_t b = BITS == 4 ? (uint32_t)((e >> 1) & 3) : (uint32_t)(e >> 2);
+  const uint32_t sh = BITS == 4 ? 4u * (uint32_t)(e & 1) : 2u * (uint32_t)(e & 3);
+  const uint32_t mask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+  const uint32_t sb = 2u * (uint32_t)(g & 1);
+  const h2 s01 = fp8pair_pos_h(__builtin_amdgcn_perm(sz4.y, sz4.x, sel2(sb)));
+  const h2 s23 = fp8pair_pos_h(__builtin_amdgcn_perm(sz4.w, sz4.z, sel2(sb)));
+  const h2 m1024 = (h2){(_Float16)-1024.f, (_Float16)-1024.f};
+  uint32_t p01 = __builtin_amdgcn_perm(x.y, x.x, sel2(b)) >> sh;
+  uint32_t p23 = __builtin_amdgcn_perm(x.w, x.z, sel2(b)) >> sh;
+  const h2 v01 = pk_fma(as_h2(and_or(p01, mask, magic)), s01, s01 * m1024);
+  const h2 v23 = pk_fma(as_h2(and_or(p23, mask, magic)), s23, s23 * m1024);
+  return (h4){v01.x, v01.y, v23.x, v23.y};
+}
+
+// V-side offset operand: row i = group (lane row), tokens 4c..4c+3.
+template <int NG>
+__device__ __forceinline__ h4 vz_operand(const lds_u8* szg, int i, int c) {
+  const int gg = min(i >> 1, NG / 2 - 1);
+  const u32x4 y = lds_u32x4(szg + (gg * 16 + 4 * c) * 4);
+  const uint32_t b = 2u * (uint32_t)(i & 1) + 1u;
+  h2 z01 = fp8pair_h(__builtin_amdgcn_perm(y.y, y.x, sel2(b)));
+  h2 z23 = fp8pair_h(__builtin_amdgcn_perm(y.w, y.z, sel2(b)));
+  if (i >= NG) z01 = z23 = (h2){(_Float16)0.f, (_Float16)0.f};
+  return (h4){z01.x, z01.y, z23.x, z23.y};
+}
+
+// v as an fp16 high part and the fp16 rounding of the rest
+__device__ __forceinline__ h2 split_hl(float v) {
+  const _Float16 h = (_Float16)v;
+  return (h2){h, (_Float16)(v - (float)h)};
+}
+
+template <int D, int B1, int B2, bool PAGED>
+__global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
+  using GS = GStage<D, B1, B2>;
+  constexpr int NG = GS::NG;
+  constexpr bool TWO = GS::TWO;
+  constexpr int B2E = TWO ? B2 : 2;
+  constexpr int KM1 = GS::KM1, KM2 = GS::KM2;
+  constexpr int R1 = D * B1 / 8, R2 = D * B2E / 8, RS = GS::RS;
+  constexpr int kRing = NW * 2 * GS::BYTES;
+  constexpr int kMerge = (2 * 16 * D + 2 * 16 * 16) * 4;
+  const Geometry& g = a.g;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kMerge ? kRing : kMerge];
+  // B operands of the Q K^T products in lane order, [mm][lane][8 halves]:
+  // the prescaled queries (exact) and the rotated queries' high and low parts
+  __shared__ __attribute__((aligned(16))) _Float16 fq[KM1][64][8];
+  __shared__ __attribute__((aligned(16))) _Float16 fuh[TWO ? KM2 : 1][64][8];
+  __shared__ __attribute__((aligned(16))) _Float16 ful[TWO ? KM2 : 1][64][8];
+  __shared__ float sqs[16][8], sus[16][8];       // per-group sums of the two
+  __shared__ float spq[16], spu[16];             // per-head prescales
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int split = blockIdx.x, bk = blockIdx.y;     // bk = batch row * kv_heads + kv head
+  const int b = bk / g.kv_heads, kvh = bk % g.kv_heads;
+  const int G = a.group_ratio;
+  const bool rotated = TWO && g.rotation == RQ_ROT_HADAMARD;
+  uint32_t magic;
+  asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kMagic));
+
+  const int n_row = a.lengths ? min(max(a.lengths[b], 0), a.n_tokens) : a.n_tokens;
+  const int t_begin = split * a.tokens_per_split;
+  const int t_end = min(n_row, t_begin + a.tokens_per_split);
+
+  // ---- buffer resources (paged: rebuilt per tile at the tile's block)
+  const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
+  const uint32_t sb1 = (uint32_t)g.slot_bytes[g.is_anchor(loop1) ? 0 : 1];
+  const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
+  const int brow = PAGED ? 0 : b;
+  const uint8_t* bk1 = a.cache + g.slot_offset(0, brow, a.layer, loop1, kvh);
+  const uint8_t* bv1 = a.cache + g.slot_offset(1, brow, a.layer, loop1, kvh);
+  const uint8_t* bk2 = a.cache + g.slot_offset(0, brow, a.layer, a.loop, kvh);
+  const uint8_t* bv2 = a.cache + g.slot_offset(1, brow, a.layer, a.loop, kvh);
+  rsrc_t rk1, rv1, rk2, rv2;
+  auto point_at = [&](uint64_t delta) __attribute__((always_inline)) {
+    rk1 = make_rsrc(bk1 + delta, sb1);
+    rv1 = make_rsrc(bv1 + delta, sb1);
+    rk2 = make_rsrc(bk2 + delta, sb2);
+    rv2 = make_rsrc(bv2 + delta, sb2);
+  };
+  if constexpr (!PAGED) point_at(0);
+  typedef const __attribute__((address_space(4))) int32_t c_i32;
+  const c_i32* btab = (const c_i32*)(a.paging.table + (uint64_t)b * a.paging.max_blocks);
+  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;
+  const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
+  const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
+
+  // ---- this wave's tiles through its two-stage ring
+  lds_u8* ring = (lds_u8*)smem + w * 2 * GS::BYTES;
+  const int first = t_begin + w * TT;
+  const int n_tiles = first < t_end ? (t_end - first + NW * TT - 1) / (NW * TT) : 0;
+  auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
+    constexpr bool F = decltype(full)::value;
+    dma_gather<GS::W1, R1, F>(rk1, tb * R1, vt, st + GS::k1c, lane);
+    dma_szrows<GS::WS, RS, F>(rk1, s1rel + tb * RS, vt, st + GS::k1s, lane);
+    dma_gather<GS::W1, R1, F>(rv1, tb * R1, vt, st + GS::v1c, lane);
+    dma_gather<GS::WS, RS, F>(rv1, s1rel + tb * RS, vt, st + GS::v1s, lane);
+    if constexpr (TWO) {
+      dma_gather<GS::W2, R2, F>(rk2, tb * R2, vt, st + GS::k2c, lane);
+      dma_szrows<GS::WS, RS, F>(rk2, s2rel + tb * RS, vt, st + GS::k2s, lane);
+      dma_gather<GS::W2, R2, F>(rv2, tb * R2, vt, st + GS::v2c, lane);
+      dma_gather<GS::WS, RS, F>(rv2, s2rel + tb * RS, vt, st + GS::v2s, lane);
+      dma_alpha(rk2, arel + tb * 2, F ? TT : vt, st + GS::ka, lane);
+      dma_alpha(rv2, arel + tb * 2, F ? TT : vt, st + GS::va, lane);
+    }
+  };
+  auto issue = [&](int tile) __attribute__((always_inline)) {
+    uint32_t tb = (uint32_t)(first + tile * NW * TT);
+    lds_u8* st = ring + (tile & 1) * GS::BYTES;
+    const int vt = t_end - (int)tb;
+    if constexpr (PAGED) {
+      const int blk = min(max(btab[tb >> a.paging.block_shift], 0), g.batch - 1);
+      point_at((uint64_t)blk * bstride);
+      tb &= (1u << a.paging.block_shift) - 1u;
+    }
+    if (vt >= TT)
+      issue_t(std::integral_constant<bool, true>{}, tb, st, TT);
+    else
+      issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
+  };
+  if (n_tiles > 0) issue(0);
+
+  // ---- query side: prescaled queries and rotated queries of the G heads
+  // (wave w takes heads w, w + 4, ...; columns n >= G stay zero)
+  for (int n = w; n < 16; n += NW) {
+    const bool v1ok = (D > 64) && (lane + 64 < D);
+    const int hq = kvh * G + n;
+    float q0 = 0.f, q1 = 0.f;
+    if (n < G) {
+      const uint16_t* qrow = a.q + ((uint64_t)b * a.q_heads + hq) * D;
+      q0 = bf16_to_f32(qrow[lane]);
+      q1 = v1ok ? bf16_to_f32(qrow[lane + 64]) : 0.f;
+    }
+    const float pq = fp16_prescale(wave_max(fmaxf(fabsf(q0), fabsf(q1))));
+    const float x0 = q0 * pq, x1 = q1 * pq;
+    {
+      int mm, cc, sl;
+      kslot_of<B1>(lane, mm, cc, sl);
+      fq[mm][n + 16 * cc][sl] = (_Float16)x0;
+      if (v1ok) {
+        kslot_of<B1>(lane + 64, mm, cc, sl);
+        fq[mm][n + 16 * cc][sl] = (_Float16)x1;
+      }
+    }
+    float s0 = x0, s1 = x1;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      s0 += __shfl_xor(s0, o);
+      s1 += __shfl_xor(s1, o);
+    }
+    if (r == 0) {
+      sqs[n][c] = s0;
+      if (c + 4 < NG) sqs[n][c + 4] = s1;
+    }
+    if (lane == 0) spq[n] = pq;
+    if constexpr (TWO) {
+      float u0 = q0, u1 = q1;
+      if (rotated) {
+        const int8_t* sg = a.signs + (uint64_t)a.layer * D;  // K signs of this layer
+        u0 *= (float)sg[lane];
+        u1 = v1ok ? u1 * (float)sg[lane + 64] : 0.f;
+        wave_wht<D>(u0, u1, lane);
+        u0 *= (D == 128) ? 0.08838834764831845f : 0.125f;
+        u1 = v1ok ? u1 * ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) : 0.f;
+      }
+      const float pu = fp16_prescale(wave_max(fmaxf(fabsf(u0), fabsf(u1))));
+      const float y0 = u0 * pu, y1 = u1 * pu;
+      {
+        int mm, cc, sl;
+        kslot_of<B2E>(lane, mm, cc, sl);
+        h2 hl = split_hl(y0);
+        fuh[mm][n + 16 * cc][sl] = hl.x;
+        ful[mm][n + 16 * cc][sl] = hl.y;
+        if (v1ok) {
+          kslot_of<B2E>(lane + 64, mm, cc, sl);
+          hl = split_hl(y1);
+          fuh[mm][n + 16 * cc][sl] = hl.x;
+          ful[mm][n + 16 * cc][sl] = hl.y;
+        }
+      }
+      float t0 = y0, t1 = y1;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        t0 += __shfl_xor(t0, o);
+        t1 += __shfl_xor(t1, o);
+      }
+      if (r == 0) {
+        sus[n][c] = t0;
+        if (c + 4 < NG) sus[n][c + 4] = t1;
+      }
+      if (lane == 0) spu[n] = pu;
+    }
+  }
+  __syncthreads();
+
+  // ---- this lane's B operands (query head r)
+  typedef __attribute__((address_space(3))) const h8 lh8;
+  h4 BzQ, BzU;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int gz = 4 * (c & 1) + j;
+    const h2 hl = gz < NG ? split_hl(sqs[r][gz] * kZs) : (h2){(_Float16)0.f, (_Float16)0.f};
+    BzQ[j] = c < 2 ? hl.x : hl.y;
+  }
+  if constexpr (TWO) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gz = 4 * (c & 1) + j;
+      const h2 hl = gz < NG ? split_hl(sus[r][gz] * kZs) : (h2){(_Float16)0.f, (_Float16)0.f};
+      BzU[j] = c < 2 ? hl.x : hl.y;
+    }
+  }
+  // logit = qscale * 2^8 * (S_A / pq + alpha S_R / pu)   (s', z' carry 2^-8)
+  const float cA = a.qscale * 256.f / spq[r];
+  const float cR = TWO ? a.qscale * 256.f / spu[r] : 0.f;
+
+  f4 OA[NG], OR_[TWO ? NG : 1], OZA = {0.f, 0.f, 0.f, 0.f}, OZR = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NG; ++i) OA[i] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (TWO ? NG : 1); ++i) OR_[i] = (f4){0.f, 0.f, 0.f, 0.f};
+  float m = kEmpty, l = 0.f;
+
+  for (int it = 0; it < n_tiles; ++it) {
+    if (it + 1 < n_tiles) {
+      issue(it + 1);
+      wait_vm<GS::N_DMA>();
+    } else {
+      wait_vm<0>();
+    }
+    const lds_u8* st = ring + (it & 1) * GS::BYTES;
+    const int vt = t_end - (first + it * NW * TT);  // in-range tokens of this tile
+
+    // ---- logits S^T (lane: head r, tokens 4c + j)
+    f4 SA = {0.f, 0.f, 0.f, 0.f};
+    {
+      const u32x4 szr = lds_u32x4(st + GS::k1s + r * 16);
+#pragma unroll
+      for (int mm = 0; mm < KM1; ++mm)
+        SA = mfma32(k_operand<B1>(st + GS::k1c, szr, mm, r, c, magic), *(lh8*)&fq[mm][lane][0], SA);
+      // the offset term starts its own accumulator: chaining a 16x16x16 MFMA
+      // onto the 16x16x32 results (C operand) gave wrong sums on gfx950
+      SA += mfma16(kz_operand<NG>(szr, c), BzQ, (f4){0.f, 0.f, 0.f, 0.f}) * (1.f / kZs);
+    }
+    f4 SR = {0.f, 0.f, 0.f, 0.f};
+    u32x4 alk = {0u, 0u, 0u, 0u}, alv = {0u, 0u, 0u, 0u};
+    if constexpr (TWO) {
+      const u32x4 szr = lds_u32x4(st + GS::k2s + r * 16);
+#pragma unroll
+      for (int mm = 0; mm < KM2; ++mm) {
+        const h8 x = k_operand<B2E>(st + GS::k2c, szr, mm, r, c, magic);
+        SR = mfma32(x, *(lh8*)&fuh[mm][lane][0], SR);
+        SR = mfma32(x, *(lh8*)&ful[mm][lane][0], SR);
+      }
+      SR += mfma16(kz_operand<NG>(szr, c), BzU, (f4){0.f, 0.f, 0.f, 0.f}) * (1.f / kZs);
+      alk = lds_u32x4(st + GS::ka + 16 * c);   // alpha of token i at byte 4 i
+      alv = lds_u32x4(st + GS::va + 16 * c);
+    }
+    float lg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = SA[j] * cA;
+      if constexpr (TWO) v = fmaf(bf16_to_f32(alk[j] & 0xFFFFu) * cR, SR[j], v);
+      lg[j] = (4 * c + j < vt) ? v : kEmpty;
+    }
+
+    // ---- online softmax per head (the four lanes of a head agree)
+    float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx > m + kLazy) {
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
+      l *= corr;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) OA[i] *= corr;
+      OZA *= corr;
+      if constexpr (TWO) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) OR_[i] *= corr;
+        OZR *= corr;
+      }
+      m = mx;
+    }
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = (4 * c + j < vt) ? __builtin_amdgcn_exp2f(lg[j] - m) : 0.f;
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    h4 Ph, Pl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h2 hl = split_hl(p[j]);
+      Ph[j] = hl.x;
+      Pl[j] = hl.y;
+    }
+
+    // ---- values: O^T[e][head] per group, and the offset sums per group
+    {
+      u32x4 sz4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int gq = 0; gq < NG; ++gq) {
+        if ((gq & 1) == 0) sz4 = lds_u32x4(st + GS::v1s + ((gq >> 1) * 16 + 4 * c) * 4);
+        const h4 x = v_operand<B1>(st + GS::v1c, sz4, gq, r, c, magic);
+        OA[gq] = mfma16(x, Ph, OA[gq]);
+        OA[gq] = mfma16(x, Pl, OA[gq]);
+      }
+      const h4 z = vz_operand<NG>(st + GS::v1s, r, c);
+      OZA = mfma16(z, Ph, OZA);
+      OZA = mfma16(z, Pl, OZA);
+    }
+    if constexpr (TWO) {
+      h4 Qh, Ql;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h2 hl = split_hl(p[j] * bf16_to_f32(alv[j] & 0xFFFFu));
+        Qh[j] = hl.x;
+        Ql[j] = hl.y;
+      }
+      u32x4 sz4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int gq = 0; gq < NG; ++gq) {
+        if ((gq & 1) == 0) sz4 = lds_u32x4(st + GS::v2s + ((gq >> 1) * 16 + 4 * c) * 4);
+        const h4 x = v_operand<B2E>(st + GS::v2c, sz4, gq, r, c, magic);
+        OR_[gq] = mfma16(x, Qh, OR_[gq]);
+        OR_[gq] = mfma16(x, Ql, OR_[gq]);
+      }
+      const h4 z = vz_operand<NG>(st + GS::v2s, r, c);
+      OZR = mfma16(z, Qh, OZR);
+      OZR = mfma16(z, Ql, OZR);
+    }
+  }
+
+  // ---- merge the waves: running max per head, then the sums in wave order
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (c == 0) {
+    sm_m[w][r] = m;
+    sm_l[w][r] = l;
+  }
+  __syncthreads();  // every wave is done with its ring: the merge buffers reuse it
+  float M = sm_m[0][r];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][r]);
+  const float f = exp2f(m - M) * 256.f;  // also takes out the 2^-8 of s' and z'
+  float* bufA = reinterpret_cast<float*>(smem);        // [16 heads][D]
+  float* bufR = bufA + 16 * D;
+  float* bufZA = bufR + 16 * D;                        // [16 heads][16 groups]
+  float* bufZR = bufZA + 16 * 16;
+  for (int ww = 0; ww < NW; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 16 * gq + 4 * c + j;
+          bufA[r * D + e] = (ww ? bufA[r * D + e] : 0.f) + f * OA[gq][j];
+          if constexpr (TWO) bufR[r * D + e] = (ww ? bufR[r * D + e] : 0.f) + f * OR_[gq][j];
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        bufZA[r * 16 + i] = (ww ? bufZA[r * 16 + i] : 0.f) + f * OZA[j];
+        if constexpr (TWO) bufZR[r * 16 + i] = (ww ? bufZR[r * 16 + i] : 0.f) + f * OZR[j];
+      }
+    }
+    __syncthreads();
+  }
+  auto head_l = [&](int n) {
+    float s = 0.f, Mn = sm_m[0][n];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s = fmaf(exp2f(sm_m[ww][n] - Mn), sm_l[ww][n], s);
+    return s;
+  };
+  auto head_m = [&](int n) {
+    float Mn = sm_m[0][n];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
+    return Mn;
+  };
+  auto accA = [&](int n, int e) { return bufA[n * D + e] + bufZA[n * 16 + (e >> 4)]; };
+  auto accR = [&](int n, int e) { return TWO ? bufR[n * D + e] + bufZR[n * 16 + (e >> 4)] : 0.f; };
+
+  if (a.splits > 1) {
+    // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
+    // kernel writes it, for the combine kernel
+    constexpr int Wd = 2 + 2 * D;
+    for (int i = tid; i < G * Wd; i += NW * 64) {
+      const int n = i / Wd, k = i % Wd;
+      const int bh = b * a.q_heads + kvh * G + n;
+      float* mine = a.partials + ((uint64_t)bh * a.splits + split) * Wd;
+      float v;
+      if (k == 0) v = head_m(n);
+      else if (k == 1) v = head_l(n);
+      else if (k < 2 + D) v = accA(n, k - 2);
+      else v = accR(n, k - 2 - D);
+      mine[k] = v;
+    }
+    return;
+  }
+  // ---- a single split: finish here, one wave per head
+  const bool v1ok = (D > 64) && (lane + 64 < D);
+  for (int n = w; n < G; n += NW) {
+    const float Ln = head_l(n);
+    const float A0 = accA(n, lane), A1 = v1ok ? accA(n, lane + 64) : 0.f;
+    float R0 = accR(n, lane), R1 = v1ok ? accR(n, lane + 64) : 0.f;
+    if (rotated) {
+      wave_wht<D>(R0, R1, lane);
+      const int8_t* sg = a.signs + ((uint64_t)g.layers + a.layer) * D;  // V signs
+      R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
+      if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
+    }
+    const float inv = Ln > 0.f ? 1.f / Ln : 0.f;
+    const uint64_t bh = (uint64_t)b * a.q_heads + kvh * G + n;
+    a.out[bh * D + lane] = (A0 + R0) * inv;
+    if (v1ok) a.out[bh * D + lane + 64] = (A1 + R1) * inv;
+  }
+}
+
+template <int D, int B1, int B2>
+hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.rows * a.g.kv_heads);
+  if (a.paging.table)
+    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, true>), grid, dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, false>), grid, dim3(NW * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_combine(a, B2 != 0, s);
+}
+
+template <int D>
+hipError_t launch_gqa_d(const DecodeArgs& a, hipStream_t s) {
+  const Geometry& g = a.g;
+  if (g.mode == RQ_MODE_DIRECT || g.is_anchor(a.loop))
+    return g.bits_of(a.loop) == 4 ? launch_gqa_t<D, 4, 0>(a, s) : launch_gqa_t<D, 2, 0>(a, s);
+  return g.anchor_bits == 4 ? launch_gqa_t<D, 4, 2>(a, s) : launch_gqa_t<D, 2, 2>(a, s);
+}
+
+}  // namespace
+
+int gqa_tile_tokens() { return NW * TT; }
+
+bool gqa_supported(const Geometry& g, int loop, int group_ratio) {
+  if (group_ratio < 2 || group_ratio > 16) return false;
+  if (g.mode == RQ_MODE_DIRECT || g.is_anchor(loop)) return true;   // one plane of 2 or 4 bits
+  if (g.mode == RQ_MODE_CHAINED && g.P - 1 - loop % g.P > 1) return false;
+  return g.residual_bits == 2;
+}
+
+hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s) {
+  switch (a.g.d) {
+    case 64: return launch_gqa_d<64>(a, s);
+    case 96: return launch_gqa_d<96>(a, s);
+    default: return launch_gqa_d<128>(a, s);
+  }
+}
+
+}  // namespace rq

@@ -58,6 +58,13 @@ struct DecodeArgs {
   float qscale;           // softmax scale * log2(e)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// the split-merge kernel shared by the decode kernels (`two`: residual sums present)
+hipError_t launch_combine(const DecodeArgs& a, bool two, hipStream_t s);
+// grouped-query decode on matrix cores: one workgroup per (split, batch row,
+// KV head) serves the group_ratio query heads of the KV head
+bool gqa_supported(const Geometry& g, int loop, int group_ratio);
+hipError_t launch_gqa(const DecodeArgs& a, hipStream_t s);
+int gqa_tile_tokens();
 
 struct Bf16DecodeArgs {
   int32_t batch, loops, layers, kv_heads, max_tokens, d;

@@ -82,6 +82,12 @@ WORKLOADS = {
     # the 8k/batch 4 shapes in a paged cache: blocks of 16 tokens in random pool order
     "ouro8k_b4_paged16": Workload("ouro8k_b4_paged16", batch=4, loops=4, layers=24, kv_heads=16,
                                   q_heads=16, head_dim=128, n_tokens=8192, page_tokens=16),
+    # grouped-query variants of the Ouro-like shapes with the same KV bytes per call
+    # (64 (batch, KV head) rows x 8192 tokens): 4 and 8 query heads per KV head
+    "ouro8k_b16_gqa4": Workload("ouro8k_b16_gqa4", batch=16, loops=4, layers=24, kv_heads=4,
+                                q_heads=16, head_dim=128, n_tokens=8192),
+    "ouro8k_b32_gqa8": Workload("ouro8k_b32_gqa8", batch=32, loops=4, layers=24, kv_heads=2,
+                                q_heads=16, head_dim=128, n_tokens=8192),
     # Huginn-3.5B-like looped core: 4 layers x 32 loops (8 groups of 4), 55 x 96, 8k, b2.
     "huginn8k_b2": Workload("huginn8k_b2", batch=2, loops=32, layers=4, kv_heads=55,
                             q_heads=55, head_dim=96, n_tokens=8192,
