@@ -93,9 +93,9 @@ def dominant_calls(run):
 
 
 def dominant_kernel_ms(run, steps: int, torch, use_graph: bool):
-    """Average duration of one dominant call (its decode kernel and split-combine
-    kernel), from events on the stream the kernels run on around `steps`
-    back-to-back passes over all dominant calls of a step."""
+    """Average duration of one dominant call (one decode kernel launch, which
+    also merges its splits), from events on the stream the kernel runs on
+    around `steps` back-to-back passes over all dominant calls of a step."""
     calls = dominant_calls(run)
 
     def once():
@@ -315,9 +315,12 @@ def main():
     dom_bytes = sum(run.call_bytes(loop) for loop, _ in calls) // len(calls)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     two = w.mode != 1
-    kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
-             f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()}>"
-             f" + combine_kernel<{w.head_dim},{str(two).lower()}>")
+    if w.q_heads > w.kv_heads:
+        kname = (f"gqa_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
+                 f"{str(w.page_tokens > 0).lower()}>")
+    else:
+        kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
+                 f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()}>")
     log(f"[bench] dominant call ({kname}): {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
         f"{achieved:.0f} GB/s")
 

@@ -244,6 +244,12 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
                                                                                     : RQ_ERR_LAUNCH;
 }
 
+// The workspace starts with a fixed block of split-arrival counters, one per
+// (row, query head), so that calls of any shape find them at the same place
+// and never overlap another call's partial states; the partial states follow.
+static constexpr int32_t kMaxRowHeads = 1 << 16;  // also the grid's y extent
+static constexpr uint64_t kCounterBytes = (uint64_t)kMaxRowHeads * 4u;
+
 // Whether a call runs the grouped-query kernel (one workgroup per KV head);
 // its split plan then counts (batch row, KV head) rows.
 static bool grouped(const rq_cache_desc* desc, int32_t loop, int32_t q_heads) {
@@ -265,7 +271,7 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
                                             rq::gqa_tile_tokens(), rq::kDecodeTarget);
     s = sg > s ? sg : s;
   }
-  return s > 1 ? (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
+  return s > 1 ? kCounterBytes + (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
@@ -289,6 +295,7 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
       n_tokens < 0)
     return RQ_ERR_INVALID_ARG;
   if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
+  if ((int64_t)rows * q_heads > kMaxRowHeads) return RQ_ERR_UNSUPPORTED;
   const int64_t cap = pg.table ? ((int64_t)pg.max_blocks << pg.block_shift) : desc->max_tokens;
   if (n_tokens > cap) return RQ_ERR_CAPACITY;
   const uint64_t need = workspace_for(desc, rows, q_heads, n_tokens);
@@ -315,7 +322,8 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   a.signs = signs;
   a.q = q_bf16;
   a.out = out;
-  a.partials = static_cast<float*>(workspace);
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kCounterBytes);
   a.lengths = lengths;
   a.rows = rows;
   a.paging = pg;

@@ -39,10 +39,12 @@
 //   raised when a logit exceeds it by 8 (log2 units), so the rescale of the
 //   accumulators is rare.  Lanes are merged with DPP row rotations and LDS.
 //   With one split the workgroup's first wave applies H^T and writes the fp32
-//   output; otherwise each workgroup stores its partial state and a small
-//   combine kernel merges the splits.  The kernel boundary orders the two:
-//   merging in the last workgroup to finish would need an agent-scope release
-//   per workgroup, an L2 write-back that costs far more than the extra launch.
+//   output; otherwise each workgroup stores its partial state with
+//   write-through (device-scope) stores, waits for them to complete and takes
+//   a ticket from the row's counter, and the workgroup holding the last
+//   ticket reads all partial states with device-scope loads and merges them.
+//   No cache write-back or invalidation is needed (a release fence per
+//   workgroup, an L2 write-back, cost far more than a separate merge kernel).
 #include <hip/hip_runtime.h>
 
 #include "rq_device.h"
@@ -306,64 +308,6 @@ __device__ __forceinline__ void value_acc(const PairPlane<BITS>& pp, h2 wh, h2 w
   }
 }
 
-// Merges the split partial states (m, l, accA[D], accR[D]) of one (batch row,
-// query head), applies H^T to the residual sum and writes the fp32 output;
-// one wave per workgroup, two elements per lane.  Splits are merged online,
-// sixteen per round, so each round's loads issue together and the merge
-// waits on memory about once per sixteen splits.
-template <int D, bool TWO>
-__global__ void __launch_bounds__(64) combine_kernel(DecodeArgs a) {
-  constexpr int W = 2 + 2 * D;
-  const int bh = blockIdx.x, lane = threadIdx.x, ns = a.splits;
-  const bool v1ok = (D > 64) && (lane + 64 < D);
-  const float* all = a.partials + (uint64_t)bh * ns * W;
-  auto ld = [](const float* p) { return *p; };
-  float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
-  constexpr int R = 16;  // splits per round
-  for (int s0 = 0; s0 < ns; s0 += R) {
-    float ms[R], ls[R], a0[R], a1[R], r0[R], r1[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int sj = min(s0 + j, ns - 1);
-      const float* ps = all + (uint64_t)sj * W;
-      ms[j] = (s0 + j < ns) ? ld(ps) : kEmpty;
-      ls[j] = ld(ps + 1);
-      a0[j] = ld(ps + 2 + lane);
-      a1[j] = v1ok ? ld(ps + 2 + lane + 64) : 0.f;
-      r0[j] = TWO ? ld(ps + 2 + D + lane) : 0.f;
-      r1[j] = (TWO && v1ok) ? ld(ps + 2 + D + lane + 64) : 0.f;
-    }
-    float Mn = M;
-#pragma unroll
-    for (int j = 0; j < R; ++j) Mn = fmaxf(Mn, ms[j]);
-    const float c = exp2f(M - Mn);
-    L *= c;
-    A0 *= c;
-    A1 *= c;
-    R0 *= c;
-    R1 *= c;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float f = exp2f(ms[j] - Mn);
-      L = fmaf(f, ls[j], L);
-      A0 = fmaf(f, a0[j], A0);
-      A1 = fmaf(f, a1[j], A1);
-      R0 = fmaf(f, r0[j], R0);
-      R1 = fmaf(f, r1[j], R1);
-    }
-    M = Mn;
-  }
-  if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
-    wave_wht<D>(R0, R1, lane);
-    const int8_t* sg = a.signs + ((uint64_t)a.g.layers + a.layer) * D;  // V signs
-    R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
-    if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  a.out[(uint64_t)bh * D + lane] = (A0 + R0) * inv;
-  if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
-}
-
 // NR > 1 (chained mode): loop a.loop reads the residual planes of loops
 // a.loop .. a.loop + NR - 1, all accumulated into the one residual sum.
 // PAGED: row b's tokens live in the pool blocks its block-table row names; a
@@ -389,6 +333,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   __shared__ float s_scale[2];
   __shared__ __attribute__((aligned(16))) uint32_t spre[8][32];  // per-group query pairs
   __shared__ float sm_m[NW];
+  __shared__ uint32_t s_ticket;
   typedef float AccRows[LY::PAIRS][kRow];
   AccRows* sm_acc = reinterpret_cast<AccRows*>(smem);             // [wave][pair][accA | accR | l]
 
@@ -762,17 +707,19 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     return s;
   };
   if (a.splits > 1) {
-    // partial state (m, l, accA[D], accR[D]) for the combine kernel; the
-    // kernel boundary orders these stores before its loads
+    // partial state (m, l, accA[D], accR[D]) of this split; the workgroup
+    // that finishes the row last merges all of them
     float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + 2 * D);
     for (int i = tid; i <= 2 * D; i += NW * 64) {
       if (i == 2 * D) {
-        mine[0] = M;
-        mine[1] = merged(kRow - 1);
+        store_dev(mine, M);
+        store_dev(mine + 1, merged(kRow - 1));
       } else {
-        mine[2 + i] = (TWO || i < D) ? merged(i) : 0.f;
+        store_dev(mine + 2 + i, (TWO || i < D) ? merged(i) : 0.f);
       }
     }
+    if (!arrive_last(a, bh, tid, &s_ticket) || w != 0) return;
+    merge_row<D, TWO>(a, bh, lane);
     return;
   }
   // ---- a single split: finish here (first wave, two elements per lane)
@@ -803,9 +750,6 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true>), grid, dim3(NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false>), grid, dim3(NW * 64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D, B2 != 0>), dim3(a.rows * a.q_heads), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -846,24 +790,6 @@ int decode_tile_tokens(int d) {
     case 96: return NW * Lay<96>::TPW;
     default: return NW * Lay<128>::TPW;
   }
-}
-
-hipError_t launch_combine(const DecodeArgs& a, bool two, hipStream_t s) {
-  const dim3 grid(a.rows * a.q_heads);
-  switch (a.g.d) {
-    case 64:
-      if (two) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(64), 0, s, a);
-      break;
-    case 96:
-      if (two) hipLaunchKernelGGL((combine_kernel<96, true>), grid, dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((combine_kernel<96, false>), grid, dim3(64), 0, s, a);
-      break;
-    default:
-      if (two) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(64), 0, s, a);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

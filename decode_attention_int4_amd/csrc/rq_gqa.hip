@@ -271,6 +271,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   __shared__ float sqs[16][8], sus[16][8];       // per-group sums of the two
   __shared__ float spq[16], spu[16];             // per-head prescales
   __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ uint32_t s_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -607,7 +608,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 
   if (a.splits > 1) {
     // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
-    // kernel writes it, for the combine kernel
+    // kernel writes it
     constexpr int Wd = 2 + 2 * D;
     for (int i = tid; i < G * Wd; i += NW * 64) {
       const int n = i / Wd, k = i % Wd;
@@ -618,8 +619,13 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       else if (k == 1) v = head_l(n);
       else if (k < 2 + D) v = accA(n, k - 2);
       else v = accR(n, k - 2 - D);
-      mine[k] = v;
+      store_dev(mine + k, v);
     }
+    // the workgroup that finishes the KV head last merges its G rows (one
+    // counter per KV head: that of its first query head)
+    const int bh0 = b * a.q_heads + kvh * G;
+    if (!arrive_last(a, bh0, tid, &s_ticket)) return;
+    for (int n = w; n < G; n += NW) merge_row<D, TWO>(a, bh0 + n, lane);
     return;
   }
   // ---- a single split: finish here, one wave per head
@@ -648,9 +654,7 @@ hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gqa_kernel<D, B1, B2, true>), grid, dim3(NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((gqa_kernel<D, B1, B2, false>), grid, dim3(NW * 64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  return launch_combine(a, B2 != 0, s);
+  return hipGetLastError();
 }
 
 template <int D>

@@ -42,7 +42,8 @@ struct ReconArgs {
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 
 // Split-K decode: with more than one split, partial states live in the
-// workspace and a combine kernel merges them.
+// workspace, and the workgroup that finishes a row last (by a ticket counter
+// per row, also in the workspace) merges them.
 struct DecodeArgs {
   Geometry g;
   const uint8_t* cache;
@@ -50,6 +51,7 @@ struct DecodeArgs {
   const uint16_t* q;      // [B][Hq][d]
   float* out;             // [B][Hq][d]
   float* partials;        // [B*Hq][splits][2 + 2d]
+  uint32_t* counters;     // [B*Hq] split arrivals, zero between calls
   const int32_t* lengths;  // [rows] tokens per row (clamped to n_tokens), or null
   int32_t rows;           // query rows (the descriptor's batch unless paged)
   Paging paging;
@@ -58,8 +60,6 @@ struct DecodeArgs {
   float qscale;           // softmax scale * log2(e)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-// the split-merge kernel shared by the decode kernels (`two`: residual sums present)
-hipError_t launch_combine(const DecodeArgs& a, bool two, hipStream_t s);
 // grouped-query decode on matrix cores: one workgroup per (split, batch row,
 // KV head) serves the group_ratio query heads of the KV head
 bool gqa_supported(const Geometry& g, int loop, int group_ratio);

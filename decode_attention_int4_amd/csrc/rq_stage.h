@@ -8,6 +8,8 @@
 
 #include <type_traits>
 
+#include "rq_kernels.h"
+
 namespace rq {
 namespace {
 
@@ -129,6 +131,92 @@ __device__ __forceinline__ float fp16_prescale(float maxabs) {
   int e;
   frexpf(maxabs, &e);
   return ldexpf(1.f, 14 - e);
+}
+
+
+// ------------------------------------------------------------ split-K merge
+// Device-wide (agent scope) relaxed accesses.  Stores write through to the
+// memory level that all XCDs share and loads read from it (global_store and
+// global_load with sc1), so partial states pass between workgroups on
+// different XCDs without cache write-backs or invalidations.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of a workgroup once its partial states are stored
+// with store_dev.  Each wave first waits until its own stores have completed,
+// then one thread takes a ticket from counter `ctr`; the workgroup that
+// arrives last sees every other partial already written, resets the counter
+// to zero for the next call and returns true.  `ticket` is a word of LDS.
+__device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int ctr, int tid, uint32_t* ticket) {
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0)
+    *ticket = __hip_atomic_fetch_add(a.counters + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const bool last = *ticket == (uint32_t)a.splits - 1u;
+  if (last && tid == 0) __hip_atomic_store(a.counters + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Merges the split partial states (m, l, accA[D], accR[D]) of one (batch row,
+// query head), applies H^T to the residual sum and writes the fp32 output;
+// one wave, two elements per lane.  Splits are merged online, sixteen per
+// round, so each round's loads issue together and the merge waits on memory
+// about once per sixteen splits.
+template <int D, bool TWO>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane) {
+  constexpr int W = 2 + 2 * D;
+  const int ns = a.splits;
+  const bool v1ok = (D > 64) && (lane + 64 < D);
+  const float* all = a.partials + (uint64_t)bh * ns * W;
+  float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
+  constexpr int R = 16;  // splits per round
+  for (int s0 = 0; s0 < ns; s0 += R) {
+    float ms[R], ls[R], a0[R], a1[R], r0[R], r1[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int sj = min(s0 + j, ns - 1);
+      const float* ps = all + (uint64_t)sj * W;
+      ms[j] = (s0 + j < ns) ? load_dev(ps) : kEmpty;
+      ls[j] = load_dev(ps + 1);
+      a0[j] = load_dev(ps + 2 + lane);
+      a1[j] = v1ok ? load_dev(ps + 2 + lane + 64) : 0.f;
+      r0[j] = TWO ? load_dev(ps + 2 + D + lane) : 0.f;
+      r1[j] = (TWO && v1ok) ? load_dev(ps + 2 + D + lane + 64) : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < R; ++j) Mn = fmaxf(Mn, ms[j]);
+    const float c = exp2f(M - Mn);
+    L *= c;
+    A0 *= c;
+    A1 *= c;
+    R0 *= c;
+    R1 *= c;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float f = exp2f(ms[j] - Mn);
+      L = fmaf(f, ls[j], L);
+      A0 = fmaf(f, a0[j], A0);
+      A1 = fmaf(f, a1[j], A1);
+      R0 = fmaf(f, r0[j], R0);
+      R1 = fmaf(f, r1[j], R1);
+    }
+    M = Mn;
+  }
+  if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
+    wave_wht<D>(R0, R1, lane);
+    const int8_t* sg = a.signs + ((uint64_t)a.g.layers + a.layer) * D;  // V signs
+    R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
+    if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  a.out[(uint64_t)bh * D + lane] = (A0 + R0) * inv;
+  if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
 }
 
 }  // namespace

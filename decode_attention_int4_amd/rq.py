@@ -180,8 +180,9 @@ def alloc_cache(desc: CacheDesc, device="cuda") -> torch.Tensor:
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """Workspace for split-K partial states (no initialization needed)."""
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """Workspace for split-K states, zero-filled once as the library requires
+    (its split counters must start at zero; every call leaves them at zero)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- device calls

@@ -184,7 +184,9 @@ rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache,
                                     int32_t t_new, const int8_t* signs, void* stream);
 
 /* Bytes of workspace rq_decode_attention needs for `q_heads` query heads and
- * any n_tokens <= max_n_tokens. */
+ * any n_tokens <= max_n_tokens (0 when no call of that size splits the
+ * tokens).  The workspace starts with a fixed block of 65536 split counters
+ * followed by the split partial states; see rq_decode_attention. */
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
                                    int32_t max_n_tokens);
 
@@ -200,11 +202,17 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
  *   q_bf16     device BF16 [batch][q_heads][d], contiguous, 4-byte aligned
  *   workspace  device, >= rq_decode_workspace_bytes(desc, q_heads, n_tokens),
  *              256-byte aligned (may be NULL when that size is 0).  Holds the
- *              split-K partial states between the decode kernel and the
- *              combine kernel; needs no initialization.  Calls that share a
- *              workspace must be ordered (same stream), not concurrent.
+ *              split-K partial states and, in its first 256 KiB, one arrival
+ *              counter per (batch row, query head): the workgroup that
+ *              finishes a row last merges the row's partial states.  Those
+ *              counters must be ZERO before a workspace is first used (fill
+ *              it with zeros once); every call returns the counters it used
+ *              to zero, so the workspace then serves any sequence of calls of
+ *              any shape.  Calls that share a workspace must be ordered (same
+ *              stream), not concurrent.
  *   out        device fp32 [batch][q_heads][d]; n_tokens == 0 writes zeros.
- * Errors: RQ_ERR_UNSUPPORTED when q_heads is not a multiple of kv_heads;
+ * Errors: RQ_ERR_UNSUPPORTED when q_heads is not a multiple of kv_heads or
+ * batch * q_heads exceeds 65536;
  * RQ_ERR_CAPACITY when n_tokens > max_tokens; RQ_ERR_WORKSPACE.
  */
 rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache,
@@ -250,7 +258,7 @@ rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cach
  */
 
 /* Workspace for rq_paged_decode_attention: as rq_decode_workspace_bytes with
- * n_seqs rows. */
+ * n_seqs rows (same layout and zero-once rule). */
 uint64_t rq_paged_decode_workspace_bytes(const rq_cache_desc* pool, int32_t q_heads,
                                          int32_t n_seqs, int32_t max_n_tokens);
 

@@ -93,23 +93,56 @@ def test_tiny_step_and_append(tiny):
                 assert np.array_equal(getattr(g, name), getattr(e, name)), name
 
 
-def test_workspace_needs_no_initialization():
-    """A NaN-filled workspace and a NaN-filled output do not leak into results
-    (several splits, so the combine kernel reads what the decode kernel wrote)."""
-    w = Workload("ws_poison", batch=2, loops=4, layers=1, kv_heads=2, q_heads=2, head_dim=128,
+def test_workspace_zeroed_once_serves_calls_of_any_shape():
+    """The workspace's counter block is zeroed once; its partial-state area may
+    hold anything (NaN here).  Calls of different shapes then share it: several
+    split counts, per-head and grouped-query kernels, ragged rows; every
+    result matches the oracle and every counter is back to zero afterwards.
+    Repeated alternating calls give bit-identical outputs each time, so no
+    merge reads a partial state left by an earlier call."""
+    w = Workload("ws_share", batch=2, loops=4, layers=1, kv_heads=2, q_heads=4, head_dim=128,
                  n_tokens=4000, seed=5)
     keep = [(1, 0, 1)]
     run = RQDecode(w, keep=keep)
-    need = rq.decode_workspace_bytes(run.desc, w.q_heads, run.N)
-    assert need > 0
+    need = max(rq.decode_workspace_bytes(run.desc, hq, run.N) for hq in (2, 4))
+    counter_bytes = 1 << 18
+    assert need > counter_bytes
     ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
-    out = torch.full((2, 2, 128), float("nan"), device="cuda")
+    ws[:counter_bytes].zero_()
+    out = torch.full((2, 4, 128), float("nan"), device="cuda")
     ek, ev, HK, HV = encode_kept(w, run.kept[keep[0]], 0)
+    lengths = torch.tensor([3000, 4000], dtype=torch.int32, device="cuda")
+    q2 = run.q[:, 0][:, :, ::2].contiguous()      # 2 query heads = one per KV head
+    calls = []
     for loop in range(4):
-        rq.decode_attention(run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], run.N,
-                            w.softmax_scale, ws, out=out)
-        ref = oracle_attention(w, ek, ev, HK, HV, bits16(run.q[loop, 0, 1, 1]), loop, run.N)
-        assert_close_attention(out[1, 1].cpu().numpy(), ref, f"poisoned workspace loop {loop}")
+        calls.append(("grouped", loop, lambda loop=loop: rq.decode_attention(
+            run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], run.N, w.softmax_scale, ws,
+            out=out)))
+        calls.append(("per-head", loop, lambda loop=loop: rq.decode_attention(
+            run.desc, run.cache, run.signs, loop, 0, q2[loop], run.N, w.softmax_scale, ws,
+            out=out[:, :2].contiguous())))
+        calls.append(("short", loop, lambda loop=loop: rq.decode_attention(
+            run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], 500, w.softmax_scale, ws,
+            out=out)))
+        calls.append(("ragged", loop, lambda loop=loop: rq.decode_attention_ragged(
+            run.desc, run.cache, run.signs, loop, 0, run.q[loop, 0], lengths, run.N,
+            w.softmax_scale, ws, out=out)))
+    first = {}
+    for rep in range(3):
+        for kind, loop, fn in calls:
+            got = fn().clone()
+            torch.cuda.synchronize()
+            key = (kind, loop)
+            if key not in first:
+                first[key] = got
+                n = {"short": 500, "ragged": 4000}.get(kind, run.N)
+                hq = 1 if kind == "per-head" else 3       # query heads of KV head 1
+                q = q2[loop, 1, 1] if kind == "per-head" else run.q[loop, 0, 1, 3]
+                ref = oracle_attention(w, ek, ev, HK, HV, bits16(q), loop, n)
+                assert_close_attention(got[1, hq].cpu().numpy(), ref, f"{kind} loop {loop}")
+            else:
+                assert torch.equal(got, first[key]), f"{kind} loop {loop} repeat {rep}"
+    assert not ws[:counter_bytes].any(), "split counters not returned to zero"
 
 
 def test_graph_replay_matches_eager():
