@@ -16,14 +16,14 @@ int decode_wave_tokens(int d);
 int bf16_tile_tokens();
 
 // Split-K planning.  Small batch*heads products are split along the tokens
-// until the grid fills the GPU once: three 4-wave workgroups per CU for a
-// two-plane (residual-loop) decode kernel (768 on 256 CUs), four for a
-// one-plane kernel, two for the BF16 baseline (measured best; longer splits
-// amortize each workgroup's query setup and merge).  Splits never shrink
-// below two tiles.  The result is non-decreasing in
-// n_tokens, so a workspace sized for n serves any smaller n.
-static constexpr int32_t kDecodeTargetTwo = 768;
-static constexpr int32_t kDecodeTargetOne = 1024;
+// until the grid holds about two 4-wave workgroups per CU (512 on 256 CUs)
+// for every decode kernel: with the splits merged inside the kernel, fewer
+// and longer splits measured faster than filling all workgroup slots (768
+// or 1024); the BF16 baseline also targets 512.  Splits never shrink below
+// two tiles.  The result is non-decreasing in n_tokens, so a workspace sized
+// for n serves any smaller n.
+static constexpr int32_t kDecodeTargetTwo = 512;
+static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
 static constexpr int32_t kDecodeTarget =
     kDecodeTargetTwo > kDecodeTargetOne ? kDecodeTargetTwo : kDecodeTargetOne;  // workspace bound
