@@ -28,16 +28,21 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "decode_attention_int4_amd", "csrc", "rq_decode.hip")
+# the sources the dominant kernel's code and launch depend on
+DECODE_SRCS = [os.path.join(ROOT, "decode_attention_int4_amd", "csrc", f)
+               for f in ("rq_decode.hip", "rq_stage.h", "rq_api.hip")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_sha(path=DECODE_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_sha(paths=DECODE_SRCS) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(config: str):
