@@ -79,6 +79,8 @@ struct GStage {
   static constexpr int N_DMA = 2 * n_gather(W1) + 1 + n_gather(WS) +
                                (TWO ? 2 * n_gather(W2) + 1 + n_gather(WS) + 2 : 0);
   static constexpr int KM1 = D / 32, KM2 = D / 32;   // K-side MFMAs (32 elements each) per plane
+  // the V scale tables (96 bytes per group) reuse the K planes' space
+  static_assert(k1s + 256 - k1c >= NG * 96 && (!TWO || k2s + 256 - k2c >= NG * 96), "V table space");
   static_assert(N_DMA < 64, "pending DMA count must fit vmcnt");
 };
 
@@ -211,35 +213,58 @@ __device__ __forceinline__ h4 kz_operand(u32x4 szrow, int c) {
   return (h4){z01.x, z01.y, z23.x, z23.y};
 }
 
+// Scale tables of one V plane for one tile, built by the wave before its
+// value products so that the 16 lanes sharing a token quad do not each
+// rebuild the same fp16 pairs.  Entry [g][c] of the first table holds, for
+// tokens 4c..4c+3 of group g, the pairs (s'_0, s'_1), (s'_2, s'_3) and the
+// same times -1024; entry [g][c] of the second holds (z'_0, z'_1),
+// (z'_2, z'_3).  Lane l fills token pair l % 8 of group l / 8.  The tables
+// (96 bytes per group) take the place of the tile's K-side planes, which are
+// no longer needed once the logits are known.
+template <int NG>
+__device__ __forceinline__ void v_tables(const lds_u8* szg, lds_u8* tab, int lane) {
+  typedef __attribute__((address_space(3))) uint32_t lu32;
+  typedef __attribute__((address_space(3))) const u32x2 lu32x2;
+  const int g = lane >> 3, tp = lane & 7;
+  const u32x2 y = *reinterpret_cast<lu32x2*>(szg + (min(g >> 1, NG / 2 - 1) * 16 + 2 * tp) * 4);
+  const uint32_t sb = 2u * (uint32_t)(g & 1);
+  const h2 sp = fp8pair_pos_h(__builtin_amdgcn_perm(y.y, y.x, sel2(sb)));
+  const h2 op = sp * (h2){(_Float16)-1024.f, (_Float16)-1024.f};
+  const h2 zp = fp8pair_h(__builtin_amdgcn_perm(y.y, y.x, sel2(sb + 1u)));
+  if (NG == 8 || g < NG) {
+    lu32* S = reinterpret_cast<lu32*>(tab) + (g * 4 + (tp >> 1)) * 4;
+    S[tp & 1] = __builtin_bit_cast(uint32_t, sp);
+    S[2 + (tp & 1)] = __builtin_bit_cast(uint32_t, op);
+    lu32* Z = reinterpret_cast<lu32*>(tab + NG * 64) + (g * 4 + (tp >> 1)) * 2;
+    Z[tp & 1] = __builtin_bit_cast(uint32_t, zp);
+  }
+}
+
 // V-side A operand for group g: element e (lane row) of tokens 4c..4c+3,
-// times their scales, exact in fp16.
+// times their scales (from the plane's table), exact in fp16.
 template <int BITS>
-__device__ __forceinline__ h4 v_operand(const lds_u8* codes, u32x4 sz4, int g, int e, int c,
+__device__ __forceinline__ h4 v_operand(const lds_u8* codes, const lds_u8* tab, int g, int e, int c,
                                         uint32_t magic) {
   const int w = BITS == 4 ? 2 * g + (e >> 3) : g;
   const u32x4 x = lds_u32x4(codes + (w * 16 + 4 * c) * 4);
+  const u32x4 sc = lds_u32x4(tab + (g * 4 + c) * 16);
   const uint32_t b = BITS == 4 ? (uint32_t)((e >> 1) & 3) : (uint32_t)(e >> 2);
   const uint32_t sh = BITS == 4 ? 4u * (uint32_t)(e & 1) : 2u * (uint32_t)(e & 3);
   const uint32_t mask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-  const uint32_t sb = 2u * (uint32_t)(g & 1);
-  const h2 s01 = fp8pair_pos_h(__builtin_amdgcn_perm(sz4.y, sz4.x, sel2(sb)));
-  const h2 s23 = fp8pair_pos_h(__builtin_amdgcn_perm(sz4.w, sz4.z, sel2(sb)));
-  const h2 m1024 = (h2){(_Float16)-1024.f, (_Float16)-1024.f};
-  uint32_t p01 = __builtin_amdgcn_perm(x.y, x.x, sel2(b)) >> sh;
-  uint32_t p23 = __builtin_amdgcn_perm(x.w, x.z, sel2(b)) >> sh;
-  const h2 v01 = pk_fma(as_h2(and_or(p01, mask, magic)), s01, s01 * m1024);
-  const h2 v23 = pk_fma(as_h2(and_or(p23, mask, magic)), s23, s23 * m1024);
+  const uint32_t p01 = __builtin_amdgcn_perm(x.y, x.x, sel2(b)) >> sh;
+  const uint32_t p23 = __builtin_amdgcn_perm(x.w, x.z, sel2(b)) >> sh;
+  const h2 v01 = pk_fma(as_h2(and_or(p01, mask, magic)), as_h2(sc.x), as_h2(sc.z));
+  const h2 v23 = pk_fma(as_h2(and_or(p23, mask, magic)), as_h2(sc.y), as_h2(sc.w));
   return (h4){v01.x, v01.y, v23.x, v23.y};
 }
 
 // V-side offset operand: row i = group (lane row), tokens 4c..4c+3.
 template <int NG>
-__device__ __forceinline__ h4 vz_operand(const lds_u8* szg, int i, int c) {
-  const int gg = min(i >> 1, NG / 2 - 1);
-  const u32x4 y = lds_u32x4(szg + (gg * 16 + 4 * c) * 4);
-  const uint32_t b = 2u * (uint32_t)(i & 1) + 1u;
-  h2 z01 = fp8pair_h(__builtin_amdgcn_perm(y.y, y.x, sel2(b)));
-  h2 z23 = fp8pair_h(__builtin_amdgcn_perm(y.w, y.z, sel2(b)));
+__device__ __forceinline__ h4 vz_operand(const lds_u8* tab, int i, int c) {
+  typedef __attribute__((address_space(3))) const u32x2 lu32x2;
+  const int ii = min(i, NG - 1);
+  const u32x2 z = *reinterpret_cast<lu32x2*>(tab + NG * 64 + (ii * 4 + c) * 8);
+  h2 z01 = as_h2(z.x), z23 = as_h2(z.y);
   if (i >= NG) z01 = z23 = (h2){(_Float16)0.f, (_Float16)0.f};
   return (h4){z01.x, z01.y, z23.x, z23.y};
 }
@@ -520,15 +545,16 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 
     // ---- values: O^T[e][head] per group, and the offset sums per group
     {
-      u32x4 sz4 = {0u, 0u, 0u, 0u};
+      lds_u8* tab = const_cast<lds_u8*>(st) + GS::k1c;   // K1 planes are done with
+      v_tables<NG>(st + GS::v1s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        if ((gq & 1) == 0) sz4 = lds_u32x4(st + GS::v1s + ((gq >> 1) * 16 + 4 * c) * 4);
-        const h4 x = v_operand<B1>(st + GS::v1c, sz4, gq, r, c, magic);
+        const h4 x = v_operand<B1>(st + GS::v1c, tab, gq, r, c, magic);
         OA[gq] = mfma16(x, Ph, OA[gq]);
         OA[gq] = mfma16(x, Pl, OA[gq]);
+        __builtin_amdgcn_sched_barrier(0);  // bounds how many groups' loads are hoisted
       }
-      const h4 z = vz_operand<NG>(st + GS::v1s, r, c);
+      const h4 z = vz_operand<NG>(tab, r, c);
       OZA = mfma16(z, Ph, OZA);
       OZA = mfma16(z, Pl, OZA);
     }
@@ -540,15 +566,16 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
         Qh[j] = hl.x;
         Ql[j] = hl.y;
       }
-      u32x4 sz4 = {0u, 0u, 0u, 0u};
+      lds_u8* tab = const_cast<lds_u8*>(st) + GS::k2c;   // K2 planes are done with
+      v_tables<NG>(st + GS::v2s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        if ((gq & 1) == 0) sz4 = lds_u32x4(st + GS::v2s + ((gq >> 1) * 16 + 4 * c) * 4);
-        const h4 x = v_operand<B2E>(st + GS::v2c, sz4, gq, r, c, magic);
+        const h4 x = v_operand<B2E>(st + GS::v2c, tab, gq, r, c, magic);
         OR_[gq] = mfma16(x, Qh, OR_[gq]);
         OR_[gq] = mfma16(x, Ql, OR_[gq]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const h4 z = vz_operand<NG>(st + GS::v2s, r, c);
+      const h4 z = vz_operand<NG>(tab, r, c);
       OZR = mfma16(z, Qh, OZR);
       OZR = mfma16(z, Ql, OZR);
     }
