@@ -25,8 +25,8 @@ int bf16_tile_tokens();
 static constexpr int32_t kDecodeTargetTwo = 512;
 static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
-static constexpr int32_t kDecodeTarget =
-    kDecodeTargetTwo > kDecodeTargetOne ? kDecodeTargetTwo : kDecodeTargetOne;  // workspace bound
+static constexpr int32_t kGqaTarget = 512;         // grouped-query kernel
+static constexpr int32_t kDecodeTarget = 512;      // the largest target: workspace bound
 static constexpr int32_t kBf16Target = 512;
 
 static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
@@ -268,7 +268,7 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
     any_grouped = any_grouped || grouped(desc, loop, q_heads);
   if (any_grouped) {
     const int32_t sg = rq::max_splits_bound(rows * desc->kv_heads, max_n_tokens,
-                                            rq::gqa_tile_tokens(), rq::kDecodeTarget);
+                                            rq::gqa_tile_tokens(), rq::kGqaTarget);
     s = sg > s ? sg : s;
   }
   return s > 1 ? kCounterBytes + (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
@@ -314,7 +314,7 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
       chain ? rq::kDecodeTargetChain : two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne;
   const rq::SplitPlan plan =
       grouped(desc, loop, q_heads)
-          ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), target)
+          ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget)
           : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim), target);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
