@@ -331,7 +331,9 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
   __shared__ float sq[D], su[D];
   __shared__ float s_scale[2];
-  __shared__ __attribute__((aligned(16))) uint32_t spre[8][32];  // per-group query pairs
+  // per-group query pairs; rows padded to 36 dwords so that the 16-byte
+  // reads of the eight groups' rows fall in eight different bank quads
+  __shared__ __attribute__((aligned(16))) uint32_t spre[8][36];
   __shared__ float sm_m[NW];
   __shared__ uint32_t s_ticket;
   typedef float AccRows[LY::PAIRS][kRow];
