@@ -284,7 +284,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   constexpr int KM1 = GS::KM1, KM2 = GS::KM2;
   constexpr int R1 = D * B1 / 8, R2 = D * B2E / 8, RS = GS::RS;
   constexpr int kRing = NW * 2 * GS::BYTES;
-  constexpr int kMerge = (2 * 16 * D + 2 * 16 * 16) * 4;
+  constexpr int kMerge = (2 * 20 * D + 2 * 20 * 16) * 4;
   const Geometry& g = a.g;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kMerge ? kRing : kMerge];
@@ -593,10 +593,13 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][r]);
   const float f = exp2f(m - M) * 256.f;  // also takes out the 2^-8 of s' and z'
-  float* bufA = reinterpret_cast<float*>(smem);        // [16 heads][D]
-  float* bufR = bufA + 16 * D;
-  float* bufZA = bufR + 16 * D;                        // [16 heads][16 groups]
-  float* bufZR = bufZA + 16 * 16;
+  // [element][head] with a row stride of 20 floats: the 64 lanes of one
+  // store (heads r, elements 4c + j) then fall in 64 different banks
+  constexpr int kMS = 20;
+  float* bufA = reinterpret_cast<float*>(smem);        // [D][kMS]
+  float* bufR = bufA + kMS * D;
+  float* bufZA = bufR + kMS * D;                       // [16 groups][kMS]
+  float* bufZR = bufZA + kMS * 16;
   for (int ww = 0; ww < NW; ++ww) {
     if (w == ww) {
 #pragma unroll
@@ -604,14 +607,14 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 16 * gq + 4 * c + j;
-          bufA[r * D + e] = (ww ? bufA[r * D + e] : 0.f) + f * OA[gq][j];
-          if constexpr (TWO) bufR[r * D + e] = (ww ? bufR[r * D + e] : 0.f) + f * OR_[gq][j];
+          bufA[e * kMS + r] = (ww ? bufA[e * kMS + r] : 0.f) + f * OA[gq][j];
+          if constexpr (TWO) bufR[e * kMS + r] = (ww ? bufR[e * kMS + r] : 0.f) + f * OR_[gq][j];
         }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * c + j;
-        bufZA[r * 16 + i] = (ww ? bufZA[r * 16 + i] : 0.f) + f * OZA[j];
-        if constexpr (TWO) bufZR[r * 16 + i] = (ww ? bufZR[r * 16 + i] : 0.f) + f * OZR[j];
+        bufZA[i * kMS + r] = (ww ? bufZA[i * kMS + r] : 0.f) + f * OZA[j];
+        if constexpr (TWO) bufZR[i * kMS + r] = (ww ? bufZR[i * kMS + r] : 0.f) + f * OZR[j];
       }
     }
     __syncthreads();
@@ -630,8 +633,8 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
     return Mn;
   };
-  auto accA = [&](int n, int e) { return bufA[n * D + e] + bufZA[n * 16 + (e >> 4)]; };
-  auto accR = [&](int n, int e) { return TWO ? bufR[n * D + e] + bufZR[n * 16 + (e >> 4)] : 0.f; };
+  auto accA = [&](int n, int e) { return bufA[e * kMS + n] + bufZA[(e >> 4) * kMS + n]; };
+  auto accR = [&](int n, int e) { return TWO ? bufR[e * kMS + n] + bufZR[(e >> 4) * kMS + n] : 0.f; };
 
   if (a.splits > 1) {
     // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
