@@ -336,6 +336,8 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t spre[8][36];
   __shared__ float sm_m[NW];
   __shared__ uint32_t s_ticket;
+  // the query row (BF16) and this layer's key signs, staged by DMA
+  __shared__ __attribute__((aligned(16))) uint8_t s_in[512];
   typedef float AccRows[LY::PAIRS][kRow];
   AccRows* sm_acc = reinterpret_cast<AccRows*>(smem);             // [wave][pair][accA | accR | l]
 
@@ -392,6 +394,9 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
   const int first = t_begin + w * TPW;
   const int n_tiles = first < t_end ? (t_end - first + NW * TPW - 1) / (NW * TPW) : 0;
+  // tiles in flight before the query side is built: the whole ring, unless
+  // its DMA count would not fit the wait below
+  constexpr int kPre = ST::COUNT * ST::N_DMA < 64 ? ST::COUNT : ST::COUNT - 1;
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
     dma_piece<ST::C1, ST::R1, F>(rk1, tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
@@ -427,22 +432,40 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
+  // Wave 0 stages the query row and the key signs by DMA ahead of its tiles:
+  // a plain load issued after the tiles' DMAs would wait for all of them
+  if (w == 0) {
+    dma1<4>(make_rsrc((const uint8_t*)(a.q + (uint64_t)bh * D), 2 * D), (lds_u8*)s_in,
+            min(4 * lane, 2 * D - 4), 0u);
+    if (rotated)
+      dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), (lds_u8*)s_in + 256,
+              min(4 * lane, D - 4), 0u);
+  }
 #pragma unroll
-  for (int i = 0; i < ST::COUNT - 1; ++i)
+  for (int i = 0; i < kPre; ++i)
     if (i < n_tiles) issue(i);
 
   // ---- query side, once per workgroup (wave 0): q, u = H q, their fp16
   // prescales, and for every group the fp16 pairs matching the code pairs,
   // the magic constants 1024 * sum(pair) and the plain sums
   if (w == 0) {
+    // the staged row has landed once at most the tiles' DMAs are pending
+    static_assert(kPre <= 2, "waits below cover two tiles");
+    const int pre = min(kPre, n_tiles);
+    if constexpr (kPre == 2) {
+      if (pre == 2) wait_vm<2 * ST::N_DMA>();
+    }
+    if (pre == 1) wait_vm<ST::N_DMA>();
+    else if (pre == 0) wait_vm<0>();
     const bool v1ok = (D > 64) && (lane + 64 < D);
-    const float q0 = bf16_to_f32(a.q[(uint64_t)bh * D + lane]);
-    const float q1 = v1ok ? bf16_to_f32(a.q[(uint64_t)bh * D + lane + 64]) : 0.f;
+    const lds_u8* qin = (const lds_u8*)s_in;
+    const float q0 = bf16_to_f32(lds_u16(qin + 2 * lane));
+    const float q1 = v1ok ? bf16_to_f32(lds_u16(qin + 2 * (lane + 64))) : 0.f;
     sq[lane] = q0;
     if (v1ok) sq[lane + 64] = q1;
     float u0 = q0, u1 = q1;
     if (rotated) {
-      const int8_t* sg = a.signs + (uint64_t)a.layer * D;  // K signs of this layer
+      const int8_t* sg = (const int8_t*)(s_in + 256);  // K signs of this layer
       u0 *= (float)sg[lane];
       u1 = v1ok ? u1 * (float)sg[lane + 64] : 0.f;
       wave_wht<D>(u0, u1, lane);
@@ -530,7 +553,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   // one loop body for every stage: stage-specialized copies would make the
   // compiler shuffle all live accumulators between them on every iteration
   for (int it = 0; it < n_tiles; ++it) {
-    if (it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
+    if (it + ST::COUNT - 1 >= kPre && it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
     // wait for tile `it`: the tiles issued after it may stay in flight
     const int later = min(ST::COUNT - 1, n_tiles - 1 - it);
     static_assert(ST::COUNT <= 3, "wait counts below cover rings up to 3 deep");

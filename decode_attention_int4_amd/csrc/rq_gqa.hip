@@ -289,10 +289,16 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kMerge ? kRing : kMerge];
   // B operands of the Q K^T products in lane order, [mm][lane][8 halves]:
-  // the prescaled queries (exact) and the rotated queries' high and low parts
-  __shared__ __attribute__((aligned(16))) _Float16 fq[KM1][64][8];
-  __shared__ __attribute__((aligned(16))) _Float16 fuh[TWO ? KM2 : 1][64][8];
-  __shared__ __attribute__((aligned(16))) _Float16 ful[TWO ? KM2 : 1][64][8];
+  // the prescaled queries (exact) and the rotated queries' high and low parts.
+  // Before they are built, the same bytes stage the query rows (256 bytes
+  // per head) and the key signs by DMA.
+  typedef _Float16 QOp[64][8];
+  constexpr int kOpBytes = (KM1 + 2 * (TWO ? KM2 : 1)) * (int)sizeof(QOp);
+  constexpr int kStageBytes = 16 * 256 + 256;
+  __shared__ __attribute__((aligned(16))) uint8_t qop[kOpBytes > kStageBytes ? kOpBytes : kStageBytes];
+  QOp* fq = reinterpret_cast<QOp*>(qop);
+  QOp* fuh = fq + KM1;
+  QOp* ful = fuh + (TWO ? KM2 : 1);
   __shared__ float sqs[16][8], sus[16][8];       // per-group sums of the two
   __shared__ float spq[16], spu[16];             // per-head prescales
   __shared__ float sm_m[NW][16], sm_l[NW][16];
@@ -368,19 +374,76 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
+  // ---- the query rows of this wave's heads (w, w + 4, ... below G) and the
+  // key signs come in by DMA ahead of the first tile: a plain load issued
+  // after the tile's DMAs would wait for all of them.  (Issuing the second
+  // tile here as well measured slower.)
+  lds_u8* stage = (lds_u8*)qop;
+  for (int n = w; n < G; n += NW) {
+    const uint16_t* qrow = a.q + ((uint64_t)b * a.q_heads + kvh * G + n) * D;
+    dma1<4>(make_rsrc((const uint8_t*)qrow, 2 * D), stage + n * 256, min(4 * lane, 2 * D - 4), 0u);
+  }
+  if (rotated && w == 0)
+    dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), stage + 16 * 256,
+            min(4 * lane, D - 4), 0u);
   if (n_tiles > 0) issue(0);
+  if (n_tiles > 0) wait_vm<GS::N_DMA>();
+  else wait_vm<0>();
+  __syncthreads();   // every wave's rows and the signs are in LDS
+  constexpr int kHw = 16 / NW;   // operand columns per wave
+  const bool v1ok = (D > 64) && (lane + 64 < D);
+  float qv0[kHw], qv1[kHw];
+#pragma unroll
+  for (int j = 0; j < kHw; ++j) {
+    const int n = w + NW * j;
+    const lds_u8* row = stage + min(n, 15) * 256;
+    qv0[j] = n < G ? bf16_to_f32(lds_u16(row + 2 * lane)) : 0.f;
+    qv1[j] = (n < G && v1ok) ? bf16_to_f32(lds_u16(row + 2 * (lane + 64))) : 0.f;
+  }
+  float sg0 = 1.f, sg1 = 1.f;
+  if (rotated) {
+    const int8_t* sg = (const int8_t*)(qop + 16 * 256);  // K signs of this layer
+    sg0 = (float)sg[lane];
+    sg1 = v1ok ? (float)sg[lane + 64] : 0.f;
+  }
+  __syncthreads();   // the operand tables below overwrite the staged rows
 
-  // ---- query side: prescaled queries and rotated queries of the G heads
-  // (wave w takes heads w, w + 4, ...; columns n >= G stay zero)
-  for (int n = w; n < 16; n += NW) {
-    const bool v1ok = (D > 64) && (lane + 64 < D);
-    const int hq = kvh * G + n;
-    float q0 = 0.f, q1 = 0.f;
-    if (n < G) {
-      const uint16_t* qrow = a.q + ((uint64_t)b * a.q_heads + hq) * D;
-      q0 = bf16_to_f32(qrow[lane]);
-      q1 = v1ok ? bf16_to_f32(qrow[lane + 64]) : 0.f;
+  // ---- query side: prescaled queries and rotated queries of the G heads;
+  // the columns n >= G are zero
+#pragma unroll
+  for (int j = 0; j < kHw; ++j) {
+    const int n = w + NW * j;
+    if (n >= G) {
+      int mm, cc, sl;
+      kslot_of<B1>(lane, mm, cc, sl);
+      fq[mm][n + 16 * cc][sl] = (_Float16)0.f;
+      if (v1ok) {
+        kslot_of<B1>(lane + 64, mm, cc, sl);
+        fq[mm][n + 16 * cc][sl] = (_Float16)0.f;
+      }
+      if (r == 0) {
+        sqs[n][c] = 0.f;
+        if (c + 4 < NG) sqs[n][c + 4] = 0.f;
+      }
+      if (lane == 0) spq[n] = 1.f;
+      if constexpr (TWO) {
+        kslot_of<B2E>(lane, mm, cc, sl);
+        fuh[mm][n + 16 * cc][sl] = (_Float16)0.f;
+        ful[mm][n + 16 * cc][sl] = (_Float16)0.f;
+        if (v1ok) {
+          kslot_of<B2E>(lane + 64, mm, cc, sl);
+          fuh[mm][n + 16 * cc][sl] = (_Float16)0.f;
+          ful[mm][n + 16 * cc][sl] = (_Float16)0.f;
+        }
+        if (r == 0) {
+          sus[n][c] = 0.f;
+          if (c + 4 < NG) sus[n][c + 4] = 0.f;
+        }
+        if (lane == 0) spu[n] = 1.f;
+      }
+      continue;
     }
+    const float q0 = qv0[j], q1 = qv1[j];
     const float pq = fp16_prescale(wave_max(fmaxf(fabsf(q0), fabsf(q1))));
     const float x0 = q0 * pq, x1 = q1 * pq;
     {
@@ -406,9 +469,8 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     if constexpr (TWO) {
       float u0 = q0, u1 = q1;
       if (rotated) {
-        const int8_t* sg = a.signs + (uint64_t)a.layer * D;  // K signs of this layer
-        u0 *= (float)sg[lane];
-        u1 = v1ok ? u1 * (float)sg[lane + 64] : 0.f;
+        u0 *= sg0;
+        u1 = v1ok ? u1 * sg1 : 0.f;
         wave_wht<D>(u0, u1, lane);
         u0 *= (D == 128) ? 0.08838834764831845f : 0.125f;
         u1 = v1ok ? u1 * ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) : 0.f;
@@ -472,12 +534,10 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   float m = kEmpty, l = 0.f;
 
   for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) {
-      issue(it + 1);
-      wait_vm<GS::N_DMA>();
-    } else {
-      wait_vm<0>();
-    }
+    // tile it + 1 goes into the slot tile it - 1 has left
+    if (it + 1 < n_tiles) issue(it + 1);
+    if (it + 1 < n_tiles) wait_vm<GS::N_DMA>();
+    else wait_vm<0>();
     const lds_u8* st = ring + (it & 1) * GS::BYTES;
     const int vt = t_end - (first + it * NW * TT);  // in-range tokens of this tile
 
@@ -659,7 +719,6 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     return;
   }
   // ---- a single split: finish here, one wave per head
-  const bool v1ok = (D > 64) && (lane + 64 < D);
   for (int n = w; n < G; n += NW) {
     const float Ln = head_l(n);
     const float A0 = accA(n, lane), A1 = v1ok ? accA(n, lane + 64) : 0.f;
