@@ -284,7 +284,11 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   constexpr int KM1 = GS::KM1, KM2 = GS::KM2;
   constexpr int R1 = D * B1 / 8, R2 = D * B2E / 8, RS = GS::RS;
   constexpr int kRing = NW * 2 * GS::BYTES;
-  constexpr int kMerge = (2 * 20 * D + 2 * 20 * 16) * 4;
+  // merge rows of one head: value sums (first plane | residual) and the
+  // offset sums per group, padded to whole float4s plus one
+  constexpr int kZOff = (TWO ? 2 : 1) * D;
+  constexpr int kRowF = (kZOff + (TWO ? 2 : 1) * NG + 3) / 4 * 4 + 4;
+  constexpr int kMerge = 32 * kRowF * 4;   // 4 regions x 8 heads, or 2 x 16
   const Geometry& g = a.g;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kMerge ? kRing : kMerge];
@@ -641,44 +645,51 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the waves: running max per head, then the sums in wave order
+  // ---- merge the waves: running max per head, then the G heads' sums of
+  // every wave side by side (one round), or, for G > 8, two waves into each
+  // of two regions (two rounds)
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (c == 0) {
     sm_m[w][r] = m;
     sm_l[w][r] = l;
   }
-  __syncthreads();  // every wave is done with its ring: the merge buffers reuse it
+  __syncthreads();  // every wave is done with its ring: the merge regions reuse it
   float M = sm_m[0][r];
 #pragma unroll
   for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][r]);
   const float f = exp2f(m - M) * 256.f;  // also takes out the 2^-8 of s' and z'
-  // [element][head] with a row stride of 20 floats: the 64 lanes of one
-  // store (heads r, elements 4c + j) then fall in 64 different banks
-  constexpr int kMS = 20;
-  float* bufA = reinterpret_cast<float*>(smem);        // [D][kMS]
-  float* bufR = bufA + kMS * D;
-  float* bufZA = bufR + kMS * D;                       // [16 groups][kMS]
-  float* bufZR = bufZA + kMS * 16;
-  for (int ww = 0; ww < NW; ++ww) {
-    if (w == ww) {
+  const int nreg = G <= 8 ? NW : 2;
+  float* regs = reinterpret_cast<float*>(smem);   // [region][head][kRowF]
+  auto put = [&](float* row, bool add) __attribute__((always_inline)) {
 #pragma unroll
-      for (int gq = 0; gq < NG; ++gq)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 16 * gq + 4 * c + j;
-          bufA[e * kMS + r] = (ww ? bufA[e * kMS + r] : 0.f) + f * OA[gq][j];
-          if constexpr (TWO) bufR[e * kMS + r] = (ww ? bufR[e * kMS + r] : 0.f) + f * OR_[gq][j];
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * c + j;
-        bufZA[i * kMS + r] = (ww ? bufZA[i * kMS + r] : 0.f) + f * OZA[j];
-        if constexpr (TWO) bufZR[i * kMS + r] = (ww ? bufZR[i * kMS + r] : 0.f) + f * OZR[j];
+    for (int gq = 0; gq < NG; ++gq) {
+      f4* pa = reinterpret_cast<f4*>(row + 16 * gq + 4 * c);
+      *pa = (add ? *pa : (f4){0.f, 0.f, 0.f, 0.f}) + f * OA[gq];
+      if constexpr (TWO) {
+        f4* pr = reinterpret_cast<f4*>(row + D + 16 * gq + 4 * c);
+        *pr = (add ? *pr : (f4){0.f, 0.f, 0.f, 0.f}) + f * OR_[gq];
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * c + j;
+      if (i < NG) {
+        float* za = row + kZOff + i;
+        *za = (add ? *za : 0.f) + f * OZA[j];
+        if constexpr (TWO) {
+          float* zr = row + kZOff + NG + i;
+          *zr = (add ? *zr : 0.f) + f * OZR[j];
+        }
+      }
+    }
+  };
+  if (r < G && w < nreg) put(regs + (w * G + r) * kRowF, false);
+  if (nreg < NW) {
     __syncthreads();
+    if (r < G && w >= nreg) put(regs + ((w - nreg) * G + r) * kRowF, true);
   }
+  __syncthreads();
   auto head_l = [&](int n) {
     float s = 0.f, Mn = sm_m[0][n];
 #pragma unroll
@@ -693,8 +704,17 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
     return Mn;
   };
-  auto accA = [&](int n, int e) { return bufA[e * kMS + n] + bufZA[(e >> 4) * kMS + n]; };
-  auto accR = [&](int n, int e) { return TWO ? bufR[e * kMS + n] + bufZR[(e >> 4) * kMS + n] : 0.f; };
+  // element e of head n's value sum (plane 0: first plane, 1: residual)
+  auto acc = [&](int n, int plane, int e) {
+    float s = 0.f;
+    for (int k = 0; k < nreg; ++k) {
+      const float* row = regs + (k * G + n) * kRowF;
+      s += row[plane * D + e] + row[kZOff + plane * NG + (e >> 4)];
+    }
+    return s;
+  };
+  auto accA = [&](int n, int e) { return acc(n, 0, e); };
+  auto accR = [&](int n, int e) { return TWO ? acc(n, 1, e) : 0.f; };
 
   if (a.splits > 1) {
     // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
