@@ -30,10 +30,11 @@
 //   P V:   M = 16 elements of one quantization group, K = 16 tokens,
 //          N = heads, with B = P^T read straight from the S^T layout.
 // A wave streams 16-token tiles through a private two-stage LDS ring filled
-// by buffer_load ... lds DMA.  Code and scale planes are gathered dword by
-// dword into [dword][token] order, so a lane reads the dword it needs of one
-// token (K side) or of four consecutive tokens (V side) without bank
-// conflicts.
+// by buffer_load ... lds DMA.  Code planes land in blocks of whole tokens,
+// [dword][token] inside a block (Blocks below); scale planes are gathered
+// dword by dword into [dword][token] order.  A lane then reads the dword it
+// needs of one token (K side), or of four consecutive tokens (V side), with
+// one LDS read.
 #include <hip/hip_runtime.h>
 
 #include "rq_device.h"
@@ -55,6 +56,26 @@ constexpr float kZs = 1.f / 16.f;
 // 64-lane dword DMAs moving 16 tokens x w dwords
 __host__ __device__ constexpr int gather_dmas(int w) { return (16 * w + 63) / 64; }
 
+// Code planes of W dwords per token are staged in blocks of BT whole tokens,
+// one 64-lane dword DMA per block, so that every DMA instruction reads BT
+// consecutive token rows: one contiguous range of global memory.  Inside a
+// block the dwords are stored [dword][token], so four consecutive tokens'
+// dword w are adjacent (one 128-bit read on the value side).  Blocks lie P
+// dwords further apart than their 64, which spreads the reads of different
+// blocks over the LDS banks.  (A [dword][token] gather over all 16 tokens of
+// a tile, the layout before, reads 16 bytes of each token row per DMA
+// instruction; it streamed at well under half the rate.)
+template <int W, int P>
+struct Blocks {
+  static constexpr int BT = W > 8 ? 4 : (W > 4 ? 8 : 16);   // tokens per block
+  static constexpr int NB = 16 / BT;                         // blocks (DMA instructions) per tile
+  static constexpr int STRIDE = 64 + P;                      // dwords from block to block
+  static constexpr int SPAN = NB * STRIDE * 4;               // bytes per tile
+  static_assert(BT * W <= 64, "a block fits one DMA instruction");
+  // dword position of dword w of token t
+  __host__ __device__ static constexpr int pos(int t, int w) { return (t / BT) * STRIDE + w * BT + t % BT; }
+};
+
 template <int D, int B1, int B2>
 struct GStage {
   static constexpr int NG = D / 16;
@@ -62,22 +83,25 @@ struct GStage {
   static constexpr int W1 = D * B1 / 32, W2 = D * (TWO ? B2 : 2) / 32;  // code dwords per token
   static constexpr int WS = NG / 2;                                     // sz dwords per token
   static constexpr int RS = 2 * NG;                                     // sz bytes per token
-  // [dword][token] gathers of 16 * W dwords, in whole 64-lane DMA instructions
+  // code planes in blocks (padding measured against bank conflicts of the
+  // operand reads); sz planes as [dword][token] gathers of 16 * WS dwords
+  using CB1 = Blocks<W1, D == 64 ? 16 : 8>;
+  using CB2 = Blocks<W2, D == 64 ? 16 : 8>;
   static constexpr int n_gather(int w) { return gather_dmas(w); }
   static constexpr int span(int w) { return gather_dmas(w) * 256; }
   static constexpr int k1c = 0;
-  static constexpr int k1s = k1c + span(W1);     // sz rows padded to 16 bytes: 16 tokens
+  static constexpr int k1s = k1c + CB1::SPAN;    // sz rows padded to 16 bytes: 16 tokens
   static constexpr int v1c = k1s + 256;
-  static constexpr int v1s = v1c + span(W1);
+  static constexpr int v1s = v1c + CB1::SPAN;
   static constexpr int k2c = v1s + span(WS);
-  static constexpr int k2s = k2c + (TWO ? span(W2) : 0);
+  static constexpr int k2s = k2c + (TWO ? CB2::SPAN : 0);
   static constexpr int v2c = k2s + (TWO ? 256 : 0);
-  static constexpr int v2s = v2c + (TWO ? span(W2) : 0);
+  static constexpr int v2s = v2c + (TWO ? CB2::SPAN : 0);
   static constexpr int ka = v2s + (TWO ? span(WS) : 0);
   static constexpr int va = ka + (TWO ? 256 : 0);
   static constexpr int BYTES = va + (TWO ? 256 : 0);
-  static constexpr int N_DMA = 2 * n_gather(W1) + 1 + n_gather(WS) +
-                               (TWO ? 2 * n_gather(W2) + 1 + n_gather(WS) + 2 : 0);
+  static constexpr int N_DMA = 2 * CB1::NB + 1 + n_gather(WS) +
+                               (TWO ? 2 * CB2::NB + 1 + n_gather(WS) + 2 : 0);
   static constexpr int KM1 = D / 32, KM2 = D / 32;   // K-side MFMAs (32 elements each) per plane
   // the V scale tables (96 bytes per group) reuse the K planes' space
   static_assert(k1s + 256 - k1c >= NG * 96 && (!TWO || k2s + 256 - k2c >= NG * 96), "V table space");
@@ -94,6 +118,22 @@ __device__ __forceinline__ void dma_gather(rsrc_t r, uint32_t so, int valid, lds
     const int p = min(c * 64 + lane, 16 * W - 1);
     const int w = p >> 4, m = FULL ? (p & 15) : min(p & 15, valid - 1);
     dma1<4>(r, dst + c * 256, m * ROWB + w * 4, so);
+  }
+}
+
+// One code plane of a tile in blocks: DMA instruction b moves block b, lane
+// p the dword at position p of its [dword][token] order; lanes past the
+// block's W * BT dwords, and tokens past `valid` in a partial tile, re-read
+// in-range data.
+template <class CB, int W, int ROWB, bool FULL>
+__device__ __forceinline__ void dma_blocks(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
+  const int p = min(lane, CB::BT * W - 1);
+  const int w = p / CB::BT, tl = p % CB::BT;
+#pragma unroll
+  for (int b = 0; b < CB::NB; ++b) {
+    const int t = b * CB::BT + tl;
+    const int m = FULL ? t : min(t, valid - 1);
+    dma1<4>(r, dst + b * CB::STRIDE * 4, m * ROWB + w * 4, so);
   }
 }
 
@@ -169,11 +209,11 @@ __device__ __forceinline__ void kslot_of(int e, int& mm, int& c, int& slot) {
 
 // K-side A operand of MFMA mm for lane (token r, group c): eight codes of
 // one dword times the FP8 scale s' of their group, exact in fp16.
-template <int BITS>
+template <int BITS, class CB>
 __device__ __forceinline__ h8 k_operand(const lds_u8* codes, u32x4 szrow, int mm, int r, int c,
                                         uint32_t magic) {
   const int w = BITS == 4 ? 4 * mm + c : 2 * mm + (c >> 1);
-  const uint32_t x = lds_u32(codes + (w * 16 + r) * 4);
+  const uint32_t x = lds_u32(codes + CB::pos(r, w) * 4);
   // the dword's group (w / 2 for 4 bits, w for 2 bits) has its scale in sz
   // row dword mm, at byte 2 (c >> 1) in both cases
   const uint32_t sdw = szrow[mm];
@@ -242,11 +282,11 @@ __device__ __forceinline__ void v_tables(const lds_u8* szg, lds_u8* tab, int lan
 
 // V-side A operand for group g: element e (lane row) of tokens 4c..4c+3,
 // times their scales (from the plane's table), exact in fp16.
-template <int BITS>
+template <int BITS, class CB>
 __device__ __forceinline__ h4 v_operand(const lds_u8* codes, const lds_u8* tab, int g, int e, int c,
                                         uint32_t magic) {
   const int w = BITS == 4 ? 2 * g + (e >> 3) : g;
-  const u32x4 x = lds_u32x4(codes + (w * 16 + 4 * c) * 4);
+  const u32x4 x = lds_u32x4(codes + CB::pos(4 * c, w) * 4);   // tokens 4c..4c+3
   const u32x4 sc = lds_u32x4(tab + (g * 4 + c) * 16);
   const uint32_t b = BITS == 4 ? (uint32_t)((e >> 1) & 3) : (uint32_t)(e >> 2);
   const uint32_t sh = BITS == 4 ? 4u * (uint32_t)(e & 1) : 2u * (uint32_t)(e & 3);
@@ -351,14 +391,14 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   const int n_tiles = first < t_end ? (t_end - first + NW * TT - 1) / (NW * TT) : 0;
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
-    dma_gather<GS::W1, R1, F>(rk1, tb * R1, vt, st + GS::k1c, lane);
+    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rk1, tb * R1, vt, st + GS::k1c, lane);
     dma_szrows<GS::WS, RS, F>(rk1, s1rel + tb * RS, vt, st + GS::k1s, lane);
-    dma_gather<GS::W1, R1, F>(rv1, tb * R1, vt, st + GS::v1c, lane);
+    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rv1, tb * R1, vt, st + GS::v1c, lane);
     dma_gather<GS::WS, RS, F>(rv1, s1rel + tb * RS, vt, st + GS::v1s, lane);
     if constexpr (TWO) {
-      dma_gather<GS::W2, R2, F>(rk2, tb * R2, vt, st + GS::k2c, lane);
+      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rk2, tb * R2, vt, st + GS::k2c, lane);
       dma_szrows<GS::WS, RS, F>(rk2, s2rel + tb * RS, vt, st + GS::k2s, lane);
-      dma_gather<GS::W2, R2, F>(rv2, tb * R2, vt, st + GS::v2c, lane);
+      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rv2, tb * R2, vt, st + GS::v2c, lane);
       dma_gather<GS::WS, RS, F>(rv2, s2rel + tb * RS, vt, st + GS::v2s, lane);
       dma_alpha(rk2, arel + tb * 2, F ? TT : vt, st + GS::ka, lane);
       dma_alpha(rv2, arel + tb * 2, F ? TT : vt, st + GS::va, lane);
@@ -551,7 +591,8 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       const u32x4 szr = lds_u32x4(st + GS::k1s + r * 16);
 #pragma unroll
       for (int mm = 0; mm < KM1; ++mm)
-        SA = mfma32(k_operand<B1>(st + GS::k1c, szr, mm, r, c, magic), *(lh8*)&fq[mm][lane][0], SA);
+        SA = mfma32(k_operand<B1, typename GS::CB1>(st + GS::k1c, szr, mm, r, c, magic),
+                    *(lh8*)&fq[mm][lane][0], SA);
       // the offset term starts its own accumulator: chaining a 16x16x16 MFMA
       // onto the 16x16x32 results (C operand) gave wrong sums on gfx950
       SA += mfma16(kz_operand<NG>(szr, c), BzQ, (f4){0.f, 0.f, 0.f, 0.f}) * (1.f / kZs);
@@ -562,7 +603,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       const u32x4 szr = lds_u32x4(st + GS::k2s + r * 16);
 #pragma unroll
       for (int mm = 0; mm < KM2; ++mm) {
-        const h8 x = k_operand<B2E>(st + GS::k2c, szr, mm, r, c, magic);
+        const h8 x = k_operand<B2E, typename GS::CB2>(st + GS::k2c, szr, mm, r, c, magic);
         SR = mfma32(x, *(lh8*)&fuh[mm][lane][0], SR);
         SR = mfma32(x, *(lh8*)&ful[mm][lane][0], SR);
       }
@@ -613,7 +654,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       v_tables<NG>(st + GS::v1s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        const h4 x = v_operand<B1>(st + GS::v1c, tab, gq, r, c, magic);
+        const h4 x = v_operand<B1, typename GS::CB1>(st + GS::v1c, tab, gq, r, c, magic);
         OA[gq] = mfma16(x, Ph, OA[gq]);
         OA[gq] = mfma16(x, Pl, OA[gq]);
         __builtin_amdgcn_sched_barrier(0);  // bounds how many groups' loads are hoisted
@@ -634,7 +675,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       v_tables<NG>(st + GS::v2s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        const h4 x = v_operand<B2E>(st + GS::v2c, tab, gq, r, c, magic);
+        const h4 x = v_operand<B2E, typename GS::CB2>(st + GS::v2c, tab, gq, r, c, magic);
         OR_[gq] = mfma16(x, Qh, OR_[gq]);
         OR_[gq] = mfma16(x, Ql, OR_[gq]);
         __builtin_amdgcn_sched_barrier(0);
