@@ -7,13 +7,17 @@
 // MFMA (v_mfma_f32_16x16x32_f16 for Q K^T, v_mfma_f32_16x16x16_f16 for P V);
 // the per-token quantization scales are folded into the code operand first:
 //
-//   * codes enter fp16 through the magic-number unpack (1024 + c), and one
-//     v_pk_fma_f16 with (s', -1024 s') turns a pair into (s' c_a, s' c_b)
-//     EXACTLY: s' is the FP8 scale times 2^-8 read straight from its bits
-//     (an e4m3 byte shifted left by 7 is an fp16 of value x 2^-8, subnormals
-//     included), and s' c has at most 8 significant bits;
-//   * queries are exact in fp16 after a power-of-two prescale per head; the
-//     rotated query H q is not, so it enters as an fp16 high and low part;
+//   * codes enter fp16 through the magic-number unpack (1024 + 2^p c, the
+//     code masked where it sits, p < 8), and one v_pk_fma_f16 with
+//     (s', -1024 s') turns a pair into (2^p s' c_a, 2^p s' c_b) EXACTLY: s'
+//     is the FP8 scale times 2^-8 read straight from its bits (an e4m3 byte
+//     shifted left by 7 is an fp16 of value x 2^-8, subnormals included),
+//     and 2^p s' c has at most 8 significant bits; the 2^p is taken out on
+//     the query side (K) or per output element (V);
+//   * queries are exact in fp16 after a power-of-two prescale per head
+//     (down to 2^-26 of the head's largest element once a slot carries its
+//     2^-p); the rotated query H q is not, so it enters as an fp16 high and
+//     low part;
 //   * offsets z multiply per-group query sums, one more small MFMA whose
 //     K slots are (group, high/low part);
 //   * softmax weights enter the P V products as fp16 high + low parts.
@@ -207,8 +211,20 @@ __device__ __forceinline__ void kslot_of(int e, int& mm, int& c, int& slot) {
   }
 }
 
+// The K-side code pairs are masked where they sit in the dword (after one
+// shift by 8 for the upper half of each 16-bit unit of 4-bit codes): pair k
+// reads 2^p(k) times its codes, p = 0 or 4 for 4 bits, 2k for 2 bits.  The
+// matching query slots carry 2^-p(k) (exact: a power of two), so each
+// product is unchanged.
+template <int BITS>
+__device__ __forceinline__ float kslot_factor(int slot) {
+  const int k = slot >> 1;
+  return BITS == 4 ? ((k & 1) ? 1.f / 16.f : 1.f) : 1.f / (float)(1 << (2 * k));
+}
+
 // K-side A operand of MFMA mm for lane (token r, group c): eight codes of
-// one dword times the FP8 scale s' of their group, exact in fp16.
+// one dword times the FP8 scale s' of their group (and 2^p(k)), exact in
+// fp16: at most 8 significant bits, below 2^9.
 template <int BITS, class CB>
 __device__ __forceinline__ h8 k_operand(const lds_u8* codes, u32x4 szrow, int mm, int r, int c,
                                         uint32_t magic) {
@@ -222,9 +238,10 @@ __device__ __forceinline__ h8 k_operand(const lds_u8* codes, u32x4 szrow, int mm
   const h2 op = sp * (h2){(_Float16)-1024.f, (_Float16)-1024.f};
   h8 a;
   if constexpr (BITS == 4) {
+    const uint32_t xh = x >> 8;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const h2 v = pk_fma(as_h2(and_or(x >> (4 * k), 0x000F000Fu, magic)), sp, op);
+      const h2 v = pk_fma(as_h2(and_or(k < 2 ? x : xh, 0x000F000Fu << (4 * (k & 1)), magic)), sp, op);
       a[2 * k] = v.x;
       a[2 * k + 1] = v.y;
     }
@@ -232,7 +249,7 @@ __device__ __forceinline__ h8 k_operand(const lds_u8* codes, u32x4 szrow, int mm
     const uint32_t xs = x >> (8 * (c & 1));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const h2 v = pk_fma(as_h2(and_or(xs >> (2 * k), 0x00030003u, magic)), sp, op);
+      const h2 v = pk_fma(as_h2(and_or(xs, 0x00030003u << (2 * k), magic)), sp, op);
       a[2 * k] = v.x;
       a[2 * k + 1] = v.y;
     }
@@ -280,21 +297,40 @@ __device__ __forceinline__ void v_tables(const lds_u8* szg, lds_u8* tab, int lan
   }
 }
 
+// V-side code pairs: the byte holding element e's code of two tokens goes
+// to the low byte of each half, and the code is masked where it sits, at bit
+// sh(e) of that byte: the pair reads 1024 + 2^sh c, and the scale fold gives
+// 2^sh s' c, still exact (at most 8 significant bits, below 2^9).  The
+// factor 2^sh(e) is taken out of the element's value sum at the end
+// (v_unshift); sh(e) depends on e mod 4 only, which is the MFMA output item.
+template <int BITS>
+__device__ __forceinline__ uint32_t v_mask(int e) {
+  const uint32_t m = BITS == 4 ? 0xFu << (4 * (e & 1)) : 0x3u << (2 * (e & 3));
+  return m | (m << 16);
+}
+template <int BITS>
+__device__ __forceinline__ f4 v_unshift() {
+  return BITS == 4 ? (f4){1.f, 1.f / 16.f, 1.f, 1.f / 16.f} : (f4){1.f, 1.f / 4.f, 1.f / 16.f, 1.f / 64.f};
+}
+__device__ __forceinline__ uint32_t and_or_v(uint32_t x, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
+  return r;
+}
+
 // V-side A operand for group g: element e (lane row) of tokens 4c..4c+3,
-// times their scales (from the plane's table), exact in fp16.
+// times their scales (from the plane's table) and 2^sh(e), exact in fp16.
 template <int BITS, class CB>
 __device__ __forceinline__ h4 v_operand(const lds_u8* codes, const lds_u8* tab, int g, int e, int c,
-                                        uint32_t magic) {
+                                        uint32_t mask, uint32_t magic) {
   const int w = BITS == 4 ? 2 * g + (e >> 3) : g;
   const u32x4 x = lds_u32x4(codes + CB::pos(4 * c, w) * 4);   // tokens 4c..4c+3
   const u32x4 sc = lds_u32x4(tab + (g * 4 + c) * 16);
   const uint32_t b = BITS == 4 ? (uint32_t)((e >> 1) & 3) : (uint32_t)(e >> 2);
-  const uint32_t sh = BITS == 4 ? 4u * (uint32_t)(e & 1) : 2u * (uint32_t)(e & 3);
-  const uint32_t mask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-  const uint32_t p01 = __builtin_amdgcn_perm(x.y, x.x, sel2(b)) >> sh;
-  const uint32_t p23 = __builtin_amdgcn_perm(x.w, x.z, sel2(b)) >> sh;
-  const h2 v01 = pk_fma(as_h2(and_or(p01, mask, magic)), as_h2(sc.x), as_h2(sc.z));
-  const h2 v23 = pk_fma(as_h2(and_or(p23, mask, magic)), as_h2(sc.y), as_h2(sc.w));
+  const uint32_t p01 = __builtin_amdgcn_perm(x.y, x.x, sel2(b));
+  const uint32_t p23 = __builtin_amdgcn_perm(x.w, x.z, sel2(b));
+  const h2 v01 = pk_fma(as_h2(and_or_v(p01, mask, magic)), as_h2(sc.x), as_h2(sc.z));
+  const h2 v23 = pk_fma(as_h2(and_or_v(p23, mask, magic)), as_h2(sc.y), as_h2(sc.w));
   return (h4){v01.x, v01.y, v23.x, v23.y};
 }
 
@@ -493,10 +529,10 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     {
       int mm, cc, sl;
       kslot_of<B1>(lane, mm, cc, sl);
-      fq[mm][n + 16 * cc][sl] = (_Float16)x0;
+      fq[mm][n + 16 * cc][sl] = (_Float16)(x0 * kslot_factor<B1>(sl));
       if (v1ok) {
         kslot_of<B1>(lane + 64, mm, cc, sl);
-        fq[mm][n + 16 * cc][sl] = (_Float16)x1;
+        fq[mm][n + 16 * cc][sl] = (_Float16)(x1 * kslot_factor<B1>(sl));
       }
     }
     float s0 = x0, s1 = x1;
@@ -524,12 +560,12 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       {
         int mm, cc, sl;
         kslot_of<B2E>(lane, mm, cc, sl);
-        h2 hl = split_hl(y0);
+        h2 hl = split_hl(y0 * kslot_factor<B2E>(sl));
         fuh[mm][n + 16 * cc][sl] = hl.x;
         ful[mm][n + 16 * cc][sl] = hl.y;
         if (v1ok) {
           kslot_of<B2E>(lane + 64, mm, cc, sl);
-          hl = split_hl(y1);
+          hl = split_hl(y1 * kslot_factor<B2E>(sl));
           fuh[mm][n + 16 * cc][sl] = hl.x;
           ful[mm][n + 16 * cc][sl] = hl.y;
         }
@@ -576,6 +612,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < (TWO ? NG : 1); ++i) OR_[i] = (f4){0.f, 0.f, 0.f, 0.f};
   float m = kEmpty, l = 0.f;
+  const uint32_t vm1 = v_mask<B1>(r), vm2 = v_mask<B2E>(r);   // this lane's element row
 
   for (int it = 0; it < n_tiles; ++it) {
     // tile it + 1 goes into the slot tile it - 1 has left
@@ -654,7 +691,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       v_tables<NG>(st + GS::v1s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        const h4 x = v_operand<B1, typename GS::CB1>(st + GS::v1c, tab, gq, r, c, magic);
+        const h4 x = v_operand<B1, typename GS::CB1>(st + GS::v1c, tab, gq, r, c, vm1, magic);
         OA[gq] = mfma16(x, Ph, OA[gq]);
         OA[gq] = mfma16(x, Pl, OA[gq]);
         __builtin_amdgcn_sched_barrier(0);  // bounds how many groups' loads are hoisted
@@ -675,7 +712,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
       v_tables<NG>(st + GS::v2s, tab, lane);
 #pragma unroll
       for (int gq = 0; gq < NG; ++gq) {
-        const h4 x = v_operand<B2E, typename GS::CB2>(st + GS::v2c, tab, gq, r, c, magic);
+        const h4 x = v_operand<B2E, typename GS::CB2>(st + GS::v2c, tab, gq, r, c, vm2, magic);
         OR_[gq] = mfma16(x, Qh, OR_[gq]);
         OR_[gq] = mfma16(x, Ql, OR_[gq]);
         __builtin_amdgcn_sched_barrier(0);
@@ -706,10 +743,10 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int gq = 0; gq < NG; ++gq) {
       f4* pa = reinterpret_cast<f4*>(row + 16 * gq + 4 * c);
-      *pa = (add ? *pa : (f4){0.f, 0.f, 0.f, 0.f}) + f * OA[gq];
+      *pa = (add ? *pa : (f4){0.f, 0.f, 0.f, 0.f}) + (f * v_unshift<B1>()) * OA[gq];
       if constexpr (TWO) {
         f4* pr = reinterpret_cast<f4*>(row + D + 16 * gq + 4 * c);
-        *pr = (add ? *pr : (f4){0.f, 0.f, 0.f, 0.f}) + f * OR_[gq];
+        *pr = (add ? *pr : (f4){0.f, 0.f, 0.f, 0.f}) + (f * v_unshift<B2E>()) * OR_[gq];
       }
     }
 #pragma unroll
