@@ -535,12 +535,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
         fq[mm][n + 16 * cc][sl] = (_Float16)(x1 * kslot_factor<B1>(sl));
       }
     }
-    float s0 = x0, s1 = x1;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      s0 += __shfl_xor(s0, o);
-      s1 += __shfl_xor(s1, o);
-    }
+    const float s0 = row_sum16(x0), s1 = row_sum16(x1);
     if (r == 0) {
       sqs[n][c] = s0;
       if (c + 4 < NG) sqs[n][c + 4] = s1;
@@ -570,12 +565,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
           ful[mm][n + 16 * cc][sl] = hl.y;
         }
       }
-      float t0 = y0, t1 = y1;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        t0 += __shfl_xor(t0, o);
-        t1 += __shfl_xor(t1, o);
-      }
+      const float t0 = row_sum16(y0), t1 = row_sum16(y1);
       if (r == 0) {
         sus[n][c] = t0;
         if (c + 4 < NG) sus[n][c + 4] = t1;
@@ -694,7 +684,8 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
         const h4 x = v_operand<B1, typename GS::CB1>(st + GS::v1c, tab, gq, r, c, vm1, magic);
         OA[gq] = mfma16(x, Ph, OA[gq]);
         OA[gq] = mfma16(x, Pl, OA[gq]);
-        __builtin_amdgcn_sched_barrier(0);  // bounds how many groups' loads are hoisted
+        // bounds how many groups' loads are hoisted: two groups at a time
+        if (gq & 1) __builtin_amdgcn_sched_barrier(0);
       }
       const h4 z = vz_operand<NG>(tab, r, c);
       OZA = mfma16(z, Ph, OZA);
@@ -715,7 +706,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
         const h4 x = v_operand<B2E, typename GS::CB2>(st + GS::v2c, tab, gq, r, c, vm2, magic);
         OR_[gq] = mfma16(x, Qh, OR_[gq]);
         OR_[gq] = mfma16(x, Ql, OR_[gq]);
-        __builtin_amdgcn_sched_barrier(0);
+        if (gq & 1) __builtin_amdgcn_sched_barrier(0);
       }
       const h4 z = vz_operand<NG>(tab, r, c);
       OZR = mfma16(z, Qh, OZR);

@@ -94,24 +94,74 @@ __device__ __forceinline__ uint32_t lds_u16(const lds_u8* p) {
 }
 
 // ------------------------------------------------------------ wave helpers
+// Cross-lane moves inside 16-lane rows by DPP (a VALU modifier, no LDS round
+// trip as for ds_bpermute): quad permutations, row shifts and mirrors.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShl4 = 0x104;    // lane i reads lane i + 4 of its row
+constexpr int kDppRowShr4 = 0x114;    // lane i reads lane i - 4
+constexpr int kDppRowShl8 = 0x108;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppHalfMirror = 0x141;  // lane i reads lane 7 - i of its half row
+constexpr int kDppRowMirror = 0x140;   // lane i reads lane 15 - i of its row
+
+// Lanes whose source is outside the row keep their own value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane (lane ^ H).  For H = 4 and 8 both row shifts run on all
+// lanes before the select: a DPP read from a lane that is switched off (as
+// in either arm of a branch on the lane's bit) does not return its value.
+template <int H>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  if constexpr (H == 1) {
+    return dpp_f<kDppQuadXor1>(v);
+  } else if constexpr (H == 2) {
+    return dpp_f<kDppQuadXor2>(v);
+  } else if constexpr (H == 4 || H == 8) {
+    const float up = dpp_f<H == 4 ? kDppRowShl4 : kDppRowShl8>(v);
+    const float down = dpp_f<H == 4 ? kDppRowShr4 : kDppRowShr8>(v);
+    return (lane & H) ? down : up;
+  } else {
+    return __shfl_xor(v, H);
+  }
+}
+
+// Sum and maximum over each 16-lane row (every lane of the row gets them):
+// after the two quad steps a quad holds its total, the half mirror pairs
+// the quads of each half row and the mirror the two halves.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppRowMirror>(v);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppRowMirror>(v));
+}
+
+// One butterfly stage of the transform below: lane i pairs with i ^ H.
+template <int H>
+__device__ __forceinline__ float wht_stage(float y, int lane) {
+  const float p = xor_lane<H>(y, lane);
+  return (lane & H) ? (p - y) : (y + p);
+}
+
 // Walsh-Hadamard transform of a vector held two elements per lane (l, l+64)
 // by one wave; block diagonal 64+32 when D == 96.  Unscaled.
 template <int D>
 __device__ __forceinline__ void wave_wht(float& y0, float& y1, int lane) {
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float p0 = __shfl_xor(y0, h);
-    y0 = (lane & h) ? (p0 - y0) : (y0 + p0);
-    if constexpr (D == 128) {
-      const float p1 = __shfl_xor(y1, h);
-      y1 = (lane & h) ? (p1 - y1) : (y1 + p1);
-    } else if constexpr (D == 96) {
-      if (h < 32) {
-        const float p1 = __shfl_xor(y1, h);
-        y1 = (lane & h) ? (p1 - y1) : (y1 + p1);
-      }
-    }
-  }
+  static_for<6>([&](auto K) {
+    constexpr int h = 1 << decltype(K)::value;
+    y0 = wht_stage<h>(y0, lane);
+    if constexpr (D == 128 || (D == 96 && h < 32)) y1 = wht_stage<h>(y1, lane);
+  });
   if constexpr (D == 128) {
     const float a = y0, b = y1;
     y0 = a + b;
@@ -120,9 +170,9 @@ __device__ __forceinline__ void wave_wht(float& y0, float& y1, int lane) {
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row_max16(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
 // 2^k with max|v| * 2^k in [2^13, 2^14): fp16 then holds BF16 inputs exactly.
