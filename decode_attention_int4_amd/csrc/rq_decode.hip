@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   using ST = Stage<D, B1, B2, NR>;
   constexpr int kStaging = NW * ST::COUNT * ST::BYTES;
   constexpr int kRow = (TWO ? 2 * D : D) + 1;              // accA | accR | l
-  constexpr int kEpilogue = NW * LY::PAIRS * kRow * 4;
+  constexpr int kEpilogue = NW * kRow * 4;
   // the epilogue buffers reuse the staging area once every wave has finished
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
   __shared__ float sq[D], su[D];
@@ -338,8 +338,8 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   __shared__ uint32_t s_ticket;
   // the query row (BF16) and this layer's key signs, staged by DMA
   __shared__ __attribute__((aligned(16))) uint8_t s_in[512];
-  typedef float AccRows[LY::PAIRS][kRow];
-  AccRows* sm_acc = reinterpret_cast<AccRows*>(smem);             // [wave][pair][accA | accR | l]
+  typedef float AccRow[kRow];
+  AccRow* sm_acc = reinterpret_cast<AccRow*>(smem);               // [wave][accA | accR | l]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -700,15 +700,29 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
                      f * (zR - WR * (1024.f / (mR * kWR) + c0 / kWR)));
     }
   });
-  // ---- every lane's partial sums to LDS: [wave][token pair][accA | accR | l]
-  if (active) {
+  // ---- sum over the wave's token pairs (the lane bits above the group
+  // index) in registers, then the first pair's lanes write the wave's sums:
+  // [wave][accA | accR | l]
+  auto pairs_sum = [&](float v) __attribute__((always_inline)) {
+    if constexpr (LPP == 4) v += xor_lane<4>(v, lane);
+    v += dpp_f<kDppRowRor8>(v);
+    return pair_add<32>(pair_add<16>(v));
+  };
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm_acc[w][pj][e * 16 + i] = accA[i];
+  for (int i = 0; i < 16; ++i) accA[i] = pairs_sum(accA[i]);
+  if constexpr (TWO) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accR[i] = pairs_sum(accR[i]);
+  }
+  l = pairs_sum(l);
+  if (active && pj == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm_acc[w][e * 16 + i] = accA[i];
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm_acc[w][pj][D + e * 16 + i] = accR[i];
+      for (int i = 0; i < 16; ++i) sm_acc[w][D + e * 16 + i] = accR[i];
     }
-    if (e == 0) sm_acc[w][pj][kRow - 1] = l;
+    if (e == 0) sm_acc[w][kRow - 1] = l;
   }
   if (lane == 0) sm_m[w] = Mw;
   __syncthreads();
@@ -722,13 +736,8 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   for (int ww = 0; ww < NW; ++ww) fw[ww] = exp2f(sm_m[ww] - M);
   auto merged = [&](int i) {
     float s = 0.f;
-#pragma unroll 1
-    for (int ww = 0; ww < NW; ++ww) {
-      float t = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < LY::PAIRS; ++j) t += sm_acc[ww][j][i];
-      s = fmaf(t, fw[ww], s);
-    }
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s = fmaf(sm_acc[ww][i], fw[ww], s);
     return s;
   };
   if (a.splits > 1) {

@@ -648,8 +648,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 
     // ---- online softmax per head (the four lanes of a head agree)
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max<32>(pair_max<16>(mx));
     if (mx > m + kLazy) {
       const float corr = __builtin_amdgcn_exp2f(m - mx);
       l *= corr;
@@ -717,8 +716,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   // ---- merge the waves: running max per head, then the G heads' sums of
   // every wave side by side (one round), or, for G > 8, two waves into each
   // of two regions (two rounds)
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = pair_add<32>(pair_add<16>(l));
   if (c == 0) {
     sm_m[w][r] = m;
     sm_l[w][r] = l;

@@ -104,12 +104,28 @@ constexpr int kDppRowShl8 = 0x108;
 constexpr int kDppRowShr8 = 0x118;
 constexpr int kDppHalfMirror = 0x141;  // lane i reads lane 7 - i of its half row
 constexpr int kDppRowMirror = 0x140;   // lane i reads lane 15 - i of its row
+constexpr int kDppRowRor8 = 0x128;     // lane i reads lane (i + 8) mod 16 = i ^ 8
 
 // Lanes whose source is outside the row keep their own value.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   const int x = __builtin_bit_cast(int, v);
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+}
+
+// Rows and halves of the wave across lanes by the gfx950 permlane swaps
+// (VALU, no LDS round trip).  With both operands v, permlane16_swap returns
+// rows (0, 0, 2, 2) and (1, 1, 3, 3) of v and permlane32_swap the halves
+// (low, low) and (high, high): the two results at a lane are v of the lane
+// and of its partner lane ^ 16 (lane ^ 32), in row (half) order.
+typedef float fpair __attribute__((ext_vector_type(2)));
+template <int H>
+__device__ __forceinline__ fpair swap_rows(float v) {
+  static_assert(H == 16 || H == 32, "row or half swap");
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = H == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return (fpair){__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
 }
 
 // The value of lane (lane ^ H).  For H = 4 and 8 both row shifts run on all
@@ -126,8 +142,21 @@ __device__ __forceinline__ float xor_lane(float v, int lane) {
     const float down = dpp_f<H == 4 ? kDppRowShr4 : kDppRowShr8>(v);
     return (lane & H) ? down : up;
   } else {
-    return __shfl_xor(v, H);
+    const fpair r = swap_rows<H>(v);
+    return (lane & H) ? r.x : r.y;
   }
+}
+
+// Sum and maximum of v over lanes l and l ^ H (H = 16, 32).
+template <int H>
+__device__ __forceinline__ float pair_add(float v) {
+  const fpair r = swap_rows<H>(v);
+  return r.x + r.y;
+}
+template <int H>
+__device__ __forceinline__ float pair_max(float v) {
+  const fpair r = swap_rows<H>(v);
+  return fmaxf(r.x, r.y);
 }
 
 // Sum and maximum over each 16-lane row (every lane of the row gets them):
@@ -170,9 +199,7 @@ __device__ __forceinline__ void wave_wht(float& y0, float& y1, int lane) {
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-  v = row_max16(v);
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  return pair_max<32>(pair_max<16>(row_max16(v)));
 }
 
 // 2^k with max|v| * 2^k in [2^13, 2^14): fp16 then holds BF16 inputs exactly.
