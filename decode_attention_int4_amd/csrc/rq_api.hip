@@ -11,7 +11,6 @@
 #include "rq_layout.h"
 
 namespace rq {
-int decode_tile_tokens(int d);
 int decode_wave_tokens(int d);
 int bf16_tile_tokens();
 
@@ -25,6 +24,7 @@ int bf16_tile_tokens();
 static constexpr int32_t kDecodeTargetTwo = 512;
 static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
+static constexpr int32_t kDecodeTargetWide = 256;   // eight-wave workgroups: one per CU
 static constexpr int32_t kGqaTarget = 512;         // grouped-query kernel
 static constexpr int32_t kDecodeTarget = 512;      // the largest target: workspace bound
 static constexpr int32_t kBf16Target = 512;
@@ -261,7 +261,8 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
                               int32_t max_n_tokens) {
   if (check_desc(desc) != RQ_OK || q_heads <= 0 || rows <= 0) return 0;
   const int32_t bh = rows * q_heads;
-  int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim),
+  // four-wave tiles at the largest target bound the eight-wave plans too
+  int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim, 4),
                                    rq::kDecodeTarget);
   bool any_grouped = false;
   for (int32_t loop = 0; loop < desc->loops_per_group; ++loop)
@@ -310,12 +311,15 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
   const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
   const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
-  const int32_t target =
-      chain ? rq::kDecodeTargetChain : two ? rq::kDecodeTargetTwo : rq::kDecodeTargetOne;
+  const int waves = rq::decode_waves(desc->head_dim, chain, pg.table != nullptr);
+  const int32_t target = waves == 8 ? rq::kDecodeTargetWide
+                         : chain    ? rq::kDecodeTargetChain
+                         : two      ? rq::kDecodeTargetTwo
+                                    : rq::kDecodeTargetOne;
   const rq::SplitPlan plan =
       grouped(desc, loop, q_heads)
           ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget)
-          : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim), target);
+          : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim, waves), target);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);
@@ -335,6 +339,7 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   a.splits = plan.splits;
   a.tokens_per_split = plan.tokens_per_split;
   a.qscale = softmax_scale * 1.4426950408889634f;
+  a.waves = waves;
   return rq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
 }
 

@@ -314,8 +314,8 @@ __device__ __forceinline__ void value_acc(const PairPlane<BITS>& pp, h2 wh, h2 w
 // wave tile (TPW tokens, block sizes are powers of two >= TPW) never straddles
 // two blocks, so the tile's buffer resources are rebuilt from its block's
 // slots, with the block id read through the scalar cache.
-template <int D, int B1, int B2, int NR, bool PAGED>
-__global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
+template <int D, int B1, int B2, int NR, bool PAGED, int NWK>
+__global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(DecodeArgs a) {
   using LY = Lay<D>;
   constexpr int NG = LY::NG, LPP = LY::LPP, TPW = LY::TPW;
   constexpr bool TWO = B2 != 0;
@@ -324,9 +324,9 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   const Geometry& g = a.g;
 
   using ST = Stage<D, B1, B2, NR>;
-  constexpr int kStaging = NW * ST::COUNT * ST::BYTES;
+  constexpr int kStaging = NWK * ST::COUNT * ST::BYTES;
   constexpr int kRow = (TWO ? 2 * D : D) + 1;              // accA | accR | l
-  constexpr int kEpilogue = NW * kRow * 4;
+  constexpr int kEpilogue = NWK * kRow * 4;
   // the epilogue buffers reuse the staging area once every wave has finished
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
   __shared__ float sq[D], su[D];
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   // per-group query pairs; rows padded to 36 dwords so that the 16-byte
   // reads of the eight groups' rows fall in eight different bank quads
   __shared__ __attribute__((aligned(16))) uint32_t spre[8][36];
-  __shared__ float sm_m[NW];
+  __shared__ float sm_m[NWK];
   __shared__ uint32_t s_ticket;
   // the query row (BF16) and this layer's key signs, staged by DMA
   __shared__ __attribute__((aligned(16))) uint8_t s_in[512];
@@ -393,7 +393,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   // ---- stream this wave's tiles through its LDS ring
   lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
   const int first = t_begin + w * TPW;
-  const int n_tiles = first < t_end ? (t_end - first + NW * TPW - 1) / (NW * TPW) : 0;
+  const int n_tiles = first < t_end ? (t_end - first + NWK * TPW - 1) / (NWK * TPW) : 0;
   // tiles in flight before the query side is built: the whole ring, unless
   // its DMA count would not fit the wait below
   constexpr int kPre = ST::COUNT * ST::N_DMA < 64 ? ST::COUNT : ST::COUNT - 1;
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     }
   };
   auto issue = [&](int tile) __attribute__((always_inline)) {
-    uint32_t tb = (uint32_t)(first + tile * NW * TPW);
+    uint32_t tb = (uint32_t)(first + tile * NWK * TPW);
     lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
     const int vt = t_end - (int)tb;  // in-range tokens of this tile (>= 1)
     if constexpr (PAGED) {
@@ -561,7 +561,7 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
     else if (later >= 1) wait_vm<ST::N_DMA>();
     else wait_vm<0>();
     const lds_u8* st = ring + (it % ST::COUNT) * ST::BYTES;
-    const int tt = first + it * NW * TPW + t0;
+    const int tt = first + it * NWK * TPW + t0;
     const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
     // keys now; the value planes are read after the softmax update, so their
@@ -730,21 +730,21 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
   // ---- merge the waves and token pairs: this workgroup's state for its range
   float M = sm_m[0];
 #pragma unroll
-  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww]);
-  float fw[NW];
+  for (int ww = 1; ww < NWK; ++ww) M = fmaxf(M, sm_m[ww]);
+  float fw[NWK];
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) fw[ww] = exp2f(sm_m[ww] - M);
+  for (int ww = 0; ww < NWK; ++ww) fw[ww] = exp2f(sm_m[ww] - M);
   auto merged = [&](int i) {
     float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) s = fmaf(sm_acc[ww][i], fw[ww], s);
+    for (int ww = 0; ww < NWK; ++ww) s = fmaf(sm_acc[ww][i], fw[ww], s);
     return s;
   };
   if (a.splits > 1) {
     // partial state (m, l, accA[D], accR[D]) of this split; the workgroup
     // that finishes the row last merges all of them
     float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + 2 * D);
-    for (int i = tid; i <= 2 * D; i += NW * 64) {
+    for (int i = tid; i <= 2 * D; i += NWK * 64) {
       if (i == 2 * D) {
         store_dev(mine, M);
         store_dev(mine + 1, merged(kRow - 1));
@@ -780,10 +780,16 @@ __global__ void __launch_bounds__(NW * 64, 3) decode_kernel(DecodeArgs a) {
 template <int D, int B1, int B2, int NR = 1>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.splits, a.rows * a.q_heads);
-  if (a.paging.table)
-    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true>), grid, dim3(NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false>), grid, dim3(NW * 64), 0, s, a);
+  if (a.paging.table) {
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true, 4>), grid, dim3(4 * 64), 0, s, a);
+  } else if constexpr (D == 128 && NR == 1) {
+    if (a.waves == 8)
+      hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 8>), grid, dim3(8 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 4>), grid, dim3(4 * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 4>), grid, dim3(4 * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -818,11 +824,19 @@ int decode_wave_tokens(int d) {
   }
 }
 
-int decode_tile_tokens(int d) {
+// Waves per workgroup: eight (one workgroup per CU, half the splits to
+// merge) for d = 128 calls reading at most one residual plane from a
+// contiguous cache, where that measured faster; four otherwise (eight were
+// slower at d = 96, for chained loops and for paged anchors).
+int decode_waves(int d, bool several_planes, bool paged) {
+  return (d == 128 && !several_planes && !paged) ? 8 : 4;
+}
+
+int decode_tile_tokens(int d, int waves) {
   switch (d) {
-    case 64: return NW * Lay<64>::TPW;
-    case 96: return NW * Lay<96>::TPW;
-    default: return NW * Lay<128>::TPW;
+    case 64: return waves * Lay<64>::TPW;
+    case 96: return waves * Lay<96>::TPW;
+    default: return waves * Lay<128>::TPW;
   }
 }
 

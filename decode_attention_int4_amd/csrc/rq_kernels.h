@@ -58,8 +58,12 @@ struct DecodeArgs {
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;
   float qscale;           // softmax scale * log2(e)
+  int32_t waves;          // per-head kernel: waves per workgroup (decode_waves)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// per-head kernel geometry, shared by the split plan and the launch
+int decode_waves(int d, bool several_planes, bool paged);
+int decode_tile_tokens(int d, int waves);
 // grouped-query decode on matrix cores: one workgroup per (split, batch row,
 // KV head) serves the group_ratio query heads of the KV head
 bool gqa_supported(const Geometry& g, int loop, int group_ratio);
