@@ -25,7 +25,7 @@ static constexpr int32_t kDecodeTargetTwo = 512;
 static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
 static constexpr int32_t kDecodeTargetWide = 256;   // eight-wave workgroups: one per CU
-static constexpr int32_t kGqaTarget = 512;         // grouped-query kernel
+static constexpr int32_t kGqaTarget = 256;         // grouped-query kernel (eight waves: one per CU)
 static constexpr int32_t kDecodeTarget = 512;      // the largest target: workspace bound
 static constexpr int32_t kBf16Target = 512;
 

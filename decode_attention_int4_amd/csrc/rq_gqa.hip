@@ -53,6 +53,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int TT = 16;  // tokens per wave tile
+// Waves per workgroup: eight, one workgroup per CU at a 256-workgroup split
+// target (two waves per SIMD); measured faster than four waves at 512.
+constexpr int NWG = 8;
 // Group sums of prescaled queries reach 16 * 2^14: they enter fp16 scaled by
 // 2^-4 and the offset products are scaled back in fp32.
 constexpr float kZs = 1.f / 16.f;
@@ -352,19 +355,19 @@ __device__ __forceinline__ h2 split_hl(float v) {
 }
 
 template <int D, int B1, int B2, bool PAGED>
-__global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   using GS = GStage<D, B1, B2>;
   constexpr int NG = GS::NG;
   constexpr bool TWO = GS::TWO;
   constexpr int B2E = TWO ? B2 : 2;
   constexpr int KM1 = GS::KM1, KM2 = GS::KM2;
   constexpr int R1 = D * B1 / 8, R2 = D * B2E / 8, RS = GS::RS;
-  constexpr int kRing = NW * 2 * GS::BYTES;
+  constexpr int kRing = NWG * 2 * GS::BYTES;
   // merge rows of one head: value sums (first plane | residual) and the
   // offset sums per group, padded to whole float4s plus one
   constexpr int kZOff = (TWO ? 2 : 1) * D;
   constexpr int kRowF = (kZOff + (TWO ? 2 : 1) * NG + 3) / 4 * 4 + 4;
-  constexpr int kMerge = 32 * kRowF * 4;   // 4 regions x 8 heads, or 2 x 16
+  constexpr int kMerge = NWG * 8 * kRowF * 4;   // NWG regions x 8 heads, or NWG / 2 x 16
   const Geometry& g = a.g;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kMerge ? kRing : kMerge];
@@ -381,7 +384,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   QOp* ful = fuh + (TWO ? KM2 : 1);
   __shared__ float sqs[16][8], sus[16][8];       // per-group sums of the two
   __shared__ float spq[16], spu[16];             // per-head prescales
-  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ float sm_m[NWG][16], sm_l[NWG][16];
   __shared__ uint32_t s_ticket;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -424,7 +427,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   // ---- this wave's tiles through its two-stage ring
   lds_u8* ring = (lds_u8*)smem + w * 2 * GS::BYTES;
   const int first = t_begin + w * TT;
-  const int n_tiles = first < t_end ? (t_end - first + NW * TT - 1) / (NW * TT) : 0;
+  const int n_tiles = first < t_end ? (t_end - first + NWG * TT - 1) / (NWG * TT) : 0;
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
     dma_blocks<typename GS::CB1, GS::W1, R1, F>(rk1, tb * R1, vt, st + GS::k1c, lane);
@@ -441,7 +444,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     }
   };
   auto issue = [&](int tile) __attribute__((always_inline)) {
-    uint32_t tb = (uint32_t)(first + tile * NW * TT);
+    uint32_t tb = (uint32_t)(first + tile * NWG * TT);
     lds_u8* st = ring + (tile & 1) * GS::BYTES;
     const int vt = t_end - (int)tb;
     if constexpr (PAGED) {
@@ -459,7 +462,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   // after the tile's DMAs would wait for all of them.  (Issuing the second
   // tile here as well measured slower.)
   lds_u8* stage = (lds_u8*)qop;
-  for (int n = w; n < G; n += NW) {
+  for (int n = w; n < G; n += NWG) {
     const uint16_t* qrow = a.q + ((uint64_t)b * a.q_heads + kvh * G + n) * D;
     dma1<4>(make_rsrc((const uint8_t*)qrow, 2 * D), stage + n * 256, min(4 * lane, 2 * D - 4), 0u);
   }
@@ -470,12 +473,12 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   if (n_tiles > 0) wait_vm<GS::N_DMA>();
   else wait_vm<0>();
   __syncthreads();   // every wave's rows and the signs are in LDS
-  constexpr int kHw = 16 / NW;   // operand columns per wave
+  constexpr int kHw = 16 / NWG;   // operand columns per wave
   const bool v1ok = (D > 64) && (lane + 64 < D);
   float qv0[kHw], qv1[kHw];
 #pragma unroll
   for (int j = 0; j < kHw; ++j) {
-    const int n = w + NW * j;
+    const int n = w + NWG * j;
     const lds_u8* row = stage + min(n, 15) * 256;
     qv0[j] = n < G ? bf16_to_f32(lds_u16(row + 2 * lane)) : 0.f;
     qv1[j] = (n < G && v1ok) ? bf16_to_f32(lds_u16(row + 2 * (lane + 64))) : 0.f;
@@ -492,7 +495,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   // the columns n >= G are zero
 #pragma unroll
   for (int j = 0; j < kHw; ++j) {
-    const int n = w + NW * j;
+    const int n = w + NWG * j;
     if (n >= G) {
       int mm, cc, sl;
       kslot_of<B1>(lane, mm, cc, sl);
@@ -610,7 +613,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     if (it + 1 < n_tiles) wait_vm<GS::N_DMA>();
     else wait_vm<0>();
     const lds_u8* st = ring + (it & 1) * GS::BYTES;
-    const int vt = t_end - (first + it * NW * TT);  // in-range tokens of this tile
+    const int vt = t_end - (first + it * NWG * TT);  // in-range tokens of this tile
 
     // ---- logits S^T (lane: head r, tokens 4c + j)
     f4 SA = {0.f, 0.f, 0.f, 0.f};
@@ -715,7 +718,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
 
   // ---- merge the waves: running max per head, then the G heads' sums of
   // every wave side by side (one round), or, for G > 8, two waves into each
-  // of two regions (two rounds)
+  // of NWG / 2 regions (two rounds); either way at most 64 head rows
   l = pair_add<32>(pair_add<16>(l));
   if (c == 0) {
     sm_m[w][r] = m;
@@ -724,9 +727,9 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   __syncthreads();  // every wave is done with its ring: the merge regions reuse it
   float M = sm_m[0][r];
 #pragma unroll
-  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][r]);
+  for (int ww = 1; ww < NWG; ++ww) M = fmaxf(M, sm_m[ww][r]);
   const float f = exp2f(m - M) * 256.f;  // also takes out the 2^-8 of s' and z'
-  const int nreg = G <= 8 ? NW : 2;
+  const int nreg = G <= 8 ? NWG : NWG / 2;   // regions: at most 64 head rows
   float* regs = reinterpret_cast<float*>(smem);   // [region][head][kRowF]
   auto put = [&](float* row, bool add) __attribute__((always_inline)) {
 #pragma unroll
@@ -752,7 +755,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     }
   };
   if (r < G && w < nreg) put(regs + (w * G + r) * kRowF, false);
-  if (nreg < NW) {
+  if (nreg < NWG) {
     __syncthreads();
     if (r < G && w >= nreg) put(regs + ((w - nreg) * G + r) * kRowF, true);
   }
@@ -760,15 +763,15 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
   auto head_l = [&](int n) {
     float s = 0.f, Mn = sm_m[0][n];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
+    for (int ww = 1; ww < NWG; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) s = fmaf(exp2f(sm_m[ww][n] - Mn), sm_l[ww][n], s);
+    for (int ww = 0; ww < NWG; ++ww) s = fmaf(exp2f(sm_m[ww][n] - Mn), sm_l[ww][n], s);
     return s;
   };
   auto head_m = [&](int n) {
     float Mn = sm_m[0][n];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
+    for (int ww = 1; ww < NWG; ++ww) Mn = fmaxf(Mn, sm_m[ww][n]);
     return Mn;
   };
   // element e of head n's value sum (plane 0: first plane, 1: residual)
@@ -787,7 +790,7 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
     // kernel writes it
     constexpr int Wd = 2 + 2 * D;
-    for (int i = tid; i < G * Wd; i += NW * 64) {
+    for (int i = tid; i < G * Wd; i += NWG * 64) {
       const int n = i / Wd, k = i % Wd;
       const int bh = b * a.q_heads + kvh * G + n;
       float* mine = a.partials + ((uint64_t)bh * a.splits + split) * Wd;
@@ -802,11 +805,11 @@ __global__ void __launch_bounds__(NW * 64, 3) gqa_kernel(DecodeArgs a) {
     // counter per KV head: that of its first query head)
     const int bh0 = b * a.q_heads + kvh * G;
     if (!arrive_last(a, bh0, tid, &s_ticket)) return;
-    for (int n = w; n < G; n += NW) merge_row<D, TWO>(a, bh0 + n, lane);
+    for (int n = w; n < G; n += NWG) merge_row<D, TWO>(a, bh0 + n, lane);
     return;
   }
   // ---- a single split: finish here, one wave per head
-  for (int n = w; n < G; n += NW) {
+  for (int n = w; n < G; n += NWG) {
     const float Ln = head_l(n);
     const float A0 = accA(n, lane), A1 = v1ok ? accA(n, lane + 64) : 0.f;
     float R0 = accR(n, lane), R1 = v1ok ? accR(n, lane + 64) : 0.f;
@@ -827,9 +830,9 @@ template <int D, int B1, int B2>
 hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.splits, a.rows * a.g.kv_heads);
   if (a.paging.table)
-    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, true>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, true>), grid, dim3(NWG * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, false>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((gqa_kernel<D, B1, B2, false>), grid, dim3(NWG * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -843,7 +846,7 @@ hipError_t launch_gqa_d(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int gqa_tile_tokens() { return NW * TT; }
+int gqa_tile_tokens() { return NWG * TT; }
 
 bool gqa_supported(const Geometry& g, int loop, int group_ratio) {
   if (group_ratio < 2 || group_ratio > 16) return false;
