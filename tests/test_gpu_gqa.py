@@ -26,11 +26,15 @@ CASES = [
     (128, 2, 16, 1, 190),
     (64, 2, 8, 1, 100),
     (128, 2, 8, 2, 222),
+    # long enough for several splits per (row, KV head), so the partial states
+    # of more than 8 heads pass through the workspace and the final merge
+    (128, 1, 16, 0, 2100),
+    (128, 1, 12, 0, 1500),
 ]
 
 
 @pytest.mark.parametrize("d,kvh,hq,mode,n", CASES,
-                         ids=[f"d{c[0]}-g{c[2] // c[1]}-mode{c[3]}" for c in CASES])
+                         ids=[f"d{c[0]}-g{c[2] // c[1]}-mode{c[3]}-n{c[4]}" for c in CASES])
 def test_grouped_query_heads(d, kvh, hq, mode, n):
     w = Workload(f"gqa_d{d}_{kvh}x{hq // kvh}_m{mode}", batch=2, loops=4, layers=1, kv_heads=kvh,
                  q_heads=hq, head_dim=d, n_tokens=n, seed=d + hq + mode, mode=mode)
