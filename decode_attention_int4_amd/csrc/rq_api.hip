@@ -32,7 +32,10 @@ static constexpr int32_t kBf16Target = 512;
 static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
   if (n_tokens <= 0 || bh <= 0) return 1;
   const int32_t n_tiles = (n_tokens + tile - 1) / tile;
-  const int32_t splits = (target + bh - 1) / bh;
+  // rounded down: a grid of at most `target` workgroups runs in one round
+  // (rounding up put 550 workgroups on 512 slots for 110 rows, a second
+  // round for 38 of them)
+  const int32_t splits = target / bh > 1 ? target / bh : 1;
   const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
   return splits < max_splits ? splits : max_splits;
 }
