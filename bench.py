@@ -246,6 +246,87 @@ def capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
         b *= 2
 
 
+def variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
+    """Accuracy and cost of the method's variants on one workload's shapes.
+
+    For each variant (bit widths, alpha rule, rotation, chained anchor, and the
+    direct per-loop quantization it improves on) the same synthetic cache is
+    built and one JSON line reports: packed cache GB, algorithmic bytes per
+    step, ms/step and tokens/s of the graph-replayed step, the relative L2
+    error of the K and V reconstructions (first 128 tokens) against the BF16
+    originals, and the relative L2 error of the decode-attention outputs
+    against fp32 attention over the BF16 originals (every loop of three
+    sampled (batch, layer, head) slices).  A last line times the BF16 cache."""
+    base = WORKLOADS[args.config]
+    variants = [
+        ("INT4 anchor + INT2 residual, LS alpha, Hadamard", {}),
+        ("uniform INT4 (INT4 residual)", dict(residual_bits=4)),
+        ("uniform INT2 (INT2 anchor)", dict(anchor_bits=2)),
+        ("norm-ratio alpha", dict(alpha_mode=1)),
+        ("alpha = 1", dict(alpha_mode=2)),
+        ("rotation off", dict(rotation=0)),
+        ("chained previous-loop anchor", dict(mode=2)),
+        ("direct: INT4 anchor position, INT2 other loops", dict(mode=1)),
+        ("direct: INT4 every loop", dict(mode=1, residual_bits=4)),
+    ]
+    keep = [(0, 0, 0), (base.batch // 2, base.layers // 2, base.kv_heads // 2),
+            (base.batch - 1, base.layers - 1, base.kv_heads - 1)]
+    n_rec = min(128, base.n_tokens)
+
+    def rel(a, b):
+        return ((a - b).norm() / b.norm()).item()
+
+    for label, kw in variants:
+        torch.cuda.empty_cache()
+        w = base.with_(name=f"{base.name}_variant", **kw)
+        run = RQDecode(w, keep=keep)
+        run.step()
+        torch.cuda.synchronize()
+        att = []
+        for (b, layer, head) in keep:
+            kv = run.kept[(b, layer, head)].float().cuda()            # [2, loops, N, d]
+            for loop in range(w.loops):
+                q = run.q[loop, layer][b, head].float()
+                p = torch.softmax((kv[0, loop] @ q) * w.softmax_scale, dim=0)
+                att.append(rel(run.out[loop, layer, b, head], p @ kv[1, loop]))
+        rec = rq.reconstruct(run.desc, run.cache, run.signs, 0, n_rec, out_dtype=torch.bfloat16)
+        kerr, verr = [], []
+        for (b, layer, head) in keep:
+            orig = run.kept[(b, layer, head)][:, :, :n_rec].float().cuda()
+            got = rec[:, b, :, layer, head].float()
+            for loop in range(w.loops):
+                kerr.append(rel(got[0, loop], orig[0, loop]))
+                verr.append(rel(got[1, loop], orig[1, loop]))
+        del rec
+        g = graphed(run.step, torch)
+        for _ in range(args.warmup):
+            g.replay()
+        ms, _ = time_steps(g.replay, args.steps, torch)
+        rec_line = {"variant": label, "workload": base.name, "settings": kw,
+                    "cache_gb": round(rq.cache_bytes(run.desc) / 1e9, 2),
+                    "step_gb": round(run.step_bytes() / 1e9, 2),
+                    "ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+                    "k_rel_l2": round(sum(kerr) / len(kerr), 5), "v_rel_l2": round(sum(verr) / len(verr), 5),
+                    "attn_rel_l2_mean": round(sum(att) / len(att), 5), "attn_rel_l2_max": round(max(att), 5)}
+        print(json.dumps(rec_line), flush=True)
+        log(f"[variants] {label}: {rec_line['tokens_per_s']} tok/s, step {rec_line['step_gb']} GB, "
+            f"K/V rel-L2 {rec_line['k_rel_l2']:.4f}/{rec_line['v_rel_l2']:.4f}, "
+            f"attention rel-L2 {rec_line['attn_rel_l2_mean']:.4f} (max {rec_line['attn_rel_l2_max']:.4f})")
+        del g, run
+    torch.cuda.empty_cache()
+    run = BF16Decode(base)
+    run.step()
+    g = graphed(run.step, torch)
+    for _ in range(args.warmup):
+        g.replay()
+    ms, _ = time_steps(g.replay, args.steps, torch)
+    print(json.dumps({"variant": "BF16 cache", "workload": base.name,
+                      "cache_gb": round(2 * base.batch * base.loops * base.layers * base.kv_heads
+                                        * base.n_tokens * base.head_dim * 2 / 1e9, 2),
+                      "step_gb": round(run.step_bytes() / 1e9, 2), "ms_per_step": round(ms, 4),
+                      "tokens_per_s": round(base.batch / (ms * 1e-3), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +341,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="batch-capacity sweep (batch 1, 2, 4, ... while caches fit) instead of the "
                          "single benchmark line")
+    ap.add_argument("--variants", action="store_true",
+                    help="accuracy and cost of the method's variants on the configured shapes "
+                         "(one JSON line per variant) instead of the single benchmark line")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run a 1 GiB device copy and a 1 GiB read (known byte counts) "
                          "to calibrate FETCH_SIZE / WRITE_SIZE counters")
@@ -291,6 +375,9 @@ def main():
 
     if args.sweep:
         capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
+        return
+    if args.variants:
+        variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
         return
 
     w = WORKLOADS[args.config]
