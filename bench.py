@@ -246,17 +246,61 @@ def capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
         b *= 2
 
 
-def variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
-    """Accuracy and cost of the method's variants on one workload's shapes.
+def measure_variant(w, keep, args, torch, rq, RQDecode):
+    """Cache size, step bytes and throughput of one workload's packed cache, the
+    relative L2 error of its K and V reconstructions (first 128 tokens) against
+    the BF16 originals and of its decode-attention outputs against fp32
+    attention over the BF16 originals (every loop of the `keep` slices)."""
+    n_rec = min(128, w.n_tokens)
 
-    For each variant (bit widths, alpha rule, rotation, chained anchor, and the
-    direct per-loop quantization it improves on) the same synthetic cache is
-    built and one JSON line reports: packed cache GB, algorithmic bytes per
-    step, ms/step and tokens/s of the graph-replayed step, the relative L2
-    error of the K and V reconstructions (first 128 tokens) against the BF16
-    originals, and the relative L2 error of the decode-attention outputs
-    against fp32 attention over the BF16 originals (every loop of three
-    sampled (batch, layer, head) slices).  A last line times the BF16 cache."""
+    def rel(a, b):
+        return ((a - b).norm() / b.norm()).item()
+
+    torch.cuda.empty_cache()
+    run = RQDecode(w, keep=keep)
+    run.step()
+    torch.cuda.synchronize()
+    att = []
+    for (b, layer, head) in keep:
+        kv = run.kept[(b, layer, head)].float().cuda()            # [2, loops, N, d]
+        for loop in range(w.loops):
+            q = run.q[loop, layer][b, head].float()
+            p = torch.softmax((kv[0, loop] @ q) * w.softmax_scale, dim=0)
+            att.append(rel(run.out[loop, layer, b, head], p @ kv[1, loop]))
+    rec = rq.reconstruct(run.desc, run.cache, run.signs, 0, n_rec, out_dtype=torch.bfloat16)
+    kerr, verr = [], []
+    for (b, layer, head) in keep:
+        orig = run.kept[(b, layer, head)][:, :, :n_rec].float().cuda()
+        got = rec[:, b, :, layer, head].float()
+        for loop in range(w.loops):
+            kerr.append(rel(got[0, loop], orig[0, loop]))
+            verr.append(rel(got[1, loop], orig[1, loop]))
+    del rec
+    g = graphed(run.step, torch)
+    for _ in range(args.warmup):
+        g.replay()
+    ms, _ = time_steps(g.replay, args.steps, torch)
+    out = {"cache_gb": round(rq.cache_bytes(run.desc) / 1e9, 2), "step_gb": round(run.step_bytes() / 1e9, 2),
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+           "k_rel_l2": round(sum(kerr) / len(kerr), 5), "v_rel_l2": round(sum(verr) / len(verr), 5),
+           "attn_rel_l2_mean": round(sum(att) / len(att), 5), "attn_rel_l2_max": round(max(att), 5)}
+    del g, run
+    return out
+
+
+def study_keep(w):
+    return [(0, 0, 0), (w.batch // 2, w.layers // 2, w.kv_heads // 2),
+            (w.batch - 1, w.layers - 1, w.kv_heads - 1)]
+
+
+def variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
+    """Accuracy and cost of the method's variants on one workload's shapes:
+    bit widths, the alpha rule, the rotation, the chained anchor, and the
+    direct per-loop quantization the method improves on (one JSON line each,
+    see measure_variant), then loop groups of 4, 8 and 16 loops in residual
+    mode with the bytes a chained previous-loop anchor would read (computed:
+    the kernel reads at most three residual planes, groups of up to 4), and a
+    last line timing the BF16 cache."""
     base = WORKLOADS[args.config]
     variants = [
         ("INT4 anchor + INT2 residual, LS alpha, Hadamard", {}),
@@ -269,50 +313,31 @@ def variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
         ("direct: INT4 anchor position, INT2 other loops", dict(mode=1)),
         ("direct: INT4 every loop", dict(mode=1, residual_bits=4)),
     ]
-    keep = [(0, 0, 0), (base.batch // 2, base.layers // 2, base.kv_heads // 2),
-            (base.batch - 1, base.layers - 1, base.kv_heads - 1)]
-    n_rec = min(128, base.n_tokens)
-
-    def rel(a, b):
-        return ((a - b).norm() / b.norm()).item()
-
+    keep = study_keep(base)
     for label, kw in variants:
-        torch.cuda.empty_cache()
         w = base.with_(name=f"{base.name}_variant", **kw)
-        run = RQDecode(w, keep=keep)
-        run.step()
-        torch.cuda.synchronize()
-        att = []
-        for (b, layer, head) in keep:
-            kv = run.kept[(b, layer, head)].float().cuda()            # [2, loops, N, d]
-            for loop in range(w.loops):
-                q = run.q[loop, layer][b, head].float()
-                p = torch.softmax((kv[0, loop] @ q) * w.softmax_scale, dim=0)
-                att.append(rel(run.out[loop, layer, b, head], p @ kv[1, loop]))
-        rec = rq.reconstruct(run.desc, run.cache, run.signs, 0, n_rec, out_dtype=torch.bfloat16)
-        kerr, verr = [], []
-        for (b, layer, head) in keep:
-            orig = run.kept[(b, layer, head)][:, :, :n_rec].float().cuda()
-            got = rec[:, b, :, layer, head].float()
-            for loop in range(w.loops):
-                kerr.append(rel(got[0, loop], orig[0, loop]))
-                verr.append(rel(got[1, loop], orig[1, loop]))
-        del rec
-        g = graphed(run.step, torch)
-        for _ in range(args.warmup):
-            g.replay()
-        ms, _ = time_steps(g.replay, args.steps, torch)
-        rec_line = {"variant": label, "workload": base.name, "settings": kw,
-                    "cache_gb": round(rq.cache_bytes(run.desc) / 1e9, 2),
-                    "step_gb": round(run.step_bytes() / 1e9, 2),
-                    "ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
-                    "k_rel_l2": round(sum(kerr) / len(kerr), 5), "v_rel_l2": round(sum(verr) / len(verr), 5),
-                    "attn_rel_l2_mean": round(sum(att) / len(att), 5), "attn_rel_l2_max": round(max(att), 5)}
-        print(json.dumps(rec_line), flush=True)
-        log(f"[variants] {label}: {rec_line['tokens_per_s']} tok/s, step {rec_line['step_gb']} GB, "
-            f"K/V rel-L2 {rec_line['k_rel_l2']:.4f}/{rec_line['v_rel_l2']:.4f}, "
-            f"attention rel-L2 {rec_line['attn_rel_l2_mean']:.4f} (max {rec_line['attn_rel_l2_max']:.4f})")
-        del g, run
+        rec = {"variant": label, "workload": base.name, "settings": kw,
+               **measure_variant(w, keep, args, torch, rq, RQDecode)}
+        print(json.dumps(rec), flush=True)
+        log(f"[variants] {label}: {rec['tokens_per_s']} tok/s, step {rec['step_gb']} GB, "
+            f"K/V rel-L2 {rec['k_rel_l2']:.4f}/{rec['v_rel_l2']:.4f}, "
+            f"attention rel-L2 {rec['attn_rel_l2_mean']:.4f} (max {rec['attn_rel_l2_max']:.4f})")
+    # loop groups: P loops per group, noise ramp 0.3 .. 0.1 towards the anchor
+    d, ng = base.head_dim, base.head_dim // 16
+    for P in (4, 8, 16):
+        sig = tuple(round(0.1 + 0.2 * (P - 2 - j) / (P - 2), 4) for j in range(P - 1))
+        w = base.with_(name=f"{base.name}_group{P}", loops=P, loops_per_group=P, sigmas=sig)
+        anchor_b = d * w.anchor_bits // 8 + 2 * ng
+        resid_b = d * w.residual_bits // 8 + 2 * ng + 2
+        rows = 2 * w.batch * w.kv_heads * w.n_tokens * w.layers
+        chained = rows * sum(anchor_b + (P - 1 - j) * resid_b for j in range(P - 1)) + rows * anchor_b
+        rec = {"variant": f"loop group {P}", "workload": base.name, "settings": {"loops": P, "loops_per_group": P},
+               **measure_variant(w, study_keep(w), args, torch, rq, RQDecode),
+               "chained_step_gb_computed": round(chained / 1e9, 2)}
+        print(json.dumps(rec), flush=True)
+        log(f"[variants] loop group {P}: {rec['tokens_per_s']} tok/s, step {rec['step_gb']} GB "
+            f"(chained anchor would read {rec['chained_step_gb_computed']} GB), "
+            f"K/V rel-L2 {rec['k_rel_l2']:.4f}/{rec['v_rel_l2']:.4f}")
     torch.cuda.empty_cache()
     run = BF16Decode(base)
     run.step()
