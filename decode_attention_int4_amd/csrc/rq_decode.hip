@@ -11,7 +11,9 @@
 // the saved memory traffic).
 //
 // gfx950 mapping.
-//   grid (splits, batch * q_heads), 4 waves per workgroup.  A wave takes its
+//   grid (splits, batch * q_heads), NWK = 4 or 8 waves per workgroup (8 for
+//   d = 128 calls reading at most one residual plane from a contiguous cache:
+//   decode_waves).  A wave takes its
 //   tokens in PAIRS (t, t+1); LPP lanes share a pair and each owns one
 //   quantization group (16 head_dim elements) of both tokens, so a lane's
 //   accumulators cover just 16 elements.
@@ -37,7 +39,8 @@
 //   vector instructions.
 //   Each lane keeps its own online-softmax state; the running maximum is only
 //   raised when a logit exceeds it by 8 (log2 units), so the rescale of the
-//   accumulators is rare.  Lanes are merged with DPP row rotations and LDS.
+//   accumulators is rare.  A wave's token pairs are summed in registers (DPP
+//   and the gfx950 permlane swaps), its waves through LDS.
 //   With one split the workgroup's first wave applies H^T and writes the fp32
 //   output; otherwise each workgroup stores its partial state with
 //   write-through (device-scope) stores, waits for them to complete and takes

@@ -17,7 +17,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int NW = 4;              // waves per workgroup
 constexpr float kEmpty = -1e30f;   // running max of an empty stream (finite on purpose)
 constexpr float kLazy = 8.f;       // log2-domain headroom before the running max moves
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024, 1024)
