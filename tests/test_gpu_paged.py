@@ -6,8 +6,11 @@ the codes, FP8 bytes and alphas found at each token's block and in-block
 position must equal the oracle's encoding of that token bit for bit, and paged
 decode attention must match the fp64 oracle on each sequence's logical tokens
 (1e-3 relative L2, 2e-3 max-abs).  The same data in a contiguous cache, read
-by the ragged call, must give bit-identical outputs: the block table changes
-where the bytes live, not what the kernels compute."""
+by the ragged call, must give the same outputs up to fp32 summation order
+(relative L2 1e-6): the block table changes where the bytes live, not what
+is computed.  (At d = 128 the contiguous call runs eight-wave workgroups and
+the paged call four, with their own split plans, so the partial sums are
+added in a different order.)"""
 import numpy as np
 import pytest
 import torch
@@ -108,8 +111,9 @@ def test_paged_append_and_decode(d, bt, mode, fill, lengths):
                                             pool.table_dev, lens, max_n, w.softmax_scale, ws)
             ref_c = rq.decode_attention_ragged(run.desc, run.cache, run.signs, loop, layer, q,
                                                lens, max_n, w.softmax_scale, ws_c)
-            got, ref_c = got.cpu().numpy(), ref_c.cpu().numpy()
-            assert np.array_equal(got, ref_c), f"{w.name} loop {loop} layer {layer}: paged != contiguous"
+            got, ref_c = got.cpu().numpy().astype(np.float64), ref_c.cpu().numpy().astype(np.float64)
+            diff = np.linalg.norm(got - ref_c) / max(np.linalg.norm(ref_c), 1e-30)
+            assert diff <= 1e-6, f"{w.name} loop {loop} layer {layer}: paged vs contiguous rel-L2 {diff:.2e}"
             for (s, lay, head) in keep:
                 if lay != layer:
                     continue
