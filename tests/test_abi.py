@@ -219,6 +219,22 @@ def test_workspace_bound_is_monotone():
                 prev = w
 
 
+def test_workspace_holds_one_round_of_splits():
+    """The split planner rounds the number of splits per (row, head) down, so
+    a grid of at most 512 four-wave workgroups runs in one round: 110 rows
+    take 4 splits (440 workgroups), not 5.  The workspace is the 256 KiB
+    counter block plus one partial state (m, l, accA[d], accR[d]) per row,
+    head and split."""
+    counters = (1 << 16) * 4
+    huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs
+    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 4 * (2 + 2 * 96) * 4
+    ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs: 8 splits
+    assert rq.decode_workspace_bytes(ouro, 16, 8192) == counters + 64 * 8 * (2 + 2 * 128) * 4
+    # short contexts: at most half the 64-token tiles, and no workspace for one split
+    assert rq.decode_workspace_bytes(ouro, 16, 256) == counters + 64 * 2 * (2 + 2 * 128) * 4
+    assert rq.decode_workspace_bytes(ouro, 16, 127) == 0
+
+
 def test_status_strings():
     for s in range(7):
         assert rq._status_string(s)
