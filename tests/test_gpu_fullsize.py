@@ -42,10 +42,13 @@ def _run_case(name, keep, loops=None, w=None):
         futs = {loop: POOL.submit(oracle_attention, w, ek, ev, HK, HV,
                                   bits16(run.q[loop, layer, b, head]), loop, run.N)
                 for loop in loops}
+        worst_rel = worst_mx = 0.0
         for loop, f in futs.items():
             rel, mx = assert_close_attention(out[loop, layer, b, head], f.result(),
                                              f"{name} slice {key} loop {loop}")
-        say(f"[fullsize] {name}: slice {key} ok (last rel-L2 {rel:.2e}, max-abs {mx:.2e})")
+            worst_rel, worst_mx = max(worst_rel, rel), max(worst_mx, mx)
+        say(f"[fullsize] {name}: slice {key} ok (worst rel-L2 {worst_rel:.2e}, max-abs {worst_mx:.2e} "
+            f"over {len(futs)} loops)")
     del run
     gc.collect()
     torch.cuda.empty_cache()
