@@ -19,9 +19,8 @@ int bf16_tile_tokens();
 // for every decode kernel: with the splits merged inside the kernel, fewer
 // and longer splits measured faster than filling all workgroup slots (768
 // or 1024); the BF16 baseline also targets 512.  Splits never shrink below
-// two tiles, and a row takes at most kSplitSlots of them.  The result is
-// non-decreasing in n_tokens, so a workspace sized for n serves any smaller
-// n.
+// two tiles.  The result is non-decreasing in n_tokens, so a workspace sized
+// for n serves any smaller n.
 static constexpr int32_t kDecodeTargetTwo = 512;
 static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
@@ -36,8 +35,7 @@ static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int3
   // rounded down: a grid of at most `target` workgroups runs in one round
   // (rounding up put 550 workgroups on 512 slots for 110 rows, a second
   // round for 38 of them)
-  int32_t splits = target / bh > 1 ? target / bh : 1;
-  if (splits > kSplitSlots) splits = kSplitSlots;
+  const int32_t splits = target / bh > 1 ? target / bh : 1;
   const int32_t max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
   return splits < max_splits ? splits : max_splits;
 }
@@ -249,13 +247,11 @@ rq_status rq_reconstruct(const rq_cache_desc* desc, const void* cache, const int
                                                                                     : RQ_ERR_LAUNCH;
 }
 
-// The workspace starts with a fixed block of split-arrival counters and one
-// of epoch words, one each per (row, query head), so that calls of any shape
-// find them at the same place; the partial states follow, kSplitSlots slots
-// of (2 + 2d) 64-bit words per (row, query head), split s of row r in slot
-// r * kSplitSlots + s whatever the call's split count.
+// The workspace starts with a fixed block of split-arrival counters, one per
+// (row, query head), so that calls of any shape find them at the same place
+// and never overlap another call's partial states; the partial states follow.
 static constexpr int32_t kMaxRowHeads = 1 << 16;  // also the grid's y extent
-static constexpr uint64_t kHeaderBytes = (uint64_t)kMaxRowHeads * 8u;
+static constexpr uint64_t kCounterBytes = (uint64_t)kMaxRowHeads * 4u;
 
 // Whether a call runs the grouped-query kernel (one workgroup per KV head);
 // its split plan then counts (batch row, KV head) rows.
@@ -279,7 +275,7 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
                                             rq::gqa_tile_tokens(), rq::kGqaTarget);
     s = sg > s ? sg : s;
   }
-  return s > 1 ? kHeaderBytes + (uint64_t)bh * rq::kSplitSlots * (2 + 2 * desc->head_dim) * 8ull : 0;
+  return s > 1 ? kCounterBytes + (uint64_t)bh * s * (2 + 2 * desc->head_dim) * 4ull : 0;
 }
 
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, int32_t max_n_tokens) {
@@ -289,32 +285,6 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads, i
 uint64_t rq_paged_decode_workspace_bytes(const rq_cache_desc* pool, int32_t q_heads, int32_t n_seqs,
                                          int32_t max_n_tokens) {
   return workspace_for(pool, n_seqs, q_heads, max_n_tokens);
-}
-
-// The split plan of one decode call and the per-head kernel's waves per
-// workgroup (the grouped kernel's plan counts (row, KV head) pairs).
-static rq::SplitPlan decode_plan(const rq_cache_desc* desc, int32_t rows, int32_t loop,
-                                 int32_t q_heads, int32_t n_tokens, bool paged, int* waves) {
-  const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
-  const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
-  const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
-  *waves = rq::decode_waves(desc->head_dim, chain, paged);
-  const int32_t target = *waves == 8 ? rq::kDecodeTargetWide
-                         : chain     ? rq::kDecodeTargetChain
-                         : two       ? rq::kDecodeTargetTwo
-                                     : rq::kDecodeTargetOne;
-  if (grouped(desc, loop, q_heads))
-    return rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget);
-  return rq::plan_splits(rows * q_heads, n_tokens, rq::decode_tile_tokens(desc->head_dim, *waves),
-                         target);
-}
-
-int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads, int32_t n_tokens) {
-  if (check_desc(desc) != RQ_OK || loop < 0 || loop >= desc->loops || q_heads <= 0 ||
-      q_heads % desc->kv_heads != 0 || n_tokens < 0)
-    return 0;
-  int waves = 4;
-  return decode_plan(desc, desc->batch, loop, q_heads, n_tokens, false, &waves).splits;
 }
 
 static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* cache,
@@ -340,8 +310,19 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
     return RQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
-  int waves = 4;
-  const rq::SplitPlan plan = decode_plan(desc, rows, loop, q_heads, n_tokens, pg.table != nullptr, &waves);
+  const int32_t bh = rows * q_heads;
+  const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
+  const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
+  const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
+  const int waves = rq::decode_waves(desc->head_dim, chain, pg.table != nullptr);
+  const int32_t target = waves == 8 ? rq::kDecodeTargetWide
+                         : chain    ? rq::kDecodeTargetChain
+                         : two      ? rq::kDecodeTargetTwo
+                                    : rq::kDecodeTargetOne;
+  const rq::SplitPlan plan =
+      grouped(desc, loop, q_heads)
+          ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget)
+          : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim, waves), target);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);
@@ -349,8 +330,7 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   a.q = q_bf16;
   a.out = out;
   a.counters = static_cast<uint32_t*>(workspace);
-  a.epochs = a.counters + kMaxRowHeads;
-  a.partials = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + kHeaderBytes);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kCounterBytes);
   a.lengths = lengths;
   a.rows = rows;
   a.paging = pg;

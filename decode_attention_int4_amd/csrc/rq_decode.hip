@@ -43,13 +43,11 @@
 //   and the gfx950 permlane swaps), its waves through LDS.
 //   With one split the workgroup's first wave applies H^T and writes the fp32
 //   output; otherwise each workgroup stores its partial state with
-//   write-through (device-scope) stores of (value, tag) words and, without
-//   waiting for them to land, takes a ticket from the row's counter; the
-//   workgroup holding the last ticket reads all partial states with
-//   device-scope loads, re-reading any word whose tag is older than the
-//   call's, and merges them.  No cache write-back or invalidation is needed
-//   (a release fence per workgroup, an L2 write-back, cost far more than a
-//   separate merge kernel), and no workgroup waits for its own stores.
+//   write-through (device-scope) stores, waits for them to complete and takes
+//   a ticket from the row's counter, and the workgroup holding the last
+//   ticket reads all partial states with device-scope loads and merges them.
+//   No cache write-back or invalidation is needed (a release fence per
+//   workgroup, an L2 write-back, cost far more than a separate merge kernel).
 #include <hip/hip_runtime.h>
 
 #include "rq_device.h"
@@ -340,10 +338,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   // reads of the eight groups' rows fall in eight different bank quads
   __shared__ __attribute__((aligned(16))) uint32_t spre[8][36];
   __shared__ float sm_m[NWK];
+  __shared__ uint32_t s_ticket;
   // the query row (BF16) and this layer's key signs, staged by DMA
   __shared__ __attribute__((aligned(16))) uint8_t s_in[512];
-  // this row's epoch word (split calls), staged by DMA on all 64 lanes
-  __shared__ __attribute__((aligned(16))) uint32_t s_epoch[64];
   typedef float AccRow[kRow];
   AccRow* sm_acc = reinterpret_cast<AccRow*>(smem);               // [wave][accA | accR | l]
 
@@ -438,17 +435,14 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
-  // Wave 0 stages the query row, the key signs and the row's epoch word by
-  // DMA ahead of its tiles: a plain load issued after the tiles' DMAs would
-  // wait for all of them
+  // Wave 0 stages the query row and the key signs by DMA ahead of its tiles:
+  // a plain load issued after the tiles' DMAs would wait for all of them
   if (w == 0) {
     dma1<4>(make_rsrc((const uint8_t*)(a.q + (uint64_t)bh * D), 2 * D), (lds_u8*)s_in,
             min(4 * lane, 2 * D - 4), 0u);
     if (rotated)
       dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), (lds_u8*)s_in + 256,
               min(4 * lane, D - 4), 0u);
-    if (a.splits > 1)
-      dma1<4>(make_rsrc((const uint8_t*)(a.epochs + bh), 4), (lds_u8*)s_epoch, 0, 0u);
   }
 #pragma unroll
   for (int i = 0; i < kPre; ++i)
@@ -750,26 +744,19 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     return s;
   };
   if (a.splits > 1) {
-    // partial state (m, l, accA[D], accR[D]) of this split, in words tagged
-    // with the row's epoch plus one; nothing waits for the stores to land:
-    // the workgroup that draws the row's last ticket (first wave) re-reads
-    // any word whose tag is still older
-    const uint32_t tag = s_epoch[0] + 1u;
-    uint64_t* mine = a.partials + ((uint64_t)bh * kSplitSlots + split) * (2 + 2 * D);
+    // partial state (m, l, accA[D], accR[D]) of this split; the workgroup
+    // that finishes the row last merges all of them
+    float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + 2 * D);
     for (int i = tid; i <= 2 * D; i += NWK * 64) {
       if (i == 2 * D) {
-        store_tagged(mine, M, tag);
-        store_tagged(mine + 1, merged(kRow - 1), tag);
+        store_dev(mine, M);
+        store_dev(mine + 1, merged(kRow - 1));
       } else {
-        store_tagged(mine + 2 + i, (TWO || i < D) ? merged(i) : 0.f, tag);
+        store_dev(mine + 2 + i, (TWO || i < D) ? merged(i) : 0.f);
       }
     }
-    if (w != 0 || !wave_last(a, bh, lane)) return;
-    const bool v1ok = (D > 64) && (lane + 64 < D);
-    const OwnPart own{split, M, merged(kRow - 1), merged(lane), v1ok ? merged(lane + 64) : 0.f,
-                      TWO ? merged(D + lane) : 0.f, TWO && v1ok ? merged(D + lane + 64) : 0.f};
-    merge_row<D, TWO>(a, bh, lane, tag, own);
-    if (lane == 0) close_row(a, bh);
+    if (!arrive_last(a, bh, tid, &s_ticket) || w != 0) return;
+    merge_row<D, TWO>(a, bh, lane);
     return;
   }
   // ---- a single split: finish here (first wave, two elements per lane)

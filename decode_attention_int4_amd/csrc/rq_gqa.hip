@@ -386,8 +386,6 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   __shared__ float spq[16], spu[16];             // per-head prescales
   __shared__ float sm_m[NWG][16], sm_l[NWG][16];
   __shared__ uint32_t s_ticket;
-  // the epoch words of the G heads' rows (split calls), staged by DMA
-  __shared__ __attribute__((aligned(16))) uint32_t s_epoch[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -459,10 +457,10 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
-  // ---- the query rows of this wave's heads (w, w + NWG, ... below G), the
-  // key signs and the heads' epoch words come in by DMA ahead of the first
-  // tile: a plain load issued after the tile's DMAs would wait for all of
-  // them.  (Issuing the second tile here as well measured slower.)
+  // ---- the query rows of this wave's heads (w, w + 4, ... below G) and the
+  // key signs come in by DMA ahead of the first tile: a plain load issued
+  // after the tile's DMAs would wait for all of them.  (Issuing the second
+  // tile here as well measured slower.)
   lds_u8* stage = (lds_u8*)qop;
   for (int n = w; n < G; n += NWG) {
     const uint16_t* qrow = a.q + ((uint64_t)b * a.q_heads + kvh * G + n) * D;
@@ -471,9 +469,6 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   if (rotated && w == 0)
     dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), stage + 16 * 256,
             min(4 * lane, D - 4), 0u);
-  if (a.splits > 1 && w == 1)   // lane n < G: the epoch of query head kvh * G + n
-    dma1<4>(make_rsrc((const uint8_t*)(a.epochs + (uint64_t)b * a.q_heads + kvh * G), 4 * G),
-            (lds_u8*)s_epoch, min(4 * lane, 4 * G - 4), 0u);
   if (n_tiles > 0) issue(0);
   if (n_tiles > 0) wait_vm<GS::N_DMA>();
   else wait_vm<0>();
@@ -793,30 +788,24 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
 
   if (a.splits > 1) {
     // partial state (m, l, accA[D], accR[D]) of every head, as the per-head
-    // kernel writes it: words tagged with the head's epoch plus one, not
-    // waited for
+    // kernel writes it
     constexpr int Wd = 2 + 2 * D;
     for (int i = tid; i < G * Wd; i += NWG * 64) {
       const int n = i / Wd, k = i % Wd;
       const int bh = b * a.q_heads + kvh * G + n;
-      uint64_t* mine = a.partials + ((uint64_t)bh * kSplitSlots + split) * Wd;
+      float* mine = a.partials + ((uint64_t)bh * a.splits + split) * Wd;
       float v;
       if (k == 0) v = head_m(n);
       else if (k == 1) v = head_l(n);
       else if (k < 2 + D) v = accA(n, k - 2);
       else v = accR(n, k - 2 - D);
-      store_tagged(mine + k, v, s_epoch[n] + 1u);
+      store_dev(mine + k, v);
     }
-    // the workgroup that draws the KV head's last ticket merges its G rows
-    // (one counter per KV head: that of its first query head)
+    // the workgroup that finishes the KV head last merges its G rows (one
+    // counter per KV head: that of its first query head)
     const int bh0 = b * a.q_heads + kvh * G;
-    if (!group_last(a, bh0, tid, &s_ticket)) return;
-    for (int n = w; n < G; n += NWG) {
-      const OwnPart own{split, head_m(n), head_l(n), accA(n, lane), v1ok ? accA(n, lane + 64) : 0.f,
-                        accR(n, lane), v1ok ? accR(n, lane + 64) : 0.f};
-      merge_row<D, TWO>(a, bh0 + n, lane, s_epoch[n] + 1u, own);
-    }
-    if (tid == 0) close_row(a, bh0);
+    if (!arrive_last(a, bh0, tid, &s_ticket)) return;
+    for (int n = w; n < G; n += NWG) merge_row<D, TWO>(a, bh0 + n, lane);
     return;
   }
   // ---- a single split: finish here, one wave per head

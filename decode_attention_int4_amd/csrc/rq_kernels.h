@@ -43,24 +43,15 @@ hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 
 // Split-K decode: with more than one split, partial states live in the
 // workspace, and the workgroup that finishes a row last (by a ticket counter
-// per row, also in the workspace) merges them.  A partial state is a run of
-// 64-bit words, each an fp32 value (low half) and the call's tag (high half):
-// the tag is the row's epoch word plus one, read when the workgroups start
-// and advanced by the merging workgroup, so the merger can tell a word this
-// call has written from an older one without waiting for the writers' stores
-// to complete.  Row r's split s always sits at slot r * kSplitSlots + s,
-// whatever the call's shape, so a slot is only ever written for its own row
-// and an older word there carries an older epoch of that row.
-constexpr int kSplitSlots = 32;   // most splits per row
+// per row, also in the workspace) merges them.
 struct DecodeArgs {
   Geometry g;
   const uint8_t* cache;
   const int8_t* signs;
   const uint16_t* q;      // [B][Hq][d]
   float* out;             // [B][Hq][d]
-  uint64_t* partials;     // [B*Hq][kSplitSlots][2 + 2d] (value, tag) words
+  float* partials;        // [B*Hq][splits][2 + 2d]
   uint32_t* counters;     // [B*Hq] split arrivals, zero between calls
-  uint32_t* epochs;       // [B*Hq] calls merged so far per row
   const int32_t* lengths;  // [rows] tokens per row (clamped to n_tokens), or null
   int32_t rows;           // query rows (the descriptor's batch unless paged)
   Paging paging;

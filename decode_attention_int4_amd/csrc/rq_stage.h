@@ -211,108 +211,62 @@ __device__ __forceinline__ float fp16_prescale(float maxabs) {
 
 
 // ------------------------------------------------------------ split-K merge
-// Partial states pass between workgroups, possibly on different XCDs, as
-// 64-bit words (fp32 value, call tag) stored and loaded with device-wide
-// (agent scope) relaxed atomics: stores write through to the memory level
-// all XCDs share and loads read from it, with no cache write-backs or
-// invalidations.  An aligned 64-bit atomic is read and written whole, so a
-// word that carries this call's tag carries this call's value.
-__device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// Device-wide (agent scope) relaxed accesses.  Stores write through to the
+// memory level that all XCDs share and loads read from it (global_store and
+// global_load with sc1), so partial states pass between workgroups on
+// different XCDs without cache write-backs or invalidations.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float value_of(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Rounds of re-reads before the merge gives up on a row (its output is then
-// NaN).  Every workgroup issues its partial-state stores before it takes its
-// ticket, so the merging workgroup only ever waits for stores already on
-// their way; the bound is a guard, not a timeout anything relies on.
-constexpr int kMaxPolls = 1 << 16;
-
-// Ticket of a workgroup whose partial states are issued (not necessarily
-// landed): counter `ctr` counts the arrivals of one row and the workgroup
-// that draws the last ticket merges.  wave_last: one wave draws, and the
-// answer is that wave's; group_last: every thread calls, and `ticket` is a
-// word of LDS.  The merger resets the counter (close_row) for the next call.
-__device__ __forceinline__ bool wave_last(const DecodeArgs& a, int ctr, int lane) {
-  uint32_t t = 0;
-  if (lane == 0)
-    t = __hip_atomic_fetch_add(a.counters + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_amdgcn_readfirstlane(t) == (uint32_t)a.splits - 1u;
-}
-__device__ __forceinline__ bool group_last(const DecodeArgs& a, int ctr, int tid, uint32_t* ticket) {
+// Called by every thread of a workgroup once its partial states are stored
+// with store_dev.  Each wave first waits until its own stores have completed,
+// then one thread takes a ticket from counter `ctr`; the workgroup that
+// arrives last sees every other partial already written, resets the counter
+// to zero for the next call and returns true.  `ticket` is a word of LDS.
+__device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int ctr, int tid, uint32_t* ticket) {
+  wait_vm<0>();
+  __syncthreads();
   if (tid == 0)
     *ticket = __hip_atomic_fetch_add(a.counters + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  return *ticket == (uint32_t)a.splits - 1u;
+  const bool last = *ticket == (uint32_t)a.splits - 1u;
+  if (last && tid == 0) __hip_atomic_store(a.counters + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
 }
-__device__ __forceinline__ void close_row(const DecodeArgs& a, int ctr) {
-  __hip_atomic_store(a.counters + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The merging workgroup's own partial state as one lane holds it (elements
-// lane and lane + 64 of each sum): the merge takes it from there instead of
-// re-reading it, so the merger never waits for its own stores.
-struct OwnPart {
-  int split;
-  float m, l, a0, a1, r0, r1;
-};
 
 // Merges the split partial states (m, l, accA[D], accR[D]) of one (batch row,
-// query head), applies H^T to the residual sum, writes the fp32 output and
-// advances the row's epoch to `tag`; one wave, two elements per lane.
-// Splits are merged online, four per round: a round's loads issue
-// together, and the round is read again (after a short sleep) while any of
-// its words still carries an older tag.
+// query head), applies H^T to the residual sum and writes the fp32 output;
+// one wave, two elements per lane.  Splits are merged online, sixteen per
+// round, so each round's loads issue together and the merge waits on memory
+// about once per sixteen splits.
 template <int D, bool TWO>
-__device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane, uint32_t tag,
-                                          const OwnPart& own) {
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane) {
   constexpr int W = 2 + 2 * D;
   const int ns = a.splits;
   const bool v1ok = (D > 64) && (lane + 64 < D);
-  const uint64_t* all = a.partials + (uint64_t)bh * kSplitSlots * W;
-  const uint64_t none = (uint64_t)tag << 32;   // a word not read: 0 with this call's tag
-  // the merger's own values as words of this call
-  auto word = [&](float v) { return none | __float_as_uint(v); };
+  const float* all = a.partials + (uint64_t)bh * ns * W;
   float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
-  bool lost = false;
-  constexpr int R = 4;  // splits per round
+  constexpr int R = 16;  // splits per round
   for (int s0 = 0; s0 < ns; s0 += R) {
-    uint64_t wm[R], wl[R], wa0[R], wa1[R], wr0[R], wr1[R];
-    for (int n = 0;; ++n) {
+    float ms[R], ls[R], a0[R], a1[R], r0[R], r1[R];
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        // the merger's own split comes from its registers, in its place in
-        // the split order (so the sums do not depend on which workgroup
-        // merges); nothing past the last split is read
-        const bool mine = s0 + j == own.split, rd = s0 + j < ns && !mine;
-        const uint64_t* ps = all + (uint64_t)(s0 + j) * W;
-        wm[j] = rd ? load_tagged(ps) : mine ? word(own.m) : none;
-        wl[j] = rd ? load_tagged(ps + 1) : mine ? word(own.l) : none;
-        wa0[j] = rd ? load_tagged(ps + 2 + lane) : mine ? word(own.a0) : none;
-        wa1[j] = rd && v1ok ? load_tagged(ps + 2 + lane + 64) : mine ? word(own.a1) : none;
-        wr0[j] = rd && TWO ? load_tagged(ps + 2 + D + lane) : mine ? word(own.r0) : none;
-        wr1[j] = rd && TWO && v1ok ? load_tagged(ps + 2 + D + lane + 64) : mine ? word(own.r1) : none;
-      }
-      uint32_t stale = 0;
-#pragma unroll
-      for (int j = 0; j < R; ++j)
-        stale |= ((uint32_t)(wm[j] >> 32) ^ tag) | ((uint32_t)(wl[j] >> 32) ^ tag) |
-                 ((uint32_t)(wa0[j] >> 32) ^ tag) | ((uint32_t)(wa1[j] >> 32) ^ tag) |
-                 ((uint32_t)(wr0[j] >> 32) ^ tag) | ((uint32_t)(wr1[j] >> 32) ^ tag);
-      if (__builtin_amdgcn_ballot_w64(stale != 0) == 0) break;
-      if (n == kMaxPolls) {
-        lost = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+    for (int j = 0; j < R; ++j) {
+      const int sj = min(s0 + j, ns - 1);
+      const float* ps = all + (uint64_t)sj * W;
+      ms[j] = (s0 + j < ns) ? load_dev(ps) : kEmpty;
+      ls[j] = load_dev(ps + 1);
+      a0[j] = load_dev(ps + 2 + lane);
+      a1[j] = v1ok ? load_dev(ps + 2 + lane + 64) : 0.f;
+      r0[j] = TWO ? load_dev(ps + 2 + D + lane) : 0.f;
+      r1[j] = (TWO && v1ok) ? load_dev(ps + 2 + D + lane + 64) : 0.f;
     }
     float Mn = M;
 #pragma unroll
-    for (int j = 0; j < R; ++j) Mn = fmaxf(Mn, s0 + j < ns ? value_of(wm[j]) : kEmpty);
+    for (int j = 0; j < R; ++j) Mn = fmaxf(Mn, ms[j]);
     const float c = exp2f(M - Mn);
     L *= c;
     A0 *= c;
@@ -321,23 +275,22 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane,
     R1 *= c;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const float f = s0 + j < ns ? exp2f(value_of(wm[j]) - Mn) : 0.f;
-      L = fmaf(f, value_of(wl[j]), L);
-      A0 = fmaf(f, value_of(wa0[j]), A0);
-      A1 = fmaf(f, value_of(wa1[j]), A1);
-      R0 = fmaf(f, value_of(wr0[j]), R0);
-      R1 = fmaf(f, value_of(wr1[j]), R1);
+      const float f = exp2f(ms[j] - Mn);
+      L = fmaf(f, ls[j], L);
+      A0 = fmaf(f, a0[j], A0);
+      A1 = fmaf(f, a1[j], A1);
+      R0 = fmaf(f, r0[j], R0);
+      R1 = fmaf(f, r1[j], R1);
     }
     M = Mn;
   }
-  if (lane == 0) __hip_atomic_store(a.epochs + bh, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (TWO && a.g.rotation == RQ_ROT_HADAMARD) {
     wave_wht<D>(R0, R1, lane);
     const int8_t* sg = a.signs + ((uint64_t)a.g.layers + a.layer) * D;  // V signs
     R0 *= ((D == 128) ? 0.08838834764831845f : 0.125f) * (float)sg[lane];
     if (v1ok) R1 *= ((D == 128) ? 0.08838834764831845f : 0.17677669529663687f) * (float)sg[lane + 64];
   }
-  const float inv = lost ? __builtin_nanf("") : L > 0.f ? 1.f / L : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   a.out[(uint64_t)bh * D + lane] = (A0 + R0) * inv;
   if (v1ok) a.out[(uint64_t)bh * D + lane + 64] = (A1 + R1) * inv;
 }

@@ -186,19 +186,9 @@ rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache,
 /* Bytes of workspace rq_decode_attention needs for `q_heads` query heads and
  * any n_tokens <= max_n_tokens (0 when no call of that size splits the
  * tokens).  The workspace starts with a fixed block of 65536 split counters
- * and 65536 epoch words (512 KiB), followed by 32 partial-state slots of
- * (2 + 2 d) 64-bit words per (batch row, query head); see
- * rq_decode_attention. */
+ * followed by the split partial states; see rq_decode_attention. */
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
                                    int32_t max_n_tokens);
-
-/* Number of token splits rq_decode_attention plans for loop `loop`,
- * `q_heads` query heads and n_tokens tokens of every batch row (host only;
- * 0 for invalid arguments).  Splits are counted per (batch row, query head),
- * or per (batch row, KV head) for grouped query heads served on matrix
- * cores; at most 32, and 1 means no workspace is used. */
-int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads,
-                         int32_t n_tokens);
 
 /*
  * Fused decode attention over the packed cache (abstract: reduced KV memory
@@ -211,18 +201,15 @@ int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_head
  * term.  Query head h reads kv head h / (q_heads / kv_heads).
  *   q_bf16     device BF16 [batch][q_heads][d], contiguous, 4-byte aligned
  *   workspace  device, >= rq_decode_workspace_bytes(desc, q_heads, n_tokens),
- *              256-byte aligned (may be NULL when that size is 0).  Holds, in
- *              its first 512 KiB, one arrival counter and one epoch word per
- *              (batch row, query head), then the split-K partial states as
- *              (value, tag) words: the workgroup that finishes a row last
- *              merges the row's partial states, recognising this call's
- *              words by the tag (the row's epoch plus one).  The WHOLE
- *              workspace must be ZERO before it is first used (fill it with
- *              zeros once, and again only as a whole); every call returns
- *              the counters it used to zero and advances the epochs of the
- *              rows it split, so the workspace then serves any sequence of
- *              calls of any shape.  Calls that share a workspace must be
- *              ordered (same stream), not concurrent.
+ *              256-byte aligned (may be NULL when that size is 0).  Holds the
+ *              split-K partial states and, in its first 256 KiB, one arrival
+ *              counter per (batch row, query head): the workgroup that
+ *              finishes a row last merges the row's partial states.  Those
+ *              counters must be ZERO before a workspace is first used (fill
+ *              it with zeros once); every call returns the counters it used
+ *              to zero, so the workspace then serves any sequence of calls of
+ *              any shape.  Calls that share a workspace must be ordered (same
+ *              stream), not concurrent.
  *   out        device fp32 [batch][q_heads][d]; n_tokens == 0 writes zeros.
  * Errors: RQ_ERR_UNSUPPORTED when q_heads is not a multiple of kv_heads or
  * batch * q_heads exceeds 65536;

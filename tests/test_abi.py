@@ -219,39 +219,19 @@ def test_workspace_bound_is_monotone():
                 prev = w
 
 
-def test_split_plan_fits_one_round():
+def test_workspace_holds_one_round_of_splits():
     """The split planner rounds the number of splits per (row, head) down, so
     a grid of at most 512 four-wave workgroups runs in one round: 110 rows
-    take 4 splits (440 workgroups), not 5.  Eight-wave calls (d = 128, one
-    residual plane, contiguous cache) aim at 256 workgroups, grouped-query
-    calls count (row, KV head) pairs, and no row takes more than 32 splits
-    or splits shorter than two tiles."""
+    take 4 splits (440 workgroups), not 5.  The workspace is the 256 KiB
+    counter block plus one partial state (m, l, accA[d], accR[d]) per row,
+    head and split."""
+    counters = (1 << 16) * 4
     huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs
-    assert rq.decode_splits(huginn, 0, 55, 8192) == 4
-    ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs, eight waves
-    assert rq.decode_splits(ouro, 0, 16, 8192) == 4
-    assert rq.decode_splits(ouro, 3, 16, 8192) == 4       # the anchor loop
-    assert rq.decode_splits(ouro, 0, 16, 256) == 1        # two 128-token tiles: one split
-    assert rq.decode_splits(ouro, 0, 16, 0) == 1
-    gqa = rq.make_desc(16, 4, 1, 4, 8192, 128)             # 64 (row, KV head) pairs, 4 heads each
-    assert rq.decode_splits(gqa, 0, 16, 8192) == 4
-    one = rq.make_desc(1, 4, 1, 1, 1 << 20, 128)           # one pair: capped at 32
-    assert rq.decode_splits(one, 0, 1, 1 << 20) == 32
-    assert rq.decode_splits(ouro, 4, 16, 8192) == 0       # no such loop
-    assert rq.decode_splits(ouro, 0, 12, 8192) == 0       # 12 query heads on 16 KV heads
-
-
-def test_workspace_layout():
-    """The workspace is a 512 KiB block of arrival counters and epoch words,
-    then 32 partial-state slots of (m, l, accA[d], accR[d]) as 64-bit
-    (value, tag) words per (row, head), whatever the split count; no
-    workspace when no call of that size splits."""
-    header = (1 << 16) * 8
-    huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)
-    assert rq.decode_workspace_bytes(huginn, 55, 8192) == header + 110 * 32 * (2 + 2 * 96) * 8
-    ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)
-    assert rq.decode_workspace_bytes(ouro, 16, 8192) == header + 64 * 32 * (2 + 2 * 128) * 8
-    assert rq.decode_workspace_bytes(ouro, 16, 256) == header + 64 * 32 * (2 + 2 * 128) * 8
+    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 4 * (2 + 2 * 96) * 4
+    ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs: 8 splits
+    assert rq.decode_workspace_bytes(ouro, 16, 8192) == counters + 64 * 8 * (2 + 2 * 128) * 4
+    # short contexts: at most half the 64-token tiles, and no workspace for one split
+    assert rq.decode_workspace_bytes(ouro, 16, 256) == counters + 64 * 2 * (2 + 2 * 128) * 4
     assert rq.decode_workspace_bytes(ouro, 16, 127) == 0
 
 

@@ -94,21 +94,21 @@ def test_tiny_step_and_append(tiny):
 
 
 def test_workspace_zeroed_once_serves_calls_of_any_shape():
-    """The workspace is zeroed once.  Calls of different shapes then share it:
-    several split counts, per-head and grouped-query kernels, ragged rows, so
-    each row's partial-state slots are rewritten under several call shapes;
-    every result matches the oracle, every counter is back to zero afterwards
-    and the split calls have advanced their rows' epoch words.  Repeated
-    alternating calls give bit-identical outputs each time, so no merge takes
-    a partial state left by an earlier call for this call's."""
+    """The workspace's counter block is zeroed once; its partial-state area may
+    hold anything (NaN here).  Calls of different shapes then share it: several
+    split counts, per-head and grouped-query kernels, ragged rows; every
+    result matches the oracle and every counter is back to zero afterwards.
+    Repeated alternating calls give bit-identical outputs each time, so no
+    merge reads a partial state left by an earlier call."""
     w = Workload("ws_share", batch=2, loops=4, layers=1, kv_heads=2, q_heads=4, head_dim=128,
                  n_tokens=4000, seed=5)
     keep = [(1, 0, 1)]
     run = RQDecode(w, keep=keep)
     need = max(rq.decode_workspace_bytes(run.desc, hq, run.N) for hq in (2, 4))
-    counter_bytes, header_bytes = 1 << 18, 1 << 19     # counters, then epoch words
-    assert need > header_bytes
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    counter_bytes = 1 << 18
+    assert need > counter_bytes
+    ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
+    ws[:counter_bytes].zero_()
     out = torch.full((2, 4, 128), float("nan"), device="cuda")
     ek, ev, HK, HV = encode_kept(w, run.kept[keep[0]], 0)
     lengths = torch.tensor([3000, 4000], dtype=torch.int32, device="cuda")
@@ -143,8 +143,6 @@ def test_workspace_zeroed_once_serves_calls_of_any_shape():
             else:
                 assert torch.equal(got, first[key]), f"{kind} loop {loop} repeat {rep}"
     assert not ws[:counter_bytes].any(), "split counters not returned to zero"
-    epochs = ws[counter_bytes:header_bytes].view(torch.int32)
-    assert int(epochs.max()) >= 3 * 4, "split calls did not advance their rows' epochs"
 
 
 def test_graph_replay_matches_eager():
