@@ -287,6 +287,32 @@ uint64_t rq_paged_decode_workspace_bytes(const rq_cache_desc* pool, int32_t q_he
   return workspace_for(pool, n_seqs, q_heads, max_n_tokens);
 }
 
+// The split plan of one decode call and the per-head kernel's waves per
+// workgroup (the grouped kernel's plan counts (row, KV head) pairs).
+static rq::SplitPlan decode_plan(const rq_cache_desc* desc, int32_t rows, int32_t loop,
+                                 int32_t q_heads, int32_t n_tokens, bool paged, int* waves) {
+  const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
+  const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
+  const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
+  *waves = rq::decode_waves(desc->head_dim, chain, paged);
+  const int32_t target = *waves == 8 ? rq::kDecodeTargetWide
+                         : chain     ? rq::kDecodeTargetChain
+                         : two       ? rq::kDecodeTargetTwo
+                                     : rq::kDecodeTargetOne;
+  if (grouped(desc, loop, q_heads))
+    return rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget);
+  return rq::plan_splits(rows * q_heads, n_tokens, rq::decode_tile_tokens(desc->head_dim, *waves),
+                         target);
+}
+
+int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads, int32_t n_tokens) {
+  if (check_desc(desc) != RQ_OK || loop < 0 || loop >= desc->loops || q_heads <= 0 ||
+      q_heads % desc->kv_heads != 0 || n_tokens < 0)
+    return 0;
+  int waves = 4;
+  return decode_plan(desc, desc->batch, loop, q_heads, n_tokens, false, &waves).splits;
+}
+
 static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* cache,
                                        const int8_t* signs, int32_t loop, int32_t layer,
                                        const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
@@ -310,19 +336,8 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
     return RQ_ERR_ALIGNMENT;
   if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
-  const int32_t bh = rows * q_heads;
-  const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
-  const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
-  const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
-  const int waves = rq::decode_waves(desc->head_dim, chain, pg.table != nullptr);
-  const int32_t target = waves == 8 ? rq::kDecodeTargetWide
-                         : chain    ? rq::kDecodeTargetChain
-                         : two      ? rq::kDecodeTargetTwo
-                                    : rq::kDecodeTargetOne;
-  const rq::SplitPlan plan =
-      grouped(desc, loop, q_heads)
-          ? rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget)
-          : rq::plan_splits(bh, n_tokens, rq::decode_tile_tokens(desc->head_dim, waves), target);
+  int waves = 4;
+  const rq::SplitPlan plan = decode_plan(desc, rows, loop, q_heads, n_tokens, pg.table != nullptr, &waves);
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);

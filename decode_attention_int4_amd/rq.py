@@ -30,7 +30,8 @@ OUT_F32, OUT_BF16 = 0, 1
 EXPORTS = (
     "rq_status_string", "rq_validate_desc", "rq_cache_bytes", "rq_cache_slot",
     "rq_quantize_append", "rq_quantize_append_ragged", "rq_reconstruct",
-    "rq_decode_workspace_bytes", "rq_decode_attention", "rq_decode_attention_ragged",
+    "rq_decode_workspace_bytes", "rq_decode_splits", "rq_decode_attention",
+    "rq_decode_attention_ragged",
     "rq_bf16_decode_workspace_bytes", "rq_bf16_decode_attention",
     "rq_read_probe_sink_words", "rq_read_probe",
     "rq_paged_decode_workspace_bytes", "rq_paged_quantize_append", "rq_paged_decode_attention",
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.rq_reconstruct.argtypes = [D, _vp, _vp, _i32, _i32, _i32, _vp, _vp]
         L.rq_decode_workspace_bytes.argtypes = [D, _i32, _i32]
         L.rq_decode_workspace_bytes.restype = _u64
+        L.rq_decode_splits.argtypes = [D, _i32, _i32, _i32]
+        L.rq_decode_splits.restype = _i32
         L.rq_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
                                           ctypes.c_float, _vp, _u64, _vp, _vp]
         L.rq_decode_attention_ragged.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
@@ -167,6 +170,10 @@ def cache_slot(desc: CacheDesc, kv: int, batch: int, layer: int, loop: int, head
 
 def decode_workspace_bytes(desc: CacheDesc, q_heads: int, max_n_tokens: int) -> int:
     return int(lib().rq_decode_workspace_bytes(ctypes.byref(desc), q_heads, max_n_tokens))
+
+
+def decode_splits(desc: CacheDesc, loop: int, q_heads: int, n_tokens: int) -> int:
+    return int(lib().rq_decode_splits(ctypes.byref(desc), loop, q_heads, n_tokens))
 
 
 def bf16_decode_workspace_bytes(desc: CacheDesc, q_heads: int, max_n_tokens: int) -> int:

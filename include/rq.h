@@ -190,6 +190,14 @@ rq_status rq_quantize_append_ragged(const rq_cache_desc* desc, void* cache,
 uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
                                    int32_t max_n_tokens);
 
+/* Number of token splits rq_decode_attention plans for loop `loop`,
+ * `q_heads` query heads and n_tokens tokens of every batch row (host only;
+ * 0 for invalid arguments).  Splits are counted per (batch row, query head),
+ * or per (batch row, KV head) for grouped query heads served on matrix
+ * cores; 1 means the call uses no workspace. */
+int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads,
+                         int32_t n_tokens);
+
 /*
  * Fused decode attention over the packed cache (abstract: reduced KV memory
  * traffic; ai4snews para. 4: reconstruction must not offset the saved

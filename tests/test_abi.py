@@ -235,6 +235,27 @@ def test_workspace_holds_one_round_of_splits():
     assert rq.decode_workspace_bytes(ouro, 16, 127) == 0
 
 
+def test_split_plan_fits_one_round():
+    """The split count the library reports for a call: eight-wave calls
+    (d = 128, at most one residual plane, contiguous cache) aim at 256
+    workgroups, four-wave ones at 512 (110 rows: 4 splits, rounded down),
+    grouped-query calls count (row, KV head) pairs, and no split is shorter
+    than two tiles."""
+    huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs, four waves
+    assert rq.decode_splits(huginn, 0, 55, 8192) == 4
+    ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs, eight waves
+    assert rq.decode_splits(ouro, 0, 16, 8192) == 4
+    assert rq.decode_splits(ouro, 3, 16, 8192) == 4       # the anchor loop
+    assert rq.decode_splits(ouro, 0, 16, 256) == 1        # two 128-token tiles: one split
+    assert rq.decode_splits(ouro, 0, 16, 0) == 1
+    chained = rq.make_desc(4, 4, 1, 16, 8192, 128, mode=rq.MODE_CHAINED)
+    assert rq.decode_splits(chained, 0, 16, 8192) == 8    # three residual planes: four waves
+    gqa = rq.make_desc(16, 4, 1, 4, 8192, 128)             # 64 (row, KV head) pairs, 4 heads each
+    assert rq.decode_splits(gqa, 0, 16, 8192) == 4
+    assert rq.decode_splits(ouro, 4, 16, 8192) == 0       # no such loop
+    assert rq.decode_splits(ouro, 0, 12, 8192) == 0       # 12 query heads on 16 KV heads
+
+
 def test_status_strings():
     for s in range(7):
         assert rq._status_string(s)
