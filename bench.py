@@ -436,9 +436,10 @@ def main():
         kname = (f"gqa_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
                  f"{str(w.page_tokens > 0).lower()}>")
     else:
-        # waves per workgroup: 8 at d = 128 on a contiguous cache unless a chained
-        # loop reads several residual planes (then 4), else 4
-        waves = 8 if (w.head_dim == 128 and w.page_tokens == 0) else 4
+        # waves per workgroup: 8 at d = 128 (residual calls, and anchor calls on
+        # a contiguous cache) unless a chained loop reads several residual
+        # planes (then 4), else 4
+        waves = 8 if (w.head_dim == 128 and (w.page_tokens == 0 or two)) else 4
         kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
                  f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()},"
                  f"{'W' if w.mode == 2 and waves == 8 else waves}>")

@@ -294,7 +294,7 @@ static rq::SplitPlan decode_plan(const rq_cache_desc* desc, int32_t rows, int32_
   const int j = loop % desc->loops_per_group, a_pos = desc->loops_per_group - 1;
   const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
   const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
-  *waves = rq::decode_waves(desc->head_dim, chain, paged);
+  *waves = rq::decode_waves(desc->head_dim, chain, paged, two);
   const int32_t target = *waves == 8 ? rq::kDecodeTargetWide
                          : chain     ? rq::kDecodeTargetChain
                          : two       ? rq::kDecodeTargetTwo

@@ -12,8 +12,8 @@
 //
 // gfx950 mapping.
 //   grid (splits, batch * q_heads), NWK = 4 or 8 waves per workgroup (8 for
-//   d = 128 calls reading at most one residual plane from a contiguous cache:
-//   decode_waves).  A wave takes its
+//   d = 128 calls reading at most one residual plane, paged anchor calls
+//   aside: decode_waves).  A wave takes its
 //   tokens in PAIRS (t, t+1); LPP lanes share a pair and each owns one
 //   quantization group (16 head_dim elements) of both tokens, so a lane's
 //   accumulators cover just 16 elements.
@@ -783,16 +783,19 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 template <int D, int B1, int B2, int NR = 1>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.splits, a.rows * a.q_heads);
-  if (a.paging.table) {
-    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true, 4>), grid, dim3(4 * 64), 0, s, a);
-  } else if constexpr (D == 128 && NR == 1) {
-    if (a.waves == 8)
-      hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 8>), grid, dim3(8 * 64), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 4>), grid, dim3(4 * 64), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 4>), grid, dim3(4 * 64), 0, s, a);
+  if constexpr (D == 128 && NR == 1) {
+    if (a.waves == 8) {
+      if (a.paging.table)
+        hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true, 8>), grid, dim3(8 * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 8>), grid, dim3(8 * 64), 0, s, a);
+      return hipGetLastError();
+    }
   }
+  if (a.paging.table)
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, true, 4>), grid, dim3(4 * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, B1, B2, NR, false, 4>), grid, dim3(4 * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -828,11 +831,11 @@ int decode_wave_tokens(int d) {
 }
 
 // Waves per workgroup: eight (one workgroup per CU, half the splits to
-// merge) for d = 128 calls reading at most one residual plane from a
-// contiguous cache, where that measured faster; four otherwise (eight were
-// slower at d = 96, for chained loops and for paged anchors).
-int decode_waves(int d, bool several_planes, bool paged) {
-  return (d == 128 && !several_planes && !paged) ? 8 : 4;
+// merge) for d = 128 calls reading at most one residual plane, except anchor
+// calls on a paged cache, where that measured faster; four otherwise (eight
+// were slower at d = 96, for chained loops and for paged anchors).
+int decode_waves(int d, bool several_planes, bool paged, bool residual) {
+  return (d == 128 && !several_planes && (!paged || residual)) ? 8 : 4;
 }
 
 int decode_tile_tokens(int d, int waves) {

@@ -62,7 +62,7 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // per-head kernel geometry, shared by the split plan and the launch
-int decode_waves(int d, bool several_planes, bool paged);
+int decode_waves(int d, bool several_planes, bool paged, bool residual);
 int decode_tile_tokens(int d, int waves);
 // grouped-query decode on matrix cores: one workgroup per (split, batch row,
 // KV head) serves the group_ratio query heads of the KV head

@@ -8,9 +8,9 @@ decode attention must match the fp64 oracle on each sequence's logical tokens
 (1e-3 relative L2, 2e-3 max-abs).  The same data in a contiguous cache, read
 by the ragged call, must give the same outputs up to fp32 summation order
 (relative L2 1e-6): the block table changes where the bytes live, not what
-is computed.  (At d = 128 the contiguous call runs eight-wave workgroups and
-the paged call four, with their own split plans, so the partial sums are
-added in a different order.)"""
+is computed.  (At d = 128 anchor calls run eight-wave workgroups on the
+contiguous cache and four on the paged one, with their own split plans, so
+the partial sums are added in a different order.)"""
 import numpy as np
 import pytest
 import torch
