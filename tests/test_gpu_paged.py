@@ -6,11 +6,17 @@ the codes, FP8 bytes and alphas found at each token's block and in-block
 position must equal the oracle's encoding of that token bit for bit, and paged
 decode attention must match the fp64 oracle on each sequence's logical tokens
 (1e-3 relative L2, 2e-3 max-abs).  The same data in a contiguous cache, read
-by the ragged call, must give the same outputs up to fp32 summation order
-(relative L2 1e-6): the block table changes where the bytes live, not what
-is computed.  (At d = 128 anchor calls run eight-wave workgroups on the
-contiguous cache and four on the paged one, with their own split plans, so
-the partial sums are added in a different order.)"""
+by the ragged call, must give the same outputs up to fp32 summation order:
+the block table changes where the bytes live, not what is computed.  Calls
+that run the same kernel shape on both caches agree to rounding (well under
+1e-6); a d = 128 anchor call runs eight-wave workgroups on the contiguous
+cache and four on the paged one, with its own split plan, and its value sums
+then differ by the fp32 rounding of a different summation order, amplified
+by the magic-number unpack: each sum accumulates w (1024 + code) and drops
+1024 sum(w) at the end, about 1024 / 7.5 = 137 times the mean code term, so
+tens of fp32 adds per lane give differences of order 1e-5.  The bound is
+1e-4 relative L2; a paging mistake (a wrong block or position) moves the
+output by order one."""
 import numpy as np
 import pytest
 import torch
@@ -68,22 +74,27 @@ class Pool:
 
 
 CASES = [
-    # d, block tokens, mode, per-sequence fill, lengths attended
-    (128, 16, 0, (333, 200, 17, 333), (333, 200, 0, 101)),
-    (128, 64, 0, (333, 333, 70, 5), (320, 1, 70, 5)),
-    (96, 32, 0, (300, 129, 300, 64), (300, 129, 255, 64)),
-    (64, 32, 0, (300, 96, 31, 300), (300, 96, 31, 0)),
-    (64, 128, 1, (300, 250, 300, 3), (299, 250, 128, 3)),
-    (128, 32, 2, (290, 290, 40, 160), (290, 200, 40, 160)),
+    # d, block tokens, mode, per-sequence fill, lengths attended, query heads per KV head
+    # (2: the grouped kernel serves every call but a chained loop's several
+    # planes; 1: the per-head kernel, eight waves for d = 128 residual calls)
+    (128, 16, 0, (333, 200, 17, 333), (333, 200, 0, 101), 2),
+    (128, 64, 0, (333, 333, 70, 5), (320, 1, 70, 5), 2),
+    (96, 32, 0, (300, 129, 300, 64), (300, 129, 255, 64), 2),
+    (64, 32, 0, (300, 96, 31, 300), (300, 96, 31, 0), 2),
+    (64, 128, 1, (300, 250, 300, 3), (299, 250, 128, 3), 2),
+    (128, 32, 2, (290, 290, 40, 160), (290, 200, 40, 160), 2),
+    (128, 16, 0, (600, 333, 17, 560), (600, 333, 0, 421), 1),
+    (96, 32, 0, (500, 129, 300, 64), (500, 129, 255, 64), 1),
+    (128, 64, 1, (520, 250, 300, 3), (519, 250, 128, 3), 1),
 ]
 
 
-@pytest.mark.parametrize("d,bt,mode,fill,lengths", CASES,
-                         ids=[f"d{c[0]}-bt{c[1]}-mode{c[2]}" for c in CASES])
-def test_paged_append_and_decode(d, bt, mode, fill, lengths):
+@pytest.mark.parametrize("d,bt,mode,fill,lengths,G", CASES,
+                         ids=[f"d{c[0]}-bt{c[1]}-mode{c[2]}-G{c[5]}" for c in CASES])
+def test_paged_append_and_decode(d, bt, mode, fill, lengths, G):
     N = max(fill)
-    w = Workload(f"paged_d{d}_bt{bt}_m{mode}", batch=len(fill), loops=4, layers=2, kv_heads=2,
-                 q_heads=4, head_dim=d, n_tokens=N, seed=d + bt + mode, mode=mode)
+    w = Workload(f"paged_d{d}_bt{bt}_m{mode}_g{G}", batch=len(fill), loops=4, layers=2, kv_heads=2,
+                 q_heads=2 * G, head_dim=d, n_tokens=N, seed=d + bt + mode + G, mode=mode)
     keep = [(s, 1, 1) for s in range(w.batch)] + [(0, 0, 0)]
     chunk = 100
     say(f"[paged] {w.name} fill {fill} lengths {lengths}")
@@ -113,12 +124,12 @@ def test_paged_append_and_decode(d, bt, mode, fill, lengths):
                                                lens, max_n, w.softmax_scale, ws_c)
             got, ref_c = got.cpu().numpy().astype(np.float64), ref_c.cpu().numpy().astype(np.float64)
             diff = np.linalg.norm(got - ref_c) / max(np.linalg.norm(ref_c), 1e-30)
-            assert diff <= 1e-6, f"{w.name} loop {loop} layer {layer}: paged vs contiguous rel-L2 {diff:.2e}"
+            assert diff <= 1e-4, f"{w.name} loop {loop} layer {layer}: paged vs contiguous rel-L2 {diff:.2e}"
             for (s, lay, head) in keep:
                 if lay != layer:
                     continue
                 n = lengths[s]
-                for hq in (2 * head, 2 * head + 1):
+                for hq in range(G * head, G * head + G):
                     if n == 0:
                         assert np.all(got[s, hq] == 0)
                         continue
