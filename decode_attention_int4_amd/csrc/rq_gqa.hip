@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
     else
       issue_t(std::integral_constant<bool, false>{}, tb, st, vt);
   };
-  // ---- the query rows of this wave's heads (w, w + 4, ... below G) and the
+  // ---- the query rows of this wave's heads (w, w + NWG, ... below G) and the
   // key signs come in by DMA ahead of the first tile: a plain load issued
   // after the tile's DMAs would wait for all of them.  (Issuing the second
   // tile here as well measured slower.)
