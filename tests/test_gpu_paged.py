@@ -86,6 +86,7 @@ CASES = [
     (128, 16, 0, (600, 333, 17, 560), (600, 333, 0, 421), 1),
     (96, 32, 0, (500, 129, 300, 64), (500, 129, 255, 64), 1),
     (128, 64, 1, (520, 250, 300, 3), (519, 250, 128, 3), 1),
+    (64, 32, 2, (450, 97, 300, 33), (450, 96, 300, 0), 1),
 ]
 
 
