@@ -26,7 +26,12 @@ static constexpr int32_t kDecodeTargetOne = 512;
 static constexpr int32_t kDecodeTargetChain = 512;  // chained loops reading 2-3 residual planes
 static constexpr int32_t kDecodeTargetWide = 256;   // eight-wave workgroups: one per CU
 static constexpr int32_t kGqaTarget = 256;         // grouped-query kernel (eight waves: one per CU)
-static constexpr int32_t kDecodeTarget = 512;      // the largest target: workspace bound
+static constexpr int32_t kDecodeTarget = 512;      // the largest d = 64, 128 target: workspace bound
+// d = 96 calls reading at most one residual plane: six of every eight lanes
+// hold a group, so the kernel is heavier per byte, and three workgroups per
+// CU (768) measured faster than two (Huginn-like shapes: residual call 54.3
+// -> 52.4 us; anchor calls gain a little too)
+static constexpr int32_t kDecodeTarget96 = 768;
 static constexpr int32_t kBf16Target = 512;
 
 static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
@@ -266,7 +271,7 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
   const int32_t bh = rows * q_heads;
   // four-wave tiles at the largest target bound the eight-wave plans too
   int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim, 4),
-                                   rq::kDecodeTarget);
+                                   desc->head_dim == 96 ? rq::kDecodeTarget96 : rq::kDecodeTarget);
   bool any_grouped = false;
   for (int32_t loop = 0; loop < desc->loops_per_group; ++loop)
     any_grouped = any_grouped || grouped(desc, loop, q_heads);
@@ -295,10 +300,11 @@ static rq::SplitPlan decode_plan(const rq_cache_desc* desc, int32_t rows, int32_
   const bool two = desc->mode != RQ_MODE_DIRECT && j != a_pos;
   const bool chain = desc->mode == RQ_MODE_CHAINED && a_pos - j > 1;  // several residual planes
   *waves = rq::decode_waves(desc->head_dim, chain, paged, two);
-  const int32_t target = *waves == 8 ? rq::kDecodeTargetWide
-                         : chain     ? rq::kDecodeTargetChain
-                         : two       ? rq::kDecodeTargetTwo
-                                     : rq::kDecodeTargetOne;
+  const int32_t target = *waves == 8            ? rq::kDecodeTargetWide
+                         : chain                  ? rq::kDecodeTargetChain
+                         : desc->head_dim == 96   ? rq::kDecodeTarget96
+                         : two                    ? rq::kDecodeTargetTwo
+                                                  : rq::kDecodeTargetOne;
   if (grouped(desc, loop, q_heads))
     return rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget);
   return rq::plan_splits(rows * q_heads, n_tokens, rq::decode_tile_tokens(desc->head_dim, *waves),

@@ -221,13 +221,13 @@ def test_workspace_bound_is_monotone():
 
 def test_workspace_holds_one_round_of_splits():
     """The split planner rounds the number of splits per (row, head) down, so
-    a grid of at most 512 four-wave workgroups runs in one round: 110 rows
-    take 4 splits (440 workgroups), not 5.  The workspace is the 256 KiB
-    counter block plus one partial state (m, l, accA[d], accR[d]) per row,
-    head and split."""
+    a grid of at most its target of four-wave workgroups runs in one round
+    (512 at d = 64 and 128, 768 at d = 96: 110 rows take 6 splits, 660
+    workgroups, not 7).  The workspace is the 256 KiB counter block plus one
+    partial state (m, l, accA[d], accR[d]) per row, head and split."""
     counters = (1 << 16) * 4
     huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs
-    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 4 * (2 + 2 * 96) * 4
+    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 6 * (2 + 2 * 96) * 4
     ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs: 8 splits
     assert rq.decode_workspace_bytes(ouro, 16, 8192) == counters + 64 * 8 * (2 + 2 * 128) * 4
     # short contexts: at most half the 64-token tiles, and no workspace for one split
@@ -237,12 +237,14 @@ def test_workspace_holds_one_round_of_splits():
 
 def test_split_plan_fits_one_round():
     """The split count the library reports for a call: eight-wave calls
-    (d = 128, at most one residual plane, contiguous cache) aim at 256
-    workgroups, four-wave ones at 512 (110 rows: 4 splits, rounded down),
+    (d = 128, at most one residual plane, paged anchors aside) aim at 256
+    workgroups, four-wave ones at 512 (d = 96 calls at 768; 110 rows: 6
+    splits, rounded down),
     grouped-query calls count (row, KV head) pairs, and no split is shorter
     than two tiles."""
     huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs, four waves
-    assert rq.decode_splits(huginn, 0, 55, 8192) == 4
+    assert rq.decode_splits(huginn, 0, 55, 8192) == 6     # 768-workgroup target at d = 96
+    assert rq.decode_splits(huginn, 3, 55, 8192) == 6     # the anchor loop too
     ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs, eight waves
     assert rq.decode_splits(ouro, 0, 16, 8192) == 4
     assert rq.decode_splits(ouro, 3, 16, 8192) == 4       # the anchor loop
