@@ -190,9 +190,9 @@ __device__ __forceinline__ void dma_piece(rsrc_t r, uint32_t so, int valid, lds_
     if constexpr (FULL) {
       // the c * STEP part rides in the scalar offset
       const int vo = (c * STEP + STEP <= BYTES) ? lane * G : min(o, BYTES - G) - c * STEP;
-      dma1<G>(r, dst + c * STEP, vo, so + c * STEP);
+      dma1<G, true>(r, dst + c * STEP, vo, so + c * STEP);
     } else {
-      dma1<G>(r, dst + c * STEP, min(o, valid - G), so);
+      dma1<G, true>(r, dst + c * STEP, min(o, valid - G), so);
     }
   }
 }
@@ -329,9 +329,11 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   using ST = Stage<D, B1, B2, NR>;
   constexpr int kStaging = NWK * ST::COUNT * ST::BYTES;
   constexpr int kRow = (TWO ? 2 * D : D) + 1;              // accA | accR | l
-  constexpr int kEpilogue = NWK * kRow * 4;
-  // the epilogue buffers reuse the staging area once every wave has finished
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kEpilogue ? kStaging : kEpilogue];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging];
+  // each wave's sums, written as soon as its last tile is done (their own
+  // space, so no wave waits for the others before reducing its state)
+  constexpr int kRowP = (kRow + 3) / 4 * 4;  // rows 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float sm_acc[NWK][kRowP];
   __shared__ float sq[D], su[D];
   __shared__ float s_scale[2];
   // per-group query pairs; rows padded to 36 dwords so that the 16-byte
@@ -339,10 +341,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   __shared__ __attribute__((aligned(16))) uint32_t spre[8][36];
   __shared__ float sm_m[NWK];
   __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_claim;   // next unclaimed wave tile of this split
   // the query row (BF16) and this layer's key signs, staged by DMA
   __shared__ __attribute__((aligned(16))) uint8_t s_in[512];
-  typedef float AccRow[kRow];
-  AccRow* sm_acc = reinterpret_cast<AccRow*>(smem);               // [wave][accA | accR | l]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -393,10 +394,20 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
   const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
 
-  // ---- stream this wave's tiles through its LDS ring
+  // ---- stream the split's wave tiles (tile k: TPW tokens from t_begin +
+  // k TPW) through each wave's LDS ring.  Waves start with tiles w and
+  // NWK + w; after that each wave claims the next unclaimed tile of the split
+  // from an LDS counter, one tile ahead.  With a fixed tile-to-wave mapping
+  // the second wave on each SIMD, which loses issue arbitration to the
+  // first, finished its equal share about 5 us later (residual call at 8k
+  // tokens, batch 4); claiming keeps every wave busy until the split is done.
+  // The order in which tiles are summed therefore varies from call to call:
+  // results agree to fp32 summation order, not bit for bit.
+  static_assert(ST::COUNT == 2, "the claim schedule runs a two-slot ring");
   lds_u8* ring = (lds_u8*)smem + w * ST::COUNT * ST::BYTES;
-  const int first = t_begin + w * TPW;
-  const int n_tiles = first < t_end ? (t_end - first + NWK * TPW - 1) / (NWK * TPW) : 0;
+  const int n_tot = t_end > t_begin ? (t_end - t_begin + TPW - 1) / TPW : 0;
+  int kcur = w, knext = NWK + w;   // tile being computed, tile after it
+  uint32_t claimed = 0;             // lane 0: the tile claimed for the one after
   // tiles in flight before the query side is built: the whole ring, unless
   // its DMA count would not fit the wait below
   constexpr int kPre = ST::COUNT * ST::N_DMA < 64 ? ST::COUNT : ST::COUNT - 1;
@@ -419,9 +430,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       }
     }
   };
-  auto issue = [&](int tile) __attribute__((always_inline)) {
-    uint32_t tb = (uint32_t)(first + tile * NWK * TPW);
-    lds_u8* st = ring + (tile % ST::COUNT) * ST::BYTES;
+  auto issue = [&](int k, int slot) __attribute__((always_inline)) {
+    uint32_t tb = (uint32_t)(t_begin + k * TPW);
+    lds_u8* st = ring + slot * ST::BYTES;
     const int vt = t_end - (int)tb;  // in-range tokens of this tile (>= 1)
     if constexpr (PAGED) {
       // ids outside the pool are clamped into it: garbage in, but no read
@@ -444,9 +455,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), (lds_u8*)s_in + 256,
               min(4 * lane, D - 4), 0u);
   }
-#pragma unroll
-  for (int i = 0; i < kPre; ++i)
-    if (i < n_tiles) issue(i);
+  if (kcur < n_tot) issue(kcur, 0);
+  if (kPre == 2 && knext < n_tot) issue(knext, 1);
+  if (tid == 0) s_claim = 2 * NWK;
 
   // ---- query side, once per workgroup (wave 0): q, u = H q, their fp16
   // prescales, and for every group the fp16 pairs matching the code pairs,
@@ -454,7 +465,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   if (w == 0) {
     // the staged row has landed once at most the tiles' DMAs are pending
     static_assert(kPre <= 2, "waits below cover two tiles");
-    const int pre = min(kPre, n_tiles);
+    const int pre = (kcur < n_tot ? 1 : 0) + (kPre == 2 && knext < n_tot ? 1 : 0);
     if constexpr (kPre == 2) {
       if (pre == 2) wait_vm<2 * ST::N_DMA>();
     }
@@ -553,18 +564,26 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const int o1c = t0 * ST::R1 + eg * CB1, o2c = t0 * ST::R2 + eg * CB2;
   const int osz = t0 * ST::RS + eg * 2, oal = t0 * 4;
 
+  // the claim for the third tile; its result is read after the first tile
+  auto claim = [&]() __attribute__((always_inline)) {
+    if (lane == 0)
+      claimed = __hip_atomic_fetch_add(&s_claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  claim();
   // one loop body for every stage: stage-specialized copies would make the
-  // compiler shuffle all live accumulators between them on every iteration
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + ST::COUNT - 1 >= kPre && it + ST::COUNT - 1 < n_tiles) issue(it + ST::COUNT - 1);
-    // wait for tile `it`: the tiles issued after it may stay in flight
-    const int later = min(ST::COUNT - 1, n_tiles - 1 - it);
-    static_assert(ST::COUNT <= 3, "wait counts below cover rings up to 3 deep");
-    if (ST::COUNT == 3 && later == 2) wait_vm<(ST::COUNT - 1) * ST::N_DMA>();
-    else if (later >= 1) wait_vm<ST::N_DMA>();
+  // compiler shuffle all live accumulators between them on every iteration.
+  // Tiles are claimed in increasing order, so once knext is past the split
+  // every later claim is too.
+  for (int it = 0; kcur < n_tot; ++it) {
+    // slot (it & 1) holds kcur; knext goes to the other slot (issued before
+    // the loop when the ring was filled up front)
+    if (it + 1 >= kPre && knext < n_tot) issue(knext, (it + 1) & 1);
+    if (it > 0) claim();
+    // wait for kcur: the tile issued after it may stay in flight
+    if (knext < n_tot) wait_vm<ST::N_DMA>();
     else wait_vm<0>();
-    const lds_u8* st = ring + (it % ST::COUNT) * ST::BYTES;
-    const int tt = first + it * NWK * TPW + t0;
+    const lds_u8* st = ring + (it & 1) * ST::BYTES;
+    const int tt = t_begin + kcur * TPW + t0;
     const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
     // keys now; the value planes are read after the softmax update, so their
@@ -682,14 +701,15 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
         value_acc<B2E, false>(v2, wr, wr, accR, magic);
       }
     }
+    kcur = knext;
+    knext = (int)__builtin_amdgcn_readfirstlane(claimed);
   }
-  __syncthreads();  // every wave is done with its ring before the epilogue reuses it
 
   // ---- take out the magic constant (element i holds sum w (1024 + m_i c_i);
   // the residual sum also takes out its centre c0 * sum w) and align every
   // lane to the wave maximum in the same step
   const float Mw = wave_max(m);
-  const float f = exp2f(m - Mw);
+  const float f = __builtin_amdgcn_exp2f(m - Mw);
   l *= f;
   static_for<16>([&](auto I) {
     constexpr int k1 = decltype(I)::value % Pairs<B1>::PER_UNIT;
@@ -719,11 +739,13 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   }
   l = pairs_sum(l);
   if (active && pj == 0) {
+    float4* ra = reinterpret_cast<float4*>(&sm_acc[w][e * 16]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm_acc[w][e * 16 + i] = accA[i];
+    for (int i = 0; i < 4; ++i) ra[i] = make_float4(accA[4 * i], accA[4 * i + 1], accA[4 * i + 2], accA[4 * i + 3]);
     if constexpr (TWO) {
+      float4* rr = reinterpret_cast<float4*>(&sm_acc[w][D + e * 16]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm_acc[w][D + e * 16 + i] = accR[i];
+      for (int i = 0; i < 4; ++i) rr[i] = make_float4(accR[4 * i], accR[4 * i + 1], accR[4 * i + 2], accR[4 * i + 3]);
     }
     if (e == 0) sm_acc[w][kRow - 1] = l;
   }
@@ -736,7 +758,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   for (int ww = 1; ww < NWK; ++ww) M = fmaxf(M, sm_m[ww]);
   float fw[NWK];
 #pragma unroll
-  for (int ww = 0; ww < NWK; ++ww) fw[ww] = exp2f(sm_m[ww] - M);
+  for (int ww = 0; ww < NWK; ++ww) fw[ww] = __builtin_amdgcn_exp2f(sm_m[ww] - M);
   auto merged = [&](int i) {
     float s = 0.f;
 #pragma unroll
@@ -756,7 +778,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       }
     }
     if (!arrive_last(a, bh, tid, &s_ticket) || w != 0) return;
-    merge_row<D, TWO>(a, bh, lane);
+    merge_splits<D, TWO>(a, bh, lane);
     return;
   }
   // ---- a single split: finish here (first wave, two elements per lane)

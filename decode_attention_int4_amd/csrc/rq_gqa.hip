@@ -124,7 +124,7 @@ __device__ __forceinline__ void dma_gather(rsrc_t r, uint32_t so, int valid, lds
   for (int c = 0; c < gather_dmas(W); ++c) {
     const int p = min(c * 64 + lane, 16 * W - 1);
     const int w = p >> 4, m = FULL ? (p & 15) : min(p & 15, valid - 1);
-    dma1<4>(r, dst + c * 256, m * ROWB + w * 4, so);
+    dma1<4, true>(r, dst + c * 256, m * ROWB + w * 4, so);
   }
 }
 
@@ -140,7 +140,7 @@ __device__ __forceinline__ void dma_blocks(rsrc_t r, uint32_t so, int valid, lds
   for (int b = 0; b < CB::NB; ++b) {
     const int t = b * CB::BT + tl;
     const int m = FULL ? t : min(t, valid - 1);
-    dma1<4>(r, dst + b * CB::STRIDE * 4, m * ROWB + w * 4, so);
+    dma1<4, true>(r, dst + b * CB::STRIDE * 4, m * ROWB + w * 4, so);
   }
 }
 
@@ -149,7 +149,7 @@ __device__ __forceinline__ void dma_blocks(rsrc_t r, uint32_t so, int valid, lds
 template <int WS, int ROWB, bool FULL>
 __device__ __forceinline__ void dma_szrows(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
   const int m = FULL ? (lane >> 2) : min(lane >> 2, valid - 1);
-  dma1<4>(r, dst, m * ROWB + min(lane & 3, WS - 1) * 4, so);
+  dma1<4, true>(r, dst, m * ROWB + min(lane & 3, WS - 1) * 4, so);
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const lds_u8* p) {
@@ -805,7 +805,7 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
     // counter per KV head: that of its first query head)
     const int bh0 = b * a.q_heads + kvh * G;
     if (!arrive_last(a, bh0, tid, &s_ticket)) return;
-    for (int n = w; n < G; n += NWG) merge_row<D, TWO>(a, bh0 + n, lane);
+    for (int n = w; n < G; n += NWG) merge_splits<D, TWO>(a, bh0 + n, lane);
     return;
   }
   // ---- a single split: finish here, one wave per head

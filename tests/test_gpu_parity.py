@@ -17,6 +17,14 @@ from tests.layout_decode import Geom, decode_slice
 
 pytestmark = pytest.mark.gpu
 
+# Two calls on the same inputs sum a split's tiles in different orders (the
+# per-head kernel's waves claim tiles as they free up).  fp32 rounding of the
+# magic-number value sums (1024 per unit weight, dropped at the end) is
+# amplified about 137 times for 4-bit codes, so repeats agree to about 1e-5
+# relative L2; anything that reads a wrong tile or a stale partial state moves
+# the output by far more.
+REPEAT_REL = 1e-4
+
 
 @pytest.fixture(scope="module")
 def tiny():
@@ -98,8 +106,10 @@ def test_workspace_zeroed_once_serves_calls_of_any_shape():
     hold anything (NaN here).  Calls of different shapes then share it: several
     split counts, per-head and grouped-query kernels, ragged rows; every
     result matches the oracle and every counter is back to zero afterwards.
-    Repeated alternating calls give bit-identical outputs each time, so no
-    merge reads a partial state left by an earlier call."""
+    Repeated alternating calls agree with the first call to fp32 summation
+    order (the per-head kernel's waves claim tiles dynamically, so the order in
+    which a split's tiles are summed varies; a merge that read another call's
+    partial state would move the output by order one)."""
     w = Workload("ws_share", batch=2, loops=4, layers=1, kv_heads=2, q_heads=4, head_dim=128,
                  n_tokens=4000, seed=5)
     keep = [(1, 0, 1)]
@@ -141,13 +151,16 @@ def test_workspace_zeroed_once_serves_calls_of_any_shape():
                 ref = oracle_attention(w, ek, ev, HK, HV, bits16(q), loop, n)
                 assert_close_attention(got[1, hq].cpu().numpy(), ref, f"{kind} loop {loop}")
             else:
-                assert torch.equal(got, first[key]), f"{kind} loop {loop} repeat {rep}"
+                assert torch.isfinite(got).all(), f"{kind} loop {loop} repeat {rep}"
+                rel = ((got - first[key]).norm() / first[key].norm()).item()
+                assert rel <= REPEAT_REL, f"{kind} loop {loop} repeat {rep}: rel {rel:.2e}"
     assert not ws[:counter_bytes].any(), "split counters not returned to zero"
 
 
 def test_graph_replay_matches_eager():
     """A whole decode step captured in a HIP graph (as the benchmark replays
-    it) gives bit-identical outputs and cache bytes on every replay, with
+    it) gives bit-identical cache bytes on every replay and outputs equal to
+    the eager step's to fp32 summation order (dynamic tile claiming), with
     eager work and synchronization between the replays."""
     w = Workload("graph", batch=2, loops=4, layers=2, kv_heads=2, q_heads=4, head_dim=128,
                  n_tokens=3000, seed=9)
@@ -171,7 +184,9 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(run.out, eager_out), f"replay {rep}: outputs differ"
+        assert torch.isfinite(run.out).all(), f"replay {rep}: non-finite output"
+        rel = ((run.out - eager_out).norm() / eager_out.norm()).item()
+        assert rel <= REPEAT_REL, f"replay {rep}: outputs differ by {rel:.2e}"
         assert torch.equal(run.cache, eager_cache), f"replay {rep}: cache differs"
 
 
