@@ -207,8 +207,12 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
         y0 *= (double)sg[lane];
         if (v1ok) y1 *= (double)sg[lane + 64];
         wht<D>(y0, y1, lane);
-        y0 *= sc0;
-        y1 = v1ok ? y1 * sc1 : 0.0;
+        // + 0.0 turns a -0 into +0 and changes nothing else: an element of
+        // H r whose exact sum is zero is +0 (a sum accumulated from zero),
+        // whatever signed zeros the butterflies passed through, so the FP8
+        // offset of an all-zero residual group is +0 (0x00), not 0x80
+        y0 = y0 * sc0 + 0.0;
+        y1 = v1ok ? y1 * sc1 + 0.0 : 0.0;
       }
       if (chained) {
         y0 -= corr0;

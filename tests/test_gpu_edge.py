@@ -1,0 +1,122 @@
+"""GPU parity on the quantizer's degenerate groups, through the C ABI: codes,
+FP8 bytes and alphas bit for bit against the oracle, and decode attention
+within 1e-3 relative L2 / 2e-3 max-abs.  The inputs are built by hand (seeded),
+16 tokens per kind, every loop group of every slice:
+
+  * on-grid anchors with every other loop equal to the anchor: the anchor
+    dequantizes exactly, so residuals are zero (scale and offset 0, alpha 0);
+  * constant groups (max == min): scale 0, all codes 0, the group dequantizes
+    to its FP8 offset;
+  * residuals of about 1e-3: FP8 subnormal scales and offsets;
+  * values around +-1000: FP8 offsets saturate at -448 and residual scales at
+    448, codes clamp;
+  * BF16 subnormal inputs (|x| < 2^-126): FP8 rounds them to (signed) zero;
+  * ordinary values, as a control.
+(ai4snews summary, paragraph 2: FP8 scales and offsets per group of 16.)"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_int4_amd import rq
+from decode_attention_int4_amd.synth import Workload, rotation_signs
+from decode_attention_int4_amd.workload import desc_for
+from tests.gpu_common import (assert_close_attention, assert_planes_equal, bits16, encode_kept,
+                              oracle_attention, say)
+from tests.layout_decode import Geom, decode_slice
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("on_grid_equal", "constant", "tiny_residual", "saturating", "bf16_subnormal", "normal")
+
+
+def _fp8_values():
+    """Every finite positive FP8 e4m3fn value, from the oracle's decoder."""
+    v = O.fp8_decode(np.arange(0x01, 0x7F, dtype=np.uint8))
+    return v[v > 0]
+
+
+def edge_states(rng, P, d, T):
+    """float64 [P, T, d] loop states of one slice: 16 tokens of each kind."""
+    x = np.zeros((P, T, d))
+    per = T // len(KINDS)
+    fp8 = _fp8_values()
+    for ki, kind in enumerate(KINDS):
+        sl = slice(ki * per, (ki + 1) * per)
+        n = per
+        if kind == "on_grid_equal":
+            # x = s * (c - 8) with an FP8 scale s and codes covering 0 and 15:
+            # max - min = 15 s, min = -8 s, both FP8, so the anchor is on grid
+            s = rng.choice(fp8[(fp8 > 2 ** -4) & (fp8 < 8)], size=(n, d // 16, 1))
+            c = rng.integers(0, 16, size=(n, d // 16, 16))
+            c[:, :, 0], c[:, :, 1] = 0, 15
+            a = (s * (c - 8)).reshape(n, d)
+            x[:, sl] = a[None]
+        elif kind == "constant":
+            a = np.repeat(rng.normal(size=(n, d // 16, 1)), 16, axis=2).reshape(n, d)
+            x[:, sl] = a[None] + np.repeat(rng.normal(size=(P, n, d // 16, 1)) * 0.3, 16,
+                                           axis=3).reshape(P, n, d)
+            x[P - 1, sl] = a
+        elif kind == "tiny_residual":
+            # on-grid anchor (dequantizes exactly) of magnitude ~0.1, so the
+            # residuals are the 1e-3 perturbations themselves
+            s = rng.choice(fp8[(fp8 > 2 ** -8) & (fp8 < 2 ** -5)], size=(n, d // 16, 1))
+            c = rng.integers(0, 16, size=(n, d // 16, 16))
+            c[:, :, 0], c[:, :, 1] = 0, 15
+            a = (s * (c - 8)).reshape(n, d)
+            x[:, sl] = a[None] + 1e-3 * rng.normal(size=(P, n, d))
+            x[P - 1, sl] = a
+        elif kind == "saturating":
+            a = 1000.0 * rng.normal(size=(n, d))
+            x[:, sl] = a[None] + 300.0 * rng.normal(size=(P, n, d))
+            x[P - 1, sl] = a
+        elif kind == "bf16_subnormal":
+            x[:, sl] = rng.normal(size=(P, n, d)) * 2.0 ** -130
+        else:
+            a = rng.normal(size=(n, d))
+            x[:, sl] = a[None] + 0.2 * rng.normal(size=(P, n, d))
+            x[P - 1, sl] = a
+    return x
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_edge_groups(d):
+    w = Workload(f"edge_{d}", batch=2, loops=4, layers=1, kv_heads=2, q_heads=2, head_dim=d,
+                 n_tokens=16 * len(KINDS), seed=d)
+    T, P = w.n_tokens, w.loops_per_group
+    rng = np.random.default_rng(1234 + d)
+    desc = desc_for(w, T)
+    cache = rq.alloc_cache(desc)
+    # [2, B, loops, layers, H, T, d] as BF16 bit patterns via the oracle's RNE encoder
+    x = np.zeros((2, w.batch, w.loops, 1, w.kv_heads, T, d), np.uint16)
+    for kv in range(2):
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                x[kv, b, :, 0, h] = O.bf16_encode(edge_states(rng, P, d, T))
+    kv_t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    signs = rotation_signs(w).cuda()
+    # two appends: a chunk of 40 tokens, then the rest
+    rq.quantize_append(desc, cache, kv_t[:, :, :, :, :, :40].contiguous(), 0, signs)
+    rq.quantize_append(desc, cache, kv_t[:, :, :, :, :, 40:].contiguous(), 40, signs)
+    torch.cuda.synchronize()
+    geom = Geom.of(desc)
+    q = torch.randn(w.loops, w.batch, w.q_heads, d, generator=torch.Generator().manual_seed(d)
+                    ).to(torch.bfloat16).cuda()
+    ws = rq.alloc_workspace(rq.decode_workspace_bytes(desc, w.q_heads, T))
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            kept = torch.from_numpy(x[:, b, :, 0, h].view(np.int16)).view(torch.bfloat16)
+            ek, ev, HK, HV = encode_kept(w, kept, 0)
+            for kv, enc in ((0, ek), (1, ev)):
+                gpu = decode_slice(cache, geom, kv, b, 0, h, T, 0)
+                assert_planes_equal(gpu, enc, f"{w.name} kv={kv} row={b} head={h}")
+            # the degenerate branches were reached
+            assert np.any(ek.s8[:P - 1] == 0) and np.any(ek.alpha[:P - 1] == 0)
+            assert np.any((ek.s8 > 0) & (ek.s8 < 8)), "no FP8 subnormal scale"
+            assert np.any(ek.z8 == 0xFE) and np.any(ek.s8 == 0x7E), "no saturated offset / scale"
+            for loop in range(w.loops):
+                out = rq.decode_attention(desc, cache, signs, loop, 0, q[loop], T, w.softmax_scale,
+                                          ws).cpu().numpy()
+                ref = oracle_attention(w, ek, ev, HK, HV, bits16(q[loop, b, h]), loop, T)
+                assert_close_attention(out[b, h], ref, f"{w.name} row {b} head {h} loop {loop}")
+    say(f"[edge] d={d}: planes bit-exact, attention within bounds on all degenerate kinds")
