@@ -701,13 +701,31 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
         value_acc<B2E, false>(v2, wr, wr, accR, magic);
       }
     }
+    // Every 8 tiles, fold the magic constant out of the value sums: each sum
+    // holds sum w (1024 + m c), and left in place the 1024 sum w term grows
+    // with every tile a lane adds, so the fp32 rounding of the small code term
+    // would grow with the context.  The residual sums' centring term
+    // (c0 sum w, see the final formula below) moves into their offset sum.
+    if ((it & 7) == 7) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) accA[i] = fmaf(-1024.f, WA, accA[i]);
+      WA = 0.f;
+      if constexpr (TWO) {
+        constexpr float c0 = (float)((1 << B2E) - 1) * 0.5f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accR[i] = fmaf(-1024.f, WR, accR[i]);
+        zR = fmaf(-c0 / kWR, WR, zR);
+        WR = 0.f;
+      }
+    }
     kcur = knext;
     knext = (int)__builtin_amdgcn_readfirstlane(claimed);
   }
 
-  // ---- take out the magic constant (element i holds sum w (1024 + m_i c_i);
-  // the residual sum also takes out its centre c0 * sum w) and align every
-  // lane to the wave maximum in the same step
+  // ---- take out the magic constant of the tiles since the last fold
+  // (element i holds sum w (1024 + m_i c_i); the residual sum also takes out
+  // its centre c0 * sum w) and align every lane to the wave maximum in the
+  // same step
   const float Mw = wave_max(m);
   const float f = __builtin_amdgcn_exp2f(m - Mw);
   l *= f;
