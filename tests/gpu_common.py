@@ -101,3 +101,41 @@ def assert_close_attention(gpu, ref, what):
 
 def oracle_attention(w, ek, ev, HK, HV, q_bits, loop, n):
     return O.attention_slice(params(w), ek, ev, HK, HV, q_bits, loop, n, w.softmax_scale)
+
+
+def check_reconstruct(w, run, encs, t0, t1, loops=None, tol_rel=2e-5):
+    """rq_reconstruct over tokens [t0, t1), fp32 and BF16 outputs, compared
+    element by element with the oracle's reconstruction of the same planes
+    (ai4snews summary, paragraph 3: anchor plus alpha H^T times the residual).
+
+    encs: {(batch row, layer, kv head): (enc K, enc V, signs K, signs V)}.
+    fp32: within tol_rel of max(1, max |ref|) (fp32 arithmetic of the FWHT and
+    the alpha products against the fp64 oracle); BF16: bit-equal to the
+    round-to-nearest-even of the library's own fp32 result, and within one
+    BF16 half-ulp of the fp64 reference plus the fp32 tolerance.  Returns the
+    worst fp32 error relative to max(1, max |ref|)."""
+    from decode_attention_int4_amd import rq
+    loops = range(w.loops) if loops is None else loops
+    out32 = rq.reconstruct(run.desc, run.cache, run.signs, t0, t1)
+    out16 = rq.reconstruct(run.desc, run.cache, run.signs, t0, t1, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    p = params(w)
+    worst = 0.0
+    for (b, layer, head), (ek, ev, HK, HV) in encs.items():
+        g32 = out32[:, b, :, layer, head].cpu().numpy()
+        g16 = bits16(out16[:, b, :, layer, head])
+        for kv, e, H in ((0, ek, HK), (1, ev, HV)):
+            for loop in loops:
+                ref = O.reconstruct_slice(p, e, H, loop, t0, t1)
+                got = g32[kv, loop].astype(np.float64)
+                scale = max(1.0, float(np.abs(ref).max()))
+                err = float(np.abs(got - ref).max()) / scale
+                worst = max(worst, err)
+                where = f"{w.name} kv {kv} slice {(b, layer, head)} loop {loop} tokens [{t0},{t1})"
+                assert err <= tol_rel, f"{where}: fp32 error {err:.3e} of max |ref|"
+                mine = O.bf16_encode(got)
+                assert np.array_equal(g16[kv, loop], mine), f"{where}: BF16 is not RNE of the fp32 output"
+                half_ulp = np.abs(O.bf16_decode(O.bf16_encode(ref)) - ref) + 2.0 ** -9 * np.abs(ref)
+                assert np.all(np.abs(O.bf16_decode(g16[kv, loop]) - ref) <= half_ulp + tol_rel * scale), where
+    del out32, out16
+    return worst

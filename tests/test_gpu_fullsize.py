@@ -2,7 +2,8 @@
 benchmark times (chunked fill, then one decode step: every loop x layer
 attention call and the new token's quantize-append).  The oracle checks
 sampled (batch row, layer, kv head) slices one by one: all their codes, FP8
-bytes and alphas bit for bit, and their attention outputs for every loop."""
+bytes and alphas bit for bit, their attention outputs for every loop, and
+rq_reconstruct (fp32 and BF16) over the first and the last 64 tokens."""
 import gc
 
 import numpy as np
@@ -11,8 +12,8 @@ import torch
 
 from decode_attention_int4_amd.synth import WORKLOADS
 from decode_attention_int4_amd.workload import RQDecode
-from tests.gpu_common import (assert_close_attention, bits16, check_slice_planes,
-                              oracle_attention, POOL, say)
+from tests.gpu_common import (assert_close_attention, bits16, check_reconstruct,
+                              check_slice_planes, oracle_attention, POOL, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +26,7 @@ CASES = {
 }
 
 
-def _run_case(name, keep, loops=None, w=None):
+def _run_case(name, keep, loops=None, w=None, reconstruct=True):
     w = w or WORKLOADS[name]
     say(f"[fullsize] {name}: fill {w.n_tokens} tokens, batch {w.batch}")
     run = RQDecode(w, keep=keep)
@@ -35,10 +36,12 @@ def _run_case(name, keep, loops=None, w=None):
     out = run.out.cpu().numpy()
     assert np.isfinite(out).all()
     loops = range(w.loops) if loops is None else loops
+    encs = {}
     for key in keep:
         b, layer, head = key
         say(f"[fullsize] {name}: oracle on slice {key}")
         ek, ev, HK, HV = check_slice_planes(w, run, key)
+        encs[key] = (ek, ev, HK, HV)
         futs = {loop: POOL.submit(oracle_attention, w, ek, ev, HK, HV,
                                   bits16(run.q[loop, layer, b, head]), loop, run.N)
                 for loop in loops}
@@ -49,6 +52,11 @@ def _run_case(name, keep, loops=None, w=None):
             worst_rel, worst_mx = max(worst_rel, rel), max(worst_mx, mx)
         say(f"[fullsize] {name}: slice {key} ok (worst rel-L2 {worst_rel:.2e}, max-abs {worst_mx:.2e} "
             f"over {len(futs)} loops)")
+    if reconstruct:
+        n = run.N
+        for t0, t1 in ((0, 64), (n - 64, n)):
+            err = check_reconstruct(w, run, encs, t0, t1, loops)
+            say(f"[fullsize] {name}: reconstruct tokens [{t0},{t1}) ok (worst fp32 error {err:.2e} of max |x|)")
     del run
     gc.collect()
     torch.cuda.empty_cache()
@@ -67,4 +75,6 @@ def test_capacity_batch128():
     need = 1.47e9 * 128 + 8e9
     if free < need:
         pytest.skip(f"needs {need / 1e9:.0f} GB free, have {free / 1e9:.0f} GB")
-    _run_case("ouro8k_b128", [(127, 13, 9), (64, 0, 0)], loops=[0, 3], w=w)
+    # rq_reconstruct writes every slot of a token window (13 GB at this batch
+    # for 64 tokens); the other full-size cases cover it
+    _run_case("ouro8k_b128", [(127, 13, 9), (64, 0, 0)], loops=[0, 3], w=w, reconstruct=False)
