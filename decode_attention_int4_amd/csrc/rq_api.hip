@@ -151,6 +151,25 @@ rq_status rq_cache_bytes(const rq_cache_desc* desc, uint64_t* total_bytes) {
   return RQ_OK;
 }
 
+rq_status rq_cache_layout(const rq_cache_desc* desc, rq_layout* out) {
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (!out) return RQ_ERR_INVALID_ARG;
+  const Geometry g = rq::make_geometry(*desc);
+  out->total_bytes = g.total;
+  out->layer_bytes = g.layer_block;
+  out->group_bytes = g.group_bytes;
+  for (int k = 0; k < 2; ++k) {
+    out->slot_bytes[k] = g.slot_bytes[k];
+    out->sz_offset[k] = g.codes_bytes[k];
+    out->code_row_bytes[k] = desc->head_dim * (k == 0 ? desc->anchor_bits : desc->residual_bits) / 8;
+  }
+  out->alpha_offset = g.alpha_bytes ? g.codes_bytes[1] + g.sz_bytes : UINT64_MAX;
+  out->sz_row_bytes = 2 * desc->head_dim / 16;
+  out->token_tile = rq::decode_wave_tokens(desc->head_dim);
+  return RQ_OK;
+}
+
 rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, int32_t layer,
                         int32_t loop, int32_t kv_head, rq_slot* out) {
   rq_status st = check_desc(desc);

@@ -28,7 +28,7 @@ OUT_F32, OUT_BF16 = 0, 1
 
 # Every symbol include/rq.h declares.
 EXPORTS = (
-    "rq_status_string", "rq_validate_desc", "rq_cache_bytes", "rq_cache_slot",
+    "rq_status_string", "rq_validate_desc", "rq_cache_bytes", "rq_cache_layout", "rq_cache_slot",
     "rq_quantize_append", "rq_quantize_append_ragged", "rq_reconstruct",
     "rq_decode_workspace_bytes", "rq_decode_splits", "rq_decode_attention",
     "rq_decode_attention_ragged",
@@ -60,6 +60,14 @@ class Slot(ctypes.Structure):
                 ("bits", ctypes.c_int32), ("code_bytes", ctypes.c_int32)]
 
 
+class Layout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_uint64), ("layer_bytes", ctypes.c_uint64),
+                ("group_bytes", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64 * 2),
+                ("sz_offset", ctypes.c_uint64 * 2), ("alpha_offset", ctypes.c_uint64),
+                ("code_row_bytes", ctypes.c_int32 * 2), ("sz_row_bytes", ctypes.c_int32),
+                ("token_tile", ctypes.c_int32)]
+
+
 def make_desc(batch, loops, layers, kv_heads, max_tokens, head_dim, loops_per_group=4,
               anchor_bits=4, residual_bits=2, group_size=16, mode=MODE_RESIDUAL,
               alpha_mode=ALPHA_LS, rotation=ROT_HADAMARD) -> CacheDesc:
@@ -86,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.rq_validate_desc.argtypes = [D]
         L.rq_cache_bytes.argtypes = [D, ctypes.POINTER(ctypes.c_uint64)]
         L.rq_cache_slot.argtypes = [D, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Slot)]
+        L.rq_cache_layout.argtypes = [D, ctypes.POINTER(Layout)]
         L.rq_quantize_append.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _vp]
         L.rq_quantize_append_ragged.argtypes = [D, _vp, _vp, _vp, _i32, _vp, _vp]
         L.rq_reconstruct.argtypes = [D, _vp, _vp, _i32, _i32, _i32, _vp, _vp]
@@ -109,7 +118,8 @@ def lib() -> ctypes.CDLL:
                                                 _vp]
         L.rq_read_probe_sink_words.restype = ctypes.c_uint32
         L.rq_read_probe.argtypes = [_vp, _u64, _vp, _vp]
-        for name in ("rq_validate_desc", "rq_cache_bytes", "rq_cache_slot", "rq_quantize_append",
+        for name in ("rq_validate_desc", "rq_cache_bytes", "rq_cache_layout", "rq_cache_slot",
+                     "rq_quantize_append",
                      "rq_quantize_append_ragged", "rq_reconstruct", "rq_decode_attention",
                      "rq_decode_attention_ragged", "rq_bf16_decode_attention", "rq_read_probe",
                      "rq_paged_quantize_append", "rq_paged_decode_attention"):
@@ -159,6 +169,12 @@ def cache_bytes(desc: CacheDesc) -> int:
     n = ctypes.c_uint64()
     _check(lib().rq_cache_bytes(ctypes.byref(desc), ctypes.byref(n)), "rq_cache_bytes")
     return n.value
+
+
+def cache_layout(desc: CacheDesc) -> Layout:
+    out = Layout()
+    _check(lib().rq_cache_layout(ctypes.byref(desc), ctypes.byref(out)), "rq_cache_layout")
+    return out
 
 
 def cache_slot(desc: CacheDesc, kv: int, batch: int, layer: int, loop: int, head: int) -> Slot:

@@ -119,6 +119,36 @@ typedef struct rq_slot {
   int32_t code_bytes;    /* bytes per token in the codes sub-plane */
 } rq_slot;
 
+/* The whole byte layout of a cache for one descriptor, so a caller can
+ * address any slot without further calls (host only).  With P =
+ * loops_per_group, loop = k * P + j (group k, position j; j == P - 1 is the
+ * anchor) and kind = (j == P - 1 ? 0 : 1), the slot of (kv, batch row b,
+ * layer, loop, kv_head h) starts at
+ *     ((kv * batch + b) * layers + layer) * layer_bytes
+ *       + kv_heads * (k * group_bytes + j * slot_bytes[1])
+ *       + h * slot_bytes[kind]
+ * and its sub-planes at that offset + 0 (codes), + sz_offset[kind] (FP8
+ * scale/offset pairs) and + alpha_offset (BF16 alpha; non-anchor slots of
+ * RESIDUAL and CHAINED modes only).  Token t's rows are code_row_bytes[kind]
+ * and sz_row_bytes long, at t times those sizes from their sub-plane.
+ * total_bytes equals rq_cache_bytes().  token_tile is the decode kernels'
+ * wave tile in tokens (16 at head_dim 96 and 128, 32 at 64): the smallest
+ * block size a paged pool accepts.  (rq_cache_slot gives the same offsets
+ * for one slot.) */
+typedef struct rq_layout {
+  uint64_t total_bytes;
+  uint64_t layer_bytes;       /* one (kv, batch row, layer) block */
+  uint64_t group_bytes;       /* one loop group of one kv head */
+  uint64_t slot_bytes[2];     /* [0] anchor-position slots, [1] other slots */
+  uint64_t sz_offset[2];      /* sz sub-plane offset inside a slot of each kind */
+  uint64_t alpha_offset;      /* alpha sub-plane offset in a kind-1 slot, or UINT64_MAX */
+  int32_t code_row_bytes[2];  /* d * bits / 8 of each kind */
+  int32_t sz_row_bytes;       /* 2 * d / 16 */
+  int32_t token_tile;
+} rq_layout;
+
+rq_status rq_cache_layout(const rq_cache_desc* desc, rq_layout* out);
+
 /* Human-readable name of a status; never NULL. */
 const char* rq_status_string(rq_status s);
 

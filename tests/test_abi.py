@@ -68,6 +68,43 @@ def test_geometry_matches_documented_layout(desc):
         assert s.slot_bytes == g.slot_bytes(loop)
 
 
+@pytest.mark.parametrize("desc", DESCS, ids=lambda d: f"{d.head_dim}-{d.max_tokens}-{d.mode}")
+def test_cache_layout_addresses_every_slot(desc):
+    """rq_cache_layout's strides and sub-plane offsets, through the formula
+    the header states, give every slot rq_cache_slot gives."""
+    lay = rq.cache_layout(desc)
+    assert lay.total_bytes == rq.cache_bytes(desc)
+    P = desc.loops_per_group
+    assert lay.token_tile == (32 if desc.head_dim == 64 else 16)
+    assert lay.sz_row_bytes == 2 * desc.head_dim // 16
+    for kv in range(2):
+        for b in range(desc.batch):
+            for layer in range(desc.layers):
+                for loop in range(desc.loops):
+                    for h in range(desc.kv_heads):
+                        k, j = divmod(loop, P)
+                        kind = 0 if j == P - 1 else 1
+                        off = (((kv * desc.batch + b) * desc.layers + layer) * lay.layer_bytes
+                               + desc.kv_heads * (k * lay.group_bytes + j * lay.slot_bytes[1])
+                               + h * lay.slot_bytes[kind])
+                        s = rq.cache_slot(desc, kv, b, layer, loop, h)
+                        assert s.codes_offset == off
+                        assert s.sz_offset == off + lay.sz_offset[kind]
+                        want_alpha = off + lay.alpha_offset if (kind == 1 and lay.alpha_offset
+                                                                != 2 ** 64 - 1) else 2 ** 64 - 1
+                        assert s.alpha_offset == want_alpha
+                        assert s.slot_bytes == lay.slot_bytes[kind]
+                        assert s.code_bytes == lay.code_row_bytes[kind]
+
+
+def test_cache_layout_rejects_bad_arguments():
+    L = rq.lib()
+    bad = rq.make_desc(1, 4, 1, 2, 256, 80)
+    assert L.rq_cache_layout(ctypes.byref(bad), ctypes.byref(rq.Layout())) == 2
+    good = rq.make_desc(1, 4, 1, 2, 256, 64)
+    assert L.rq_cache_layout(ctypes.byref(good), None) == 1
+
+
 @pytest.mark.parametrize("mode,ab,rb", [(0, 4, 2), (1, 4, 2), (0, 4, 4), (0, 2, 2), (2, 4, 2)])
 @pytest.mark.parametrize("d", [64, 96, 128])
 def test_cache_bytes_equal_accounting(mode, ab, rb, d):
