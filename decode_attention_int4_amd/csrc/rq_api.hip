@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/rq.h"
 #include "rq_kernels.h"
@@ -392,6 +393,76 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache, cons
                               uint64_t workspace_bytes, float* out, void* stream) {
   return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, n_tokens, nullptr,
                                softmax_scale, workspace, workspace_bytes, out, stream, desc->batch,
+                               rq::Paging{});
+}
+
+}  // extern "C"
+
+// ---- rq_decode_attention_noalloc: the split-K workspace is this file-scope
+// device array (one per GPU, held until the process ends).  Its first
+// kCounterBytes are the split counters, which must start at zero; every call
+// leaves them at zero.  In host code `scratch` names a host-side stand-in:
+// only the address from hipGetSymbolAddress, kept per device, is passed to
+// kernels or copies.
+static constexpr uint64_t kScratchBytes = 2ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_zeroed[kMaxDevices];
+
+// The current device's scratch address; the first call on a device also
+// clears the counter block with a kernel on `stream` (ahead of the decode
+// kernel on the same stream).  Returns nullptr on a HIP error.
+void* scratch_for_current_device(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(g_scratch_ptr[dev]), (uint32_t)(kCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_zeroed[dev] = true;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+rq_status rq_decode_attention_noalloc(const rq_cache_desc* desc, const void* cache,
+                                      const int8_t* signs, int32_t loop, int32_t layer,
+                                      const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                                      float softmax_scale, float* out, void* stream) {
+  // the same argument checks as rq_decode_attention, and the size limit,
+  // before anything touches the device
+  rq_status st = check_desc(desc);
+  if (st != RQ_OK) return st;
+  if (q_heads <= 0 || n_tokens < 0) return RQ_ERR_INVALID_ARG;
+  if (q_heads % desc->kv_heads != 0) return RQ_ERR_UNSUPPORTED;
+  if ((int64_t)desc->batch * q_heads > kMaxRowHeads) return RQ_ERR_UNSUPPORTED;
+  if (loop < 0 || loop >= desc->loops || layer < 0 || layer >= desc->layers) return RQ_ERR_INVALID_ARG;
+  if (n_tokens > desc->max_tokens) return RQ_ERR_CAPACITY;
+  const uint64_t need = workspace_for(desc, desc->batch, q_heads, n_tokens);
+  if (need > kScratchBytes) return RQ_ERR_WORKSPACE;
+  if (!cache || !q_bf16 || !out || (needs_signs(desc) && !signs)) return RQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 256) || !aligned(q_bf16, 4) || !aligned(out, 4)) return RQ_ERR_ALIGNMENT;
+  if (!(softmax_scale == softmax_scale)) return RQ_ERR_INVALID_ARG;
+  void* ws = scratch_for_current_device(static_cast<hipStream_t>(stream));
+  if (!ws) return RQ_ERR_LAUNCH;
+  return decode_attention_impl(desc, cache, signs, loop, layer, q_bf16, q_heads, n_tokens, nullptr,
+                               softmax_scale, ws, kScratchBytes, out, stream, desc->batch,
                                rq::Paging{});
 }
 

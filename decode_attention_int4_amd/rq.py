@@ -31,6 +31,7 @@ EXPORTS = (
     "rq_status_string", "rq_validate_desc", "rq_cache_bytes", "rq_cache_layout", "rq_cache_slot",
     "rq_quantize_append", "rq_quantize_append_ragged", "rq_reconstruct",
     "rq_decode_workspace_bytes", "rq_decode_splits", "rq_decode_attention",
+    "rq_decode_attention_noalloc",
     "rq_decode_attention_ragged",
     "rq_bf16_decode_workspace_bytes", "rq_bf16_decode_attention",
     "rq_read_probe_sink_words", "rq_read_probe",
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.rq_decode_splits.restype = _i32
         L.rq_decode_attention.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
                                           ctypes.c_float, _vp, _u64, _vp, _vp]
+        L.rq_decode_attention_noalloc.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
+                                                  ctypes.c_float, _vp, _vp]
         L.rq_decode_attention_ragged.argtypes = [D, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                                                  ctypes.c_float, _vp, _u64, _vp, _vp]
         L.rq_bf16_decode_workspace_bytes.argtypes = [D, _i32, _i32]
@@ -121,6 +124,7 @@ def lib() -> ctypes.CDLL:
         for name in ("rq_validate_desc", "rq_cache_bytes", "rq_cache_layout", "rq_cache_slot",
                      "rq_quantize_append",
                      "rq_quantize_append_ragged", "rq_reconstruct", "rq_decode_attention",
+                     "rq_decode_attention_noalloc",
                      "rq_decode_attention_ragged", "rq_bf16_decode_attention", "rq_read_probe",
                      "rq_paged_quantize_append", "rq_paged_decode_attention"):
             getattr(L, name).restype = ctypes.c_int
@@ -280,6 +284,23 @@ def decode_attention(desc: CacheDesc, cache: torch.Tensor, signs: Optional[torch
         _dev(q, torch.bfloat16, "q"), q.shape[1], n_tokens, float(softmax_scale),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
         _dev(out, torch.float32, "out"), _stream(stream)), "rq_decode_attention")
+    return out
+
+
+def decode_attention_noalloc(desc: CacheDesc, cache: torch.Tensor, signs: Optional[torch.Tensor],
+                             loop: int, layer: int, q: torch.Tensor, n_tokens: int,
+                             softmax_scale: float, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """As decode_attention, with the split-K workspace inside the library."""
+    if q.dim() != 3 or q.shape[0] != desc.batch or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match {desc}")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    s = _dev(signs, torch.int8, "signs") if signs is not None else None
+    _check(lib().rq_decode_attention_noalloc(
+        ctypes.byref(desc), _dev(cache, torch.uint8, "cache"), s, loop, layer,
+        _dev(q, torch.bfloat16, "q"), q.shape[1], n_tokens, float(softmax_scale),
+        _dev(out, torch.float32, "out"), _stream(stream)), "rq_decode_attention_noalloc")
     return out
 
 

@@ -260,6 +260,28 @@ rq_status rq_decode_attention(const rq_cache_desc* desc, const void* cache,
                               float* out, void* stream);
 
 /*
+ * rq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split-K partial states and counters
+ * live in a 2 MiB array inside the library, one per GPU, held until the
+ * process ends; the call allocates nothing.  Arguments, results and errors are
+ * those of rq_decode_attention, plus RQ_ERR_WORKSPACE when the call would need
+ * more than that array (rq_decode_workspace_bytes(desc, q_heads, n_tokens) >
+ * 2 MiB: every per-head plan fits; grouped-query calls with many query heads
+ * per KV head over many rows may not), and RQ_ERR_LAUNCH if the array's
+ * address cannot be obtained.  The first call on a GPU also enqueues a small
+ * kernel on `stream` that clears the array's counters (make that first call
+ * outside graph capture if the captured graph should hold only the decode
+ * kernel).  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (different streams without ordering) race and give wrong
+ * results; calls ordered on one stream are fine.
+ */
+rq_status rq_decode_attention_noalloc(const rq_cache_desc* desc, const void* cache,
+                                      const int8_t* signs, int32_t loop, int32_t layer,
+                                      const uint16_t* q_bf16, int32_t q_heads, int32_t n_tokens,
+                                      float softmax_scale, float* out, void* stream);
+
+/*
  * Decode attention with a length per batch row: row b attends to tokens
  * [0, lengths[b]) of its slots; otherwise identical to rq_decode_attention.
  *   lengths       device int32 [batch], 4-byte aligned, read on the device and
