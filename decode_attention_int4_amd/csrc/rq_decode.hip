@@ -230,6 +230,57 @@ __device__ __forceinline__ void lds_pair(PairPlane<BITS>& pp, const lds_u8* code
   pp.sz1 = lds_u16(sz + rs);
 }
 
+// ------------------------------------------------------------ K side on MFMA
+// At head_dim 128 the logits of a wave tile (16 tokens) come from
+// v_mfma_f32_16x16x32_f16 with the roles A = query, B = codes, D[row][token]:
+// rows 0-7 are the anchor (first plane) groups, rows 8-15 the residual
+// groups.  Lane (token n = lane % 16, block kb = lane / 16) holds B for its
+// token: slab j (32 elements) takes 8 codes of group 2 kb + j / 2 as four
+// magic-number pairs -- for 4-bit codes all of dword j of the lane's 16
+// bytes, for 2-bit codes pairs 4 (j % 2) .. + 3 of dword j / 2 of its 8 bytes.
+// The query operand is block diagonal: lane (row i, block kb) holds, for slab
+// j, the fp16 pairs of group 2 kb + j / 2 when row i is that group's row (the
+// same pairs the per-pair dot products use, in the same order), else zeros.
+// The residual plane runs twice against the high and the low fp16 parts of
+// H q, both into its rows, so D holds each group's code dot product plus the
+// magic constant.  Lane (n, block rb) then owns rows 4 rb .. 4 rb + 3 of token
+// n and applies their scales, offsets and alpha.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int BITS, int J>
+__device__ __forceinline__ h8 kslab(const uint32_t* c, uint32_t magic) {
+  if constexpr (BITS == 4) {
+    const uint32_t d = c[J];
+    const u32x4 v = {and_or(d, Pairs<4>::mask(0), magic), and_or(d, Pairs<4>::mask(1), magic),
+                     and_or(d >> 8, Pairs<4>::mask(2), magic), and_or(d >> 8, Pairs<4>::mask(3), magic)};
+    return __builtin_bit_cast(h8, v);
+  } else {
+    const uint32_t d = c[J / 2];
+    constexpr int K0 = 4 * (J % 2);
+    const u32x4 v = {__builtin_bit_cast(uint32_t, pair_of<2, K0>(d, magic)),
+                     __builtin_bit_cast(uint32_t, pair_of<2, K0 + 1>(d, magic)),
+                     __builtin_bit_cast(uint32_t, pair_of<2, K0 + 2>(d, magic)),
+                     __builtin_bit_cast(uint32_t, pair_of<2, K0 + 3>(d, magic))};
+    return __builtin_bit_cast(h8, v);
+  }
+}
+
+// The lane's code dwords of one plane of token n: 16 bytes (4-bit codes) or
+// 8 bytes (2-bit codes), block kb of the token's row.
+template <int BITS>
+__device__ __forceinline__ void kcodes(const lds_u8* row, int kb, uint32_t* c) {
+  constexpr int W = BITS;  // dwords per lane at head_dim 128: 4 or 2
+  const lds_u8* p = row + kb * 4 * W;
+  if constexpr (W == 4) {
+    typedef __attribute__((address_space(3))) const u32x4 l4;
+    const u32x4 v = *reinterpret_cast<l4*>(p);
+    c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+  } else {
+    lds_codes<8>(p, c);
+  }
+}
+
 // ------------------------------------------------------------ query side
 // fp16 pairs matching the code pairs of one token's 16 codes (plane BITS),
 // plus the constant 1024 * sum(pair) that the magic exponent adds.
@@ -324,6 +375,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   constexpr bool TWO = B2 != 0;
   constexpr int B2E = TWO ? B2 : 2;
   constexpr int CB1 = 16 * B1 / 8, CB2 = 16 * B2E / 8;  // code bytes per lane and token
+  // logits on matrix cores (see kslab): head_dim 128 with at most one
+  // residual plane; chained loops reading several planes keep the dot2 path
+  constexpr bool KM = D == 128 && NR == 1;
   const Geometry& g = a.g;
 
   using ST = Stage<D, B1, B2, NR>;
@@ -551,6 +605,40 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const float qs = a.qscale;
   const h2 ones = (h2){(_Float16)1.f, (_Float16)1.f};
 
+  // K side on matrix cores: the block-diagonal query operands (slab j:
+  // anchor, residual high part, residual low part) and, for the lane's rows,
+  // the groups' magic constants and plain query sums
+  const int kn = lane & 15, kb = lane >> 4;
+  h8 Aq[4], Auh[4], Aul[4];
+  float koff[4], ksum[4];
+  const bool kres = TWO && kb >= 2;   // lane's rows are residual rows
+  if constexpr (KM) {
+    typedef __attribute__((address_space(3))) const u32x4 lq4k;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    static_for<4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int gj = 2 * kb + j / 2;
+      const lds_u8* row = (const lds_u8*)&spre[gj][0] + 16 * (j % 2);
+      const u32x4 q4 = *reinterpret_cast<lq4k*>(row);
+      Aq[j] = __builtin_bit_cast(h8, kn == gj ? q4 : zero4);
+      if constexpr (TWO) {
+        const u32x4 h4 = *reinterpret_cast<lq4k*>(row + 32), l4 = *reinterpret_cast<lq4k*>(row + 64);
+        Auh[j] = __builtin_bit_cast(h8, kn == 8 + gj ? h4 : zero4);
+        Aul[j] = __builtin_bit_cast(h8, kn == 8 + gj ? l4 : zero4);
+      }
+    });
+    // the row sums are in prescaled units (the dot products carry the
+    // query's power-of-two prescale, taken out once per row below), so the
+    // query sums that meet the offsets are prescaled too (exactly)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gr = 4 * (kb & 1) + r;
+      const bool live = TWO || kb < 2;
+      koff[r] = live ? __builtin_bit_cast(float, spre[gr][kres ? 25 : 24]) : 0.f;
+      ksum[r] = live ? __builtin_bit_cast(float, spre[gr][kres ? 27 : 26]) * (kres ? pu : pq) : 0.f;
+    }
+  }
+
   float accA[16], accR[TWO ? 16 : 1];
 #pragma unroll
   for (int i = 0; i < 16; ++i) accA[i] = 0.f;
@@ -586,64 +674,108 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     const int tt = t_begin + kcur * TPW + t0;
     const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
-    // keys now; the value planes are read after the softmax update, so their
-    // registers are not live across the logit computation
-    PairPlane<B1> k1;
-    lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
+    float lg0, lg1;
+    if constexpr (KM) {
+      // ---- logits on matrix cores: D[group row][token] for the 16 tokens
+      f4 dk = {0.f, 0.f, 0.f, 0.f};
+      uint32_t c1[B1];
+      kcodes<B1>(st + ST::k1c + kn * ST::R1, kb, c1);
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq[j], kslab<B1, j>(c1, magic), dk, 0, 0, 0);
+      });
+      const lds_u8* rs = st + ST::res(0);
+      if constexpr (TWO) {
+        uint32_t c2[B2E];
+        kcodes<B2E>(rs + ST::k2c + kn * ST::R2, kb, c2);
+        static_for<4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          const h8 b2 = kslab<B2E, j>(c2, magic);
+          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Auh[j], b2, dk, 0, 0, 0);
+          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aul[j], b2, dk, 0, 0, 0);
+        });
+      }
+      // the lane's four rows: scale times (dot - magic) plus offset times the
+      // query sum, then alpha for residual rows, summed over the four blocks
+      typedef __attribute__((address_space(3))) const u32x2 lq2;
+      const lds_u8* szp = (kres ? rs + ST::k2s : st + ST::k1s) + kn * ST::RS + 8 * (kb & 1);
+      const u32x2 szw = *reinterpret_cast<lq2*>(szp);
+      const f2 sz0 = sz_pair(szw.x), sz1 = __builtin_amdgcn_cvt_pk_f32_fp8(szw.x, true);
+      const f2 sz2 = sz_pair(szw.y), sz3 = __builtin_amdgcn_cvt_pk_f32_fp8(szw.y, true);
+      float kp = fmaf(sz0.x, dk[0] - koff[0], sz0.y * ksum[0]);
+      kp = fmaf(sz1.x, dk[1] - koff[1], fmaf(sz1.y, ksum[1], kp));
+      kp = fmaf(sz2.x, dk[2] - koff[2], fmaf(sz2.y, ksum[2], kp));
+      kp = fmaf(sz3.x, dk[3] - koff[3], fmaf(sz3.y, ksum[3], kp));
+      float kmul = ipq;
+      if constexpr (TWO) kmul = kres ? ipu * bf16_to_f32(lds_u16(rs + ST::ka + 4 * kn)) : ipq;
+      kp = (TWO || kb < 2) ? kp * kmul : 0.f;
+      kp = pair_add<32>(pair_add<16>(kp)) * qs;   // logit of token kn
+      // to the value side's layout: lane (pair pj, group e) takes tokens 2 pj, 2 pj + 1
+      const int kbits = __builtin_bit_cast(int, kp);
+      const float lk0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(8 * pj, kbits));
+      const float lk1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(8 * pj + 4, kbits));
+      lg0 = ok0 ? lk0 : kEmpty;
+      lg1 = ok1 ? lk1 : kEmpty;
+    } else {
+      // keys now; the value planes are read after the softmax update, so their
+      // registers are not live across the logit computation
+      PairPlane<B1> k1;
+      lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
 
-    // ---- logits of the pair
-    asm volatile("" ::: "memory");  // keep the pair reads inside the loop
-    QPairs<B1> qp;
-    QPairs<B2E> uh, ul;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const u32x4 x = prow[j];
-      qp.p[4 * j] = as_h2(x.x);
-      qp.p[4 * j + 1] = as_h2(x.y);
-      qp.p[4 * j + 2] = as_h2(x.z);
-      qp.p[4 * j + 3] = as_h2(x.w);
-    }
-    qp.off = qoff;
-    if constexpr (TWO) {
-#pragma unroll
+      // ---- logits of the pair
+      asm volatile("" ::: "memory");  // keep the pair reads inside the loop
+      QPairs<B1> qp;
+      QPairs<B2E> uh, ul;
+  #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4 x = prow[2 + j], y = prow[4 + j];
-        uh.p[4 * j] = as_h2(x.x);
-        uh.p[4 * j + 1] = as_h2(x.y);
-        uh.p[4 * j + 2] = as_h2(x.z);
-        uh.p[4 * j + 3] = as_h2(x.w);
-        ul.p[4 * j] = as_h2(y.x);
-        ul.p[4 * j + 1] = as_h2(y.y);
-        ul.p[4 * j + 2] = as_h2(y.z);
-        ul.p[4 * j + 3] = as_h2(y.w);
+        const u32x4 x = prow[j];
+        qp.p[4 * j] = as_h2(x.x);
+        qp.p[4 * j + 1] = as_h2(x.y);
+        qp.p[4 * j + 2] = as_h2(x.z);
+        qp.p[4 * j + 3] = as_h2(x.w);
       }
-      uh.off = uoff;
-      ul.off = 0.f;
-    }
-    float part0, part1;
-    {
-      f2 s0 = sz_pair(k1.sz0), s1 = sz_pair(k1.sz1);
-      if (!active) s0 = s1 = (f2){0.f, 0.f};
-      part0 = fmaf(s0.x * key_dot<B1>(k1.c0, qp, magic), ipq, s0.y * qsum);
-      part1 = fmaf(s1.x * key_dot<B1>(k1.c1, qp, magic), ipq, s1.y * qsum);
-    }
-    if constexpr (TWO) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const lds_u8* rs = st + ST::res(r);
-        PairPlane<B2E> k2;
-        lds_pair<B2E>(k2, rs + ST::k2c + o2c, rs + ST::k2s + osz, ST::R2, ST::RS);
-        const uint32_t ka0 = lds_u16(rs + ST::ka + oal), ka1 = lds_u16(rs + ST::ka + oal + 4);
-        f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
+      qp.off = qoff;
+      if constexpr (TWO) {
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 x = prow[2 + j], y = prow[4 + j];
+          uh.p[4 * j] = as_h2(x.x);
+          uh.p[4 * j + 1] = as_h2(x.y);
+          uh.p[4 * j + 2] = as_h2(x.z);
+          uh.p[4 * j + 3] = as_h2(x.w);
+          ul.p[4 * j] = as_h2(y.x);
+          ul.p[4 * j + 1] = as_h2(y.y);
+          ul.p[4 * j + 2] = as_h2(y.z);
+          ul.p[4 * j + 3] = as_h2(y.w);
+        }
+        uh.off = uoff;
+        ul.off = 0.f;
+      }
+      float part0, part1;
+      {
+        f2 s0 = sz_pair(k1.sz0), s1 = sz_pair(k1.sz1);
         if (!active) s0 = s1 = (f2){0.f, 0.f};
-        const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
-        const float r1 = fmaf(s1.x * key_dot2<B2E>(k2.c1, uh, ul, magic), ipu, s1.y * usum);
-        part0 = fmaf(bf16_to_f32(ka0), r0, part0);
-        part1 = fmaf(bf16_to_f32(ka1), r1, part1);
+        part0 = fmaf(s0.x * key_dot<B1>(k1.c0, qp, magic), ipq, s0.y * qsum);
+        part1 = fmaf(s1.x * key_dot<B1>(k1.c1, qp, magic), ipq, s1.y * qsum);
       }
+      if constexpr (TWO) {
+  #pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const lds_u8* rs = st + ST::res(r);
+          PairPlane<B2E> k2;
+          lds_pair<B2E>(k2, rs + ST::k2c + o2c, rs + ST::k2s + osz, ST::R2, ST::RS);
+          const uint32_t ka0 = lds_u16(rs + ST::ka + oal), ka1 = lds_u16(rs + ST::ka + oal + 4);
+          f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
+          if (!active) s0 = s1 = (f2){0.f, 0.f};
+          const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
+          const float r1 = fmaf(s1.x * key_dot2<B2E>(k2.c1, uh, ul, magic), ipu, s1.y * usum);
+          part0 = fmaf(bf16_to_f32(ka0), r0, part0);
+          part1 = fmaf(bf16_to_f32(ka1), r1, part1);
+        }
+      }
+      lg0 = ok0 ? pair_sum<LPP>(part0) * qs : kEmpty;
+      lg1 = ok1 ? pair_sum<LPP>(part1) * qs : kEmpty;
     }
-    const float lg0 = ok0 ? pair_sum<LPP>(part0) * qs : kEmpty;
-    const float lg1 = ok1 ? pair_sum<LPP>(part1) * qs : kEmpty;
 
     // ---- online softmax
     const float mx = fmaxf(lg0, lg1);
