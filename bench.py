@@ -58,6 +58,20 @@ def traffic_from_profile(config: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def trace_from_profile(config: str):
+    """The dominant kernel's average dispatch duration in the committed
+    rocprofv3 kernel trace of this benchmark (profiles/), or None when missing
+    or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"decode_{config}_kernel_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != src_sha():
+        return None
+    return t.get("dominant_avg_us")
+
+
 def time_steps(step, steps: int, torch):
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -97,6 +111,36 @@ def dominant_calls(run):
             if (loop % P != P - 1) == (w.mode != 1)]
 
 
+def kernel_name(w) -> str:
+    """The dominant call's kernel as the profiler names it."""
+    two = w.mode != 1
+    if w.q_heads > w.kv_heads:
+        return (f"gqa_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
+                f"{str(w.page_tokens > 0).lower()}>")
+    # waves per workgroup: 8 at d = 128 (residual calls, and anchor calls on
+    # a contiguous cache) unless a chained loop reads several residual planes
+    # (then 4), else 4
+    waves = 8 if (w.head_dim == 128 and (w.page_tokens == 0 or two)) else 4
+    return (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
+            f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()},"
+            f"{'W' if w.mode == 2 and waves == 8 else waves}>")
+
+
+def dominant_roofline(run, steps: int, torch, use_graph: bool) -> dict:
+    """Roofline figures of a workload's dominant decode call: algorithmic
+    bytes per launch over the event-timed average launch (see
+    dominant_kernel_ms)."""
+    dom_ms, n_launch = dominant_kernel_ms(run, steps, torch, use_graph)
+    calls = dominant_calls(run)
+    # bytes per dominant call (chained mode: the calls read 1 to P-1 residual planes)
+    dom_bytes = sum(run.call_bytes(loop) for loop, _ in calls) // len(calls)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": kernel_name(run.w),
+            "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+            "launches_timed": n_launch}
+
+
 def dominant_kernel_ms(run, steps: int, torch, use_graph: bool):
     """Average duration of one dominant call (one decode kernel launch, which
     also merges its splits), from events on the stream the kernel runs on
@@ -114,7 +158,10 @@ def dominant_kernel_ms(run, steps: int, torch, use_graph: bool):
     return ms / len(calls), steps * len(calls)
 
 
-def read_peak_gbps(torch, rq, nbytes=8 << 30, reps=5):
+def read_peak(torch, rq, call_bytes: int, nbytes=8 << 30, reps=5):
+    """The library's streaming-read probe: GB/s over one 8 GiB read, and the
+    time to read `call_bytes` per launch in back-to-back launches over
+    distinct parts of the buffer (the floor for a decode call of that size)."""
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(7)
     sink = torch.zeros(rq.read_probe_sink_words(), dtype=torch.int32, device="cuda")
@@ -126,15 +173,38 @@ def read_peak_gbps(torch, rq, nbytes=8 << 30, reps=5):
         rq.read_probe(buf, sink)
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    del buf
-    return nbytes / (ms * 1e-3) / 1e9
+    gbps = nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9
+    words = call_bytes // 16 * 4                     # int32 words, 16-byte multiple
+    parts = [buf[i * words:(i + 1) * words] for i in range(min(40, buf.numel() // words))]
+    for p in parts:
+        rq.read_probe(p, sink)
+    torch.cuda.synchronize()
+    s.record()
+    for p in parts:
+        rq.read_probe(p, sink)
+    e.record()
+    torch.cuda.synchronize()
+    call_us = s.elapsed_time(e) / len(parts) * 1e3
+    del buf, parts
+    torch.cuda.empty_cache()
+    return gbps, call_us
+
+
+def cpu_threads():
+    """Host cores this process may run on, and the threads the oracle uses:
+    all of them, up to 16 (the CPU share a one-GPU machine gives a job)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return usable, max(1, min(16, usable))
 
 
 def cpu_baseline(run, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same step:
     attention calls of sampled (batch row, layer, head) slices for every loop,
-    plus encoding of sampled new-token loop groups; extrapolated to one full
+    plus encoding of sampled new-token loop groups, both spread over the host
+    threads (the oracle's C calls release the GIL); extrapolated to one full
     step (every loop x layer x batch row x head, and the whole append)."""
     import numpy as np
 
@@ -142,7 +212,7 @@ def cpu_baseline(run, budget_s: float = 12.0):
     from decode_attention_int4_amd.synth import rotation_signs
 
     w = run.w
-    cores = min(16, os.cpu_count() or 1)
+    usable, cores = cpu_threads()
     p = O.Params(d=w.head_dim, P=w.loops_per_group, anchor_bits=w.anchor_bits,
                  residual_bits=w.residual_bits, mode=w.mode, alpha_mode=w.alpha_mode,
                  rotate=1 if (w.rotation == 1 and w.mode != 1) else 0)
@@ -158,21 +228,12 @@ def cpu_baseline(run, budget_s: float = 12.0):
         encs.append((key, O.encode_slice(p, bits(kept[0]), HK), O.encode_slice(p, bits(kept[1]), HV),
                      HK, HV))
     jobs = [(e, loop) for e in encs for loop in range(w.loops)]
+    qbits = {(e[0], loop): bits(run.q[loop, e[0][1], e[0][0], e[0][2]]) for e, loop in jobs}
 
     def attn(job):
         (key, ek, ev, HK, HV), loop = job
-        b, layer, head = key
-        return O.attention_slice(p, ek, ev, HK, HV, bits(run.q[loop, layer, b, head]), loop,
-                                 run.N, w.softmax_scale)
-
-    n_calls = 0
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
-        while time.perf_counter() - t0 < budget_s * 0.8:
-            list(ex.map(attn, jobs * max(1, cores // len(jobs))))
-            n_calls += len(jobs) * max(1, cores // len(jobs))
-    t_attn = time.perf_counter() - t0
-    calls_per_s = n_calls / t_attn
+        return O.attention_slice(p, ek, ev, HK, HV, qbits[(key, loop)], loop, run.N,
+                                 w.softmax_scale)
 
     # append: encode new-token loop groups (one per kv, batch row, layer, head, group)
     new = run.new_kv  # [2, B, loops, layers, H, 1, d]
@@ -180,16 +241,23 @@ def cpu_baseline(run, budget_s: float = 12.0):
               for layer in range(w.layers) for head in range(w.kv_heads)
               for k in range(w.loops // w.loops_per_group)]
     rng = np.random.default_rng(0)
-    sample = [groups[i] for i in rng.choice(len(groups), size=min(256, len(groups)), replace=False)]
-    Hs = {}
-    t1 = time.perf_counter()
-    for kv, b, layer, head, k in sample:
-        if (kv, layer) not in Hs:
-            Hs[(kv, layer)] = signs[kv, layer].copy()
-        P = w.loops_per_group
-        x = O.bf16_decode(bits(new[kv, b, k * P:(k + 1) * P, layer, head, 0]))
-        O.encode_group(p, x, Hs[(kv, layer)])
-    t_enc = (time.perf_counter() - t1) / len(sample)
+    sample = [groups[i] for i in rng.choice(len(groups), size=min(1024, len(groups)), replace=False)]
+    P = w.loops_per_group
+    xs = [(O.bf16_decode(bits(new[kv, b, k * P:(k + 1) * P, layer, head, 0])), signs[kv, layer].copy())
+          for kv, b, layer, head, k in sample]
+
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        n_calls = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s * 0.8:
+            reps = max(1, cores // len(jobs))
+            list(ex.map(attn, jobs * reps))
+            n_calls += len(jobs) * reps
+        t_attn = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        list(ex.map(lambda xh: O.encode_group(p, xh[0], xh[1]), xs))
+        t_enc = (time.perf_counter() - t1) / len(xs)     # wall time per encode, all threads
+    calls_per_s = n_calls / t_attn
 
     step_calls = w.loops * w.layers * w.batch * w.q_heads
     step_s = step_calls / calls_per_s + t_enc * len(groups)
@@ -197,11 +265,12 @@ def cpu_baseline(run, budget_s: float = 12.0):
         "value": w.batch / step_s,
         "unit": "tokens/s",
         "cores": cores,
+        "host_cores": usable,
         "kind": "oracle",
         "sample": (f"{n_calls} fp64 attention calls (n={run.N}) on {len(encs)} sampled "
-                   f"(batch,layer,head) slices x {w.loops} loops with {cores} threads "
-                   f"({calls_per_s:.1f} calls/s) + {len(sample)} new-token loop-group encodes "
-                   f"({t_enc * 1e3:.2f} ms each, 1 thread); extrapolated to {step_calls} calls "
+                   f"(batch,layer,head) slices x {w.loops} loops ({calls_per_s:.1f} calls/s) + "
+                   f"{len(xs)} new-token loop-group encodes ({t_enc * 1e6:.1f} us wall each), on "
+                   f"{cores} threads of {usable} host cores; extrapolated to {step_calls} calls "
                    f"and {len(groups)} encodes per step = {step_s:.1f} s/step"),
     }
 
@@ -361,6 +430,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--also", default="ouro16k_b4",
+                    help="comma-separated workloads whose dominant decode call is also timed "
+                         "(roofline only; empty to skip)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph of the step")
     ap.add_argument("--sweep", action="store_true",
@@ -426,32 +498,40 @@ def main():
     step_bytes = run.step_bytes()
     log(f"[bench] {ms:.3f} ms/step, {tok_s:.1f} tokens/s, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
 
-    dom_ms, n_launch = dominant_kernel_ms(run, args.steps, torch, use_graph)
-    calls = dominant_calls(run)
-    # bytes per dominant call (chained mode: the calls read 1 to P-1 residual planes)
-    dom_bytes = sum(run.call_bytes(loop) for loop, _ in calls) // len(calls)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    two = w.mode != 1
-    if w.q_heads > w.kv_heads:
-        kname = (f"gqa_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
-                 f"{str(w.page_tokens > 0).lower()}>")
-    else:
-        # waves per workgroup: 8 at d = 128 (residual calls, and anchor calls on
-        # a contiguous cache) unless a chained loop reads several residual
-        # planes (then 4), else 4
-        waves = 8 if (w.head_dim == 128 and (w.page_tokens == 0 or two)) else 4
-        kname = (f"decode_kernel<{w.head_dim},{w.anchor_bits},{w.residual_bits if two else 0},"
-                 f"{'NR' if w.mode == 2 else 1},{str(w.page_tokens > 0).lower()},"
-                 f"{'W' if w.mode == 2 and waves == 8 else waves}>")
-    log(f"[bench] dominant call ({kname}): {dom_ms * 1e3:.1f} us/launch over {n_launch} launches, "
-        f"{achieved:.0f} GB/s")
+    roof = dominant_roofline(run, args.steps, torch, use_graph)
+    achieved, dom_bytes = roof["achieved"], roof["algorithmic_bytes_per_launch"]
+    log(f"[bench] dominant call ({roof['kernel']}): {roof['avg_launch_us']} us/launch over "
+        f"{roof['launches_timed']} launches, {achieved:.0f} GB/s, {roof['frac']:.3f} of 8 TB/s")
+    trace_us = trace_from_profile(args.config)
+    if trace_us:
+        roof["trace_avg_launch_us"] = trace_us
+        roof["trace_frac"] = round(dom_bytes / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
 
     extra = {}
     if not args.no_probe:
-        peak = read_peak_gbps(torch, rq)
+        peak, call_us = read_peak(torch, rq, dom_bytes)
         extra["measured_read_peak_gbps"] = round(peak, 1)
         extra["frac_of_measured_read_peak"] = round(achieved / peak, 4)
-        log(f"[bench] streaming-read probe: {peak:.0f} GB/s")
+        extra["read_probe"] = {"gbps_8gib": round(peak, 1), "call_bytes": dom_bytes,
+                               "us_per_call_bytes": round(call_us, 2),
+                               "gbps_call_bytes": round(dom_bytes / (call_us * 1e-6) / 1e9, 1)}
+        log(f"[bench] streaming-read probe: {peak:.0f} GB/s over 8 GiB; one call's "
+            f"{dom_bytes / 1e6:.0f} MB in {call_us:.1f} us per launch")
+
+    others = [o for o in args.also.split(",") if o and o != args.config]
+    if others:
+        extra["roofline_other_workloads"] = {}
+    for name in others:
+        ow = WORKLOADS[name]
+        orun = RQDecode(ow)
+        for _ in range(args.warmup):
+            orun.step()
+        oroof = dominant_roofline(orun, args.steps, torch, use_graph)
+        extra["roofline_other_workloads"][name] = oroof
+        log(f"[bench] {name} dominant call ({oroof['kernel']}): {oroof['avg_launch_us']} us/launch, "
+            f"{oroof['achieved']:.0f} GB/s, {oroof['frac']:.3f} of 8 TB/s")
+        del orun
+        torch.cuda.empty_cache()
 
     if not args.no_bf16:
         base = BF16Decode(w)
@@ -498,11 +578,7 @@ def main():
                    "launch": "hip graph of one step" if use_graph else "eager"},
         "hbm_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": kname,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "roofline": {**roof, "traffic": traffic},
         "cpu_baseline": cpu,
         **extra,
     }

@@ -83,7 +83,7 @@ struct Bf16DecodeArgs {
 };
 hipError_t launch_bf16_decode(const Bf16DecodeArgs& a, hipStream_t s);
 
-constexpr uint32_t kProbeBlocks = 2048;
+constexpr uint32_t kProbeBlocks = 1024;
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 
 // Split-K partition shared by workspace sizing and the launch.

@@ -107,19 +107,33 @@ __global__ void __launch_bounds__(256) reconstruct_kernel(ReconArgs a) {
   }
 }
 
+// Streaming-read probe: each workgroup reads one contiguous chunk of the
+// buffer with non-temporal 16-byte loads, eight in flight per thread, and
+// writes the XOR of its words to sink[blockIdx.x] (the XOR keeps the loads).
+// Of the patterns measured on MI355X (grid-stride and chunked global loads,
+// LDS-DMA rings, 256-2048 workgroups, 2-16 loads in flight, with and without
+// the non-temporal hint), this one read fastest: about 7.0 TB/s over 8 GiB,
+// and 6.4-6.5 TB/s for one decode call's 136 MB per launch.
 __global__ void __launch_bounds__(256) read_probe_kernel(const uint4* buf, uint64_t n16, uint32_t* sink) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  constexpr int U = 8;
   uint32_t x = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = buf[i];
-    const uint4 b = buf[i + stride];
-    const uint4 c = buf[i + 2 * stride];
-    const uint4 d = buf[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t b0 = (uint64_t)blockIdx.x * per;
+  const uint64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  uint64_t i = b0 + threadIdx.x;
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    u4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(buf + i + u * 256));
+    // all U loads issue before any result is used (left alone, the scheduler
+    // interleaved the XORs and kept one or two loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = buf[i];
+  for (; i < b1; i += 256) {
+    const u4 a = __builtin_nontemporal_load(reinterpret_cast<const u4*>(buf + i));
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);

@@ -376,9 +376,11 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
 
 /*
  * Streaming-read probe: reads `bytes` bytes (a multiple of 16, 16-byte
- * aligned) once with 16-byte loads and writes an XOR of all of them per
- * workgroup into `sink` (device, rq_read_probe_sink_words() uint32 words).
- * Used to measure attainable HBM read bandwidth.
+ * aligned) once with non-temporal 16-byte loads, one contiguous chunk per
+ * workgroup, and writes an XOR of each workgroup's words into `sink` (device,
+ * rq_read_probe_sink_words() uint32 words).  Measures attainable HBM read
+ * bandwidth: it was the fastest of the read patterns tried, so the decode
+ * kernels' rates are reported against it.
  */
 uint32_t rq_read_probe_sink_words(void);
 rq_status rq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
