@@ -93,9 +93,12 @@ def attention_errors(gpu: np.ndarray, ref: np.ndarray):
     return rel, np.abs(gpu - ref).max()
 
 
-def assert_close_attention(gpu, ref, what):
+def assert_close_attention(gpu, ref, what, scale=1.0):
+    """rel-L2 <= 1e-3 and max-abs <= 2e-3 * scale.  The max-abs bound is for
+    outputs of unit scale; a caller whose outputs are far larger (hand-built
+    inputs of magnitude ~10^3) passes scale = max|ref|."""
     rel, mx = attention_errors(np.asarray(gpu, np.float64), ref)
-    assert rel <= REL_L2 and mx <= MAX_ABS, f"{what}: rel-L2 {rel:.3e}, max-abs {mx:.3e}"
+    assert rel <= REL_L2 and mx <= MAX_ABS * scale, f"{what}: rel-L2 {rel:.3e}, max-abs {mx:.3e}"
     return rel, mx
 
 

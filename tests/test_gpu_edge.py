@@ -1,6 +1,7 @@
 """GPU parity on the quantizer's degenerate groups, through the C ABI: codes,
 FP8 bytes and alphas bit for bit against the oracle, and decode attention
-within 1e-3 relative L2 / 2e-3 max-abs.  The inputs are built by hand (seeded),
+within 1e-3 relative L2 and 2e-3 max-abs relative to max(1, max|output|) (the
+saturating tokens make outputs of magnitude ~10^3).  The inputs are built by hand (seeded),
 16 tokens per kind, every loop group of every slice:
 
   * on-grid anchors with every other loop equal to the anchor: the anchor
@@ -118,5 +119,8 @@ def test_edge_groups(d):
                 out = rq.decode_attention(desc, cache, signs, loop, 0, q[loop], T, w.softmax_scale,
                                           ws).cpu().numpy()
                 ref = oracle_attention(w, ek, ev, HK, HV, bits16(q[loop, b, h]), loop, T)
-                assert_close_attention(out[b, h], ref, f"{w.name} row {b} head {h} loop {loop}")
+                # outputs of the saturating tokens are ~10^3: max-abs is taken
+                # relative to the output scale there
+                assert_close_attention(out[b, h], ref, f"{w.name} row {b} head {h} loop {loop}",
+                                       scale=max(1.0, float(np.abs(ref).max())))
     say(f"[edge] d={d}: planes bit-exact, attention within bounds on all degenerate kinds")
