@@ -31,34 +31,23 @@ __device__ __forceinline__ double fp8_to_f64(uint32_t b) { return (double)fp8_to
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // ---------------------------------------------------------------- encoding
-// Rounds |x| (a double) to FP8 e4m3fn with round-half-even on the discarded
-// mantissa bits.
+// Rounds x (a double) to FP8 e4m3fn, half to even, without branches: with e
+// the exponent of |x| clamped below at -6 (the subnormal range shares the
+// quantum 2^-9 of exponent -6), k = rint(|x| * 2^(3-e)) is the mantissa
+// (8..16 for normals, 0..8 below) and the code is (e + 7) * 8 + k - 8; k = 16
+// carries into the next exponent by that same formula.  |x| >= 448
+// saturates to 0x7E, NaN gives 0x7F, the sign bit is x's.
 __device__ __forceinline__ uint32_t f64_to_fp8(double x) {
-  const uint64_t bits = (uint64_t)__double_as_longlong(x);
-  const uint32_t sign = (uint32_t)(bits >> 63) << 7;
-  const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
-  const double a = __longlong_as_double((long long)mag);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.0) return sign | 0x7Eu;
-  const int e = (int)(mag >> 52) - 1023;
-  if (e < -6) {
-    // Subnormal range: a value k * 2^-9 with k = round-half-even(a * 2^9);
-    // k == 8 is exactly the smallest normal, whose code is also 8.
-    const double k = rint(a * 512.0);
-    return sign | (uint32_t)k;
-  }
-  const uint64_t frac = mag & 0x000FFFFFFFFFFFFFull;
-  uint32_t q = (uint32_t)(frac >> 49);                 // top 3 mantissa bits
-  const uint64_t rest = frac & ((1ull << 49) - 1);
-  const uint64_t half = 1ull << 48;
-  if (rest > half || (rest == half && (q & 1u))) ++q;
-  int E = e;
-  if (q == 8u) {
-    q = 0;
-    ++E;
-  }
-  if (E > 8 || (E == 8 && q == 7u)) return sign | 0x7Eu;
-  return sign | ((uint32_t)(E + 7) << 3) | q;
+  const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(x) >> 32);
+  const uint32_t sign = (hi >> 31) << 7;
+  const double a = fabs(x);
+  const int e = (int)((hi >> 20) & 0x7FFu) - 1023;
+  const int eq = e > -6 ? e : -6;
+  const double k = rint(ldexp(a, 3 - eq));
+  uint32_t code = (uint32_t)(((eq + 7) << 3) + (int)k - 8);
+  code = a >= 448.0 ? 0x7Eu : code;
+  code = a != a ? 0x7Fu : code;
+  return sign | code;
 }
 
 __device__ __forceinline__ uint32_t f64_to_bf16(double x) {

@@ -12,6 +12,9 @@ saturating tokens make outputs of magnitude ~10^3).  The inputs are built by han
   * values around +-1000: FP8 offsets saturate at -448 and residual scales at
     448, codes clamp;
   * BF16 subnormal inputs (|x| < 2^-126): FP8 rounds them to (signed) zero;
+  * groups whose minimum (or maximum) is a zero of either sign, some of them
+    all zeros: the FP8 offset takes the sign of the first zero in index
+    order, as the definition's scan does;
   * ordinary values, as a control.
 (ai4snews summary, paragraph 2: FP8 scales and offsets per group of 16.)"""
 import numpy as np
@@ -28,7 +31,8 @@ from tests.layout_decode import Geom, decode_slice
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("on_grid_equal", "constant", "tiny_residual", "saturating", "bf16_subnormal", "normal")
+KINDS = ("on_grid_equal", "constant", "tiny_residual", "saturating", "bf16_subnormal",
+         "signed_zeros", "normal")
 
 
 def _fp8_values():
@@ -73,6 +77,15 @@ def edge_states(rng, P, d, T):
             x[P - 1, sl] = a
         elif kind == "bf16_subnormal":
             x[:, sl] = rng.normal(size=(P, n, d)) * 2.0 ** -130
+        elif kind == "signed_zeros":
+            # zeros of random sign; half the tokens also carry values of one
+            # sign, so a zero is the group's minimum or maximum
+            z = np.where(rng.random(size=(n, d)) < 0.5, 0.0, -0.0)
+            v = np.abs(rng.normal(size=(n, d))) * (rng.random(size=(n, d)) < 0.5)
+            v = v * np.where(rng.random(size=(n, 1)) < 0.5, 1.0, -1.0)
+            a = np.where(v != 0, v, z)
+            a[: n // 2] = z[: n // 2]
+            x[:, sl] = a[None]
         else:
             a = rng.normal(size=(n, d))
             x[:, sl] = a[None] + 0.2 * rng.normal(size=(P, n, d))
@@ -115,6 +128,7 @@ def test_edge_groups(d):
             assert np.any(ek.s8[:P - 1] == 0) and np.any(ek.alpha[:P - 1] == 0)
             assert np.any((ek.s8 > 0) & (ek.s8 < 8)), "no FP8 subnormal scale"
             assert np.any(ek.z8 == 0xFE) and np.any(ek.s8 == 0x7E), "no saturated offset / scale"
+            assert np.any(ek.z8[P - 1] == 0x80), "no negative-zero anchor offset"
             for loop in range(w.loops):
                 out = rq.decode_attention(desc, cache, signs, loop, 0, q[loop], T, w.softmax_scale,
                                           ws).cpu().numpy()
