@@ -375,9 +375,13 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   constexpr bool TWO = B2 != 0;
   constexpr int B2E = TWO ? B2 : 2;
   constexpr int CB1 = 16 * B1 / 8, CB2 = 16 * B2E / 8;  // code bytes per lane and token
-  // logits on matrix cores (see kslab): head_dim 128 with at most one
-  // residual plane; chained loops reading several planes keep the dot2 path
-  constexpr bool KM = D == 128 && NR == 1;
+  // logits on matrix cores (see kslab): head_dim 128 and 96 with at most one
+  // residual plane; chained loops reading several planes keep the dot2 path.
+  // At 96 the rows of groups 6 and 7 (and 14, 15) are empty: their query
+  // rows are zero and their scale / offset terms are dropped, and the code
+  // slab of lane block 3 reads the next bytes of the staged tile (finite
+  // codes that meet only zero query entries)
+  constexpr bool KM = (D == 128 || D == 96) && NR == 1;
   const Geometry& g = a.g;
 
   using ST = Stage<D, B1, B2, NR>;
@@ -577,16 +581,17 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     qsum = pair_sum<8>(qsum);
     offu = pair_sum<8>(offu);
     usum = pair_sum<8>(usum);
-    if (g8 < NG) {
-      spre[g8][k] = __builtin_bit_cast(uint32_t, (h2){ha, hb});
-      spre[g8][8 + k] = uhw;
-      spre[g8][16 + k] = ulw;
-      if (k == 0) {
-        spre[g8][24] = __builtin_bit_cast(uint32_t, offq);
-        spre[g8][25] = __builtin_bit_cast(uint32_t, offu);
-        spre[g8][26] = __builtin_bit_cast(uint32_t, qsum);
-        spre[g8][27] = __builtin_bit_cast(uint32_t, usum);
-      }
+    // rows of groups past NG (d = 96) are zero: the matrix-core logits read
+    // them as empty query rows
+    const bool gv = g8 < NG;
+    spre[g8][k] = gv ? __builtin_bit_cast(uint32_t, (h2){ha, hb}) : 0u;
+    spre[g8][8 + k] = gv ? uhw : 0u;
+    spre[g8][16 + k] = gv ? ulw : 0u;
+    if (k == 0) {
+      spre[g8][24] = gv ? __builtin_bit_cast(uint32_t, offq) : 0u;
+      spre[g8][25] = gv ? __builtin_bit_cast(uint32_t, offu) : 0u;
+      spre[g8][26] = gv ? __builtin_bit_cast(uint32_t, qsum) : 0u;
+      spre[g8][27] = gv ? __builtin_bit_cast(uint32_t, usum) : 0u;
     }
   }
   __syncthreads();
@@ -614,17 +619,16 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const bool kres = TWO && kb >= 2;   // lane's rows are residual rows
   if constexpr (KM) {
     typedef __attribute__((address_space(3))) const u32x4 lq4k;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     static_for<4>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      const int gj = 2 * kb + j / 2;
+      const int gj = 2 * kb + j / 2;   // rows of groups past NG are zero in spre
       const lds_u8* row = (const lds_u8*)&spre[gj][0] + 16 * (j % 2);
-      const u32x4 q4 = *reinterpret_cast<lq4k*>(row);
-      Aq[j] = __builtin_bit_cast(h8, kn == gj ? q4 : zero4);
+      // lane kn holds row kn: its query entries where it is group gj's row
+      const uint32_t mq = kn == gj ? ~0u : 0u, mu = kn == 8 + gj ? ~0u : 0u;
+      Aq[j] = __builtin_bit_cast(h8, *reinterpret_cast<lq4k*>(row) & mq);
       if constexpr (TWO) {
-        const u32x4 h4 = *reinterpret_cast<lq4k*>(row + 32), l4 = *reinterpret_cast<lq4k*>(row + 64);
-        Auh[j] = __builtin_bit_cast(h8, kn == 8 + gj ? h4 : zero4);
-        Aul[j] = __builtin_bit_cast(h8, kn == 8 + gj ? l4 : zero4);
+        Auh[j] = __builtin_bit_cast(h8, *reinterpret_cast<lq4k*>(row + 32) & mu);
+        Aul[j] = __builtin_bit_cast(h8, *reinterpret_cast<lq4k*>(row + 64) & mu);
       }
     });
     // the row sums are in prescaled units (the dot products carry the
@@ -633,7 +637,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int gr = 4 * (kb & 1) + r;
-      const bool live = TWO || kb < 2;
+      const bool live = (TWO || kb < 2) && gr < NG;
       koff[r] = live ? __builtin_bit_cast(float, spre[gr][kres ? 25 : 24]) : 0.f;
       ksum[r] = live ? __builtin_bit_cast(float, spre[gr][kres ? 27 : 26]) * (kres ? pu : pq) : 0.f;
     }
@@ -677,29 +681,44 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     float lg0, lg1;
     if constexpr (KM) {
       // ---- logits on matrix cores: D[group row][token] for the 16 tokens
+      // Every code operand gets registers of its own that stay live until the
+      // logits are formed: with operands rebuilt in place, a register was
+      // rewritten one instruction after the matrix op reading it (head_dim 96,
+      // 2-bit planes), and that op's sums came out wrong
       f4 dk = {0.f, 0.f, 0.f, 0.f};
       uint32_t c1[B1];
       kcodes<B1>(st + ST::k1c + kn * ST::R1, kb, c1);
-      static_for<4>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq[j], kslab<B1, j>(c1, magic), dk, 0, 0, 0);
-      });
+      h8 kb1[4], kb2[4];
+      static_for<4>([&](auto J) { kb1[decltype(J)::value] = kslab<B1, decltype(J)::value>(c1, magic); });
       const lds_u8* rs = st + ST::res(0);
       if constexpr (TWO) {
         uint32_t c2[B2E];
         kcodes<B2E>(rs + ST::k2c + kn * ST::R2, kb, c2);
+        static_for<4>([&](auto J) { kb2[decltype(J)::value] = kslab<B2E, decltype(J)::value>(c2, magic); });
+      }
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq[j], kb1[j], dk, 0, 0, 0);
+      });
+      if constexpr (TWO) {
         static_for<4>([&](auto J) {
           constexpr int j = decltype(J)::value;
-          const h8 b2 = kslab<B2E, j>(c2, magic);
-          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Auh[j], b2, dk, 0, 0, 0);
-          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aul[j], b2, dk, 0, 0, 0);
+          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Auh[j], kb2[j], dk, 0, 0, 0);
+          dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aul[j], kb2[j], dk, 0, 0, 0);
         });
       }
       // the lane's four rows: scale times (dot - magic) plus offset times the
       // query sum, then alpha for residual rows, summed over the four blocks
       typedef __attribute__((address_space(3))) const u32x2 lq2;
       const lds_u8* szp = (kres ? rs + ST::k2s : st + ST::k1s) + kn * ST::RS + 8 * (kb & 1);
-      const u32x2 szw = *reinterpret_cast<lq2*>(szp);
+      u32x2 szw;
+      if constexpr (D == 128) {
+        szw = *reinterpret_cast<lq2*>(szp);
+      } else {
+        // 12-byte rows: dword reads; groups 6 and 7 do not exist
+        szw.x = lds_u32(szp);
+        szw.y = (kb & 1) ? 0u : lds_u32(szp + 4);
+      }
       const f2 sz0 = sz_pair(szw.x), sz1 = __builtin_amdgcn_cvt_pk_f32_fp8(szw.x, true);
       const f2 sz2 = sz_pair(szw.y), sz3 = __builtin_amdgcn_cvt_pk_f32_fp8(szw.y, true);
       float kp = fmaf(sz0.x, dk[0] - koff[0], sz0.y * ksum[0]);
@@ -710,6 +729,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       if constexpr (TWO) kmul = kres ? ipu * bf16_to_f32(lds_u16(rs + ST::ka + 4 * kn)) : ipq;
       kp = (TWO || kb < 2) ? kp * kmul : 0.f;
       kp = pair_add<32>(pair_add<16>(kp)) * qs;   // logit of token kn
+      asm volatile("" :: "v"(kb1[0]), "v"(kb1[1]), "v"(kb1[2]), "v"(kb1[3]));
+      if constexpr (TWO) asm volatile("" :: "v"(kb2[0]), "v"(kb2[1]), "v"(kb2[2]), "v"(kb2[3]));
       // to the value side's layout: lane (pair pj, group e) takes tokens 2 pj, 2 pj + 1
       const int kbits = __builtin_bit_cast(int, kp);
       const float lk0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(8 * pj, kbits));

@@ -152,10 +152,6 @@ __device__ __forceinline__ void dma_szrows(rsrc_t r, uint32_t so, int valid, lds
   dma1<4, true>(r, dst, m * ROWB + min(lane & 3, WS - 1) * 4, so);
 }
 
-__device__ __forceinline__ uint32_t lds_u32(const lds_u8* p) {
-  typedef __attribute__((address_space(3))) const uint32_t l1;
-  return *reinterpret_cast<l1*>(p);
-}
 __device__ __forceinline__ u32x4 lds_u32x4(const lds_u8* p) {
   typedef __attribute__((address_space(3))) const u32x4 l4;
   return *reinterpret_cast<l4*>(p);

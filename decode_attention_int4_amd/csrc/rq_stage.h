@@ -106,6 +106,10 @@ __device__ __forceinline__ uint32_t lds_u16(const lds_u8* p) {
   typedef __attribute__((address_space(3))) const uint16_t lh;
   return *reinterpret_cast<lh*>(p);
 }
+__device__ __forceinline__ uint32_t lds_u32(const lds_u8* p) {
+  typedef __attribute__((address_space(3))) const uint32_t lw;
+  return *reinterpret_cast<lw*>(p);
+}
 
 // ------------------------------------------------------------ wave helpers
 // Cross-lane moves inside 16-lane rows by DPP (a VALU modifier, no LDS round
