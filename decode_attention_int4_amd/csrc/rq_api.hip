@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/rq.h"
@@ -130,7 +131,11 @@ rq_status check_paged(const rq_cache_desc* pool, int32_t n_seqs, const int32_t* 
 extern "C" {
 
 const char* rq_status_string(rq_status s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (a value outside the
+  // enumeration is not a valid rq_status in C++)
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case RQ_OK: return "ok";
     case RQ_ERR_INVALID_ARG: return "invalid argument";
     case RQ_ERR_UNSUPPORTED: return "unsupported configuration";

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "librq.so")
+# RQ_LIB selects another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("RQ_LIB") or os.path.join(_PKG, "librq.so")
 
 RQ_OK = 0
 STATUS_NAMES = {0: "RQ_OK", 1: "RQ_ERR_INVALID_ARG", 2: "RQ_ERR_UNSUPPORTED",

@@ -24,6 +24,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
 
 MODE_RESIDUAL = 0
 MODE_DIRECT = 1
@@ -45,13 +46,28 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_sanitized() -> str:
+    """liboracle_san.so: the same source under ASan + UBSan, built with the
+    ROCm clang so that one ASan runtime serves it and librq_san.so (load it
+    with ORACLE_LIB=<path>; see decode_attention_int4_amd/build.py)."""
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    tmp = _SAN_LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call([
+        clang, "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+        "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+        "-fno-omit-frame-pointer", "-shared-libasan", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _SAN_LIB_PATH)
+    return _SAN_LIB_PATH
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        path = os.environ.get("ORACLE_LIB") or build()
+        _lib = ctypes.CDLL(path)
         _declare(_lib)
     return _lib
 
