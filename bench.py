@@ -318,8 +318,9 @@ def capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
 def measure_variant(w, keep, args, torch, rq, RQDecode):
     """Cache size, step bytes and throughput of one workload's packed cache, the
     relative L2 error of its K and V reconstructions (first 128 tokens) against
-    the BF16 originals and of its decode-attention outputs against fp32
-    attention over the BF16 originals (every loop of the `keep` slices)."""
+    the BF16 originals, of the slice queries' logits over those keys, and of
+    its decode-attention outputs against fp32 attention over the BF16
+    originals (every loop of the `keep` slices)."""
     n_rec = min(128, w.n_tokens)
 
     def rel(a, b):
@@ -337,13 +338,21 @@ def measure_variant(w, keep, args, torch, rq, RQDecode):
             p = torch.softmax((kv[0, loop] @ q) * w.softmax_scale, dim=0)
             att.append(rel(run.out[loop, layer, b, head], p @ kv[1, loop]))
     rec = rq.reconstruct(run.desc, run.cache, run.signs, 0, n_rec, out_dtype=torch.bfloat16)
-    kerr, verr = [], []
+    kerr, verr, lerr, lmax = [], [], [], []
     for (b, layer, head) in keep:
         orig = run.kept[(b, layer, head)][:, :, :n_rec].float().cuda()
         got = rec[:, b, :, layer, head].float()
+        qh = head * (w.q_heads // w.kv_heads)
         for loop in range(w.loops):
             kerr.append(rel(got[0, loop], orig[0, loop]))
             verr.append(rel(got[1, loop], orig[1, loop]))
+            # logits of the slice's query over the reconstructed keys: the
+            # key error as attention sees it, before the softmax (whose
+            # outlier channels make it nearly one-hot on these shapes)
+            q = run.q[loop, layer][b, qh].float()
+            lg_ref, lg = (orig[0, loop] @ q) * w.softmax_scale, (got[0, loop] @ q) * w.softmax_scale
+            lerr.append(rel(lg, lg_ref))
+            lmax.append((lg - lg_ref).abs().max().item())
     del rec
     g = graphed(run.step, torch)
     for _ in range(args.warmup):
@@ -352,6 +361,7 @@ def measure_variant(w, keep, args, torch, rq, RQDecode):
     out = {"cache_gb": round(rq.cache_bytes(run.desc) / 1e9, 2), "step_gb": round(run.step_bytes() / 1e9, 2),
            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
            "k_rel_l2": round(sum(kerr) / len(kerr), 5), "v_rel_l2": round(sum(verr) / len(verr), 5),
+           "logit_rel_l2": round(sum(lerr) / len(lerr), 5), "logit_max_abs": round(max(lmax), 4),
            "attn_rel_l2_mean": round(sum(att) / len(att), 5), "attn_rel_l2_max": round(max(att), 5)}
     del g, run
     return out
@@ -390,6 +400,7 @@ def variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
         print(json.dumps(rec), flush=True)
         log(f"[variants] {label}: {rec['tokens_per_s']} tok/s, step {rec['step_gb']} GB, "
             f"K/V rel-L2 {rec['k_rel_l2']:.4f}/{rec['v_rel_l2']:.4f}, "
+            f"logit rel-L2 {rec['logit_rel_l2']:.4f} (max abs {rec['logit_max_abs']:.3f}), "
             f"attention rel-L2 {rec['attn_rel_l2_mean']:.4f} (max {rec['attn_rel_l2_max']:.4f})")
     # loop groups: P loops per group, noise ramp 0.3 .. 0.1 towards the anchor
     d, ng = base.head_dim, base.head_dim // 16
