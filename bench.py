@@ -367,6 +367,35 @@ def measure_variant(w, keep, args, torch, rq, RQDecode):
     return out
 
 
+def quant_timing(args, torch, rq, WORKLOADS):
+    """Quantize-append on the configured shapes: one fill chunk of the size the
+    cache fill uses, and the one-token append of a decode step.  Bytes are the
+    BF16 input read plus the codes, FP8 scale/offset pairs and alphas written
+    (the kernel reads each input once and writes each output once)."""
+    from decode_attention_int4_amd.synth import kv_chunk, rotation_signs
+    from decode_attention_int4_amd.workload import default_chunk, desc_for
+    w = WORKLOADS[args.config]
+    d, P, G = w.head_dim, w.loops_per_group, w.loops // w.loops_per_group
+    for T in (default_chunk(w), 1):
+        desc = desc_for(w, max(T, 64))
+        cache = rq.alloc_cache(desc)
+        x = kv_chunk(w, 0, T, "cuda")
+        signs = rotation_signs(w).cuda()
+        rq.quantize_append(desc, cache, x, 0, signs)
+        reps = max(args.steps, 5)
+        torch.cuda.synchronize()
+        ms, _ = time_steps(lambda: rq.quantize_append(desc, cache, x, 0, signs), reps, torch)
+        items = 2 * w.batch * w.layers * w.kv_heads * G * T
+        out_b = items * (d * w.anchor_bits // 8 + 2 * (d // 16) + (P - 1) * (
+            d * w.residual_bits // 8 + 2 * (d // 16) + (2 if w.mode != 1 else 0)))
+        in_b = x.numel() * 2
+        gbps = (in_b + out_b) / (ms * 1e-3) / 1e9
+        print(json.dumps({"workload": w.name, "t_new": T, "us_per_call": round(ms * 1e3, 2),
+                          "bytes_in": in_b, "bytes_out": out_b, "gbps": round(gbps, 1),
+                          "frac_of_8tbs": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
+        del cache, x
+
+
 def study_keep(w):
     return [(0, 0, 0), (w.batch // 2, w.layers // 2, w.kv_heads // 2),
             (w.batch - 1, w.layers - 1, w.kv_heads - 1)]
@@ -452,6 +481,9 @@ def main():
     ap.add_argument("--variants", action="store_true",
                     help="accuracy and cost of the method's variants on the configured shapes "
                          "(one JSON line per variant) instead of the single benchmark line")
+    ap.add_argument("--quant", action="store_true",
+                    help="only time quantize-append on the configured shapes: one fill chunk "
+                         "and the one-token append (JSON lines)")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run a 1 GiB device copy and a 1 GiB read (known byte counts) "
                          "to calibrate FETCH_SIZE / WRITE_SIZE counters")
@@ -481,6 +513,9 @@ def main():
         print(json.dumps({"calibration_bytes": n}), flush=True)
         return
 
+    if args.quant:
+        quant_timing(args, torch, rq, WORKLOADS)
+        return
     if args.sweep:
         capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
         return
