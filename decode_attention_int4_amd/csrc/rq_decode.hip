@@ -466,9 +466,6 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const int n_tot = t_end > t_begin ? (t_end - t_begin + TPW - 1) / TPW : 0;
   int kcur = w, knext = NWK + w;   // tile being computed, tile after it
   uint32_t claimed = 0;             // lane 0: the tile claimed for the one after
-  // tiles in flight before the query side is built: the whole ring, unless
-  // its DMA count would not fit the wait below
-  constexpr int kPre = ST::COUNT * ST::N_DMA < 64 ? ST::COUNT : ST::COUNT - 1;
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
     dma_piece<ST::C1, ST::R1, F>(rk1, tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
@@ -513,22 +510,21 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), (lds_u8*)s_in + 256,
               min(4 * lane, D - 4), 0u);
   }
+  // One tile per wave goes in flight before the query side is built; the
+  // second slot is filled at the top of the first iteration.  Filling the
+  // whole ring here put twice the bytes (17 MB over the grid at 8k tokens,
+  // batch 4) ahead of every workgroup's first tile: the call measured about
+  // 1 us longer at 8k and at 16k tokens.
   if (kcur < n_tot) issue(kcur, 0);
-  if (kPre == 2 && knext < n_tot) issue(knext, 1);
   if (tid == 0) s_claim = 2 * NWK;
 
   // ---- query side, once per workgroup (wave 0): q, u = H q, their fp16
   // prescales, and for every group the fp16 pairs matching the code pairs,
   // the magic constants 1024 * sum(pair) and the plain sums
   if (w == 0) {
-    // the staged row has landed once at most the tiles' DMAs are pending
-    static_assert(kPre <= 2, "waits below cover two tiles");
-    const int pre = (kcur < n_tot ? 1 : 0) + (kPre == 2 && knext < n_tot ? 1 : 0);
-    if constexpr (kPre == 2) {
-      if (pre == 2) wait_vm<2 * ST::N_DMA>();
-    }
-    if (pre == 1) wait_vm<ST::N_DMA>();
-    else if (pre == 0) wait_vm<0>();
+    // the staged row has landed once at most the first tile's DMAs are pending
+    if (kcur < n_tot) wait_vm<ST::N_DMA>();
+    else wait_vm<0>();
     const bool v1ok = (D > 64) && (lane + 64 < D);
     const lds_u8* qin = (const lds_u8*)s_in;
     const float q0 = bf16_to_f32(lds_u16(qin + 2 * lane));
@@ -667,9 +663,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   // Tiles are claimed in increasing order, so once knext is past the split
   // every later claim is too.
   for (int it = 0; kcur < n_tot; ++it) {
-    // slot (it & 1) holds kcur; knext goes to the other slot (issued before
-    // the loop when the ring was filled up front)
-    if (it + 1 >= kPre && knext < n_tot) issue(knext, (it + 1) & 1);
+    // slot (it & 1) holds kcur; knext goes to the other slot
+    if (knext < n_tot) issue(knext, (it + 1) & 1);
     if (it > 0) claim();
     // wait for kcur: the tile issued after it may stay in flight
     if (knext < n_tot) wait_vm<ST::N_DMA>();
