@@ -35,6 +35,8 @@ static constexpr int32_t kDecodeTarget = 512;      // the largest d = 64, 128 ta
 // -> 52.4 us; anchor calls gain a little too)
 static constexpr int32_t kDecodeTarget96 = 768;
 static constexpr int32_t kBf16Target = 512;
+// Targets above one workgroup per CU are balanced (see plan_splits).
+static constexpr int32_t kOneRound = 256;
 
 static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
   if (n_tokens <= 0 || bh <= 0) return 1;
@@ -47,14 +49,53 @@ static int32_t max_splits_bound(int32_t bh, int32_t n_tokens, int32_t tile, int3
   return splits < max_splits ? splits : max_splits;
 }
 
-SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target) {
-  SplitPlan p{1, tile};
+// Whether a balanced plan gives some rows one split more than `s` (the
+// rounded-down count): only when s is not capped by the two-tile minimum and
+// the rows leave workgroup slots of the target empty.
+static bool balances(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target, int32_t s) {
+  if (n_tokens <= 0 || bh <= 0 || bh > target || target % bh == 0 || s != target / bh) return false;
+  const int32_t n_tiles = (n_tokens + tile - 1) / tile;
+  return s + 1 <= n_tiles / 2;
+}
+
+// The largest split count of any row in a plan for these sizes (the
+// workspace holds that many partial states per row).
+static int32_t max_splits_hi(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target, bool balance) {
+  const int32_t s = max_splits_bound(bh, n_tokens, tile, target);
+  return balance && balances(bh, n_tokens, tile, target, s) ? s + 1 : s;
+}
+
+// With `balance` (targets above one workgroup per CU, where several
+// workgroups share a CU), rounding the splits down leaves slots empty and
+// puts one workgroup more on some CUs than on others: 110 rows at d = 96 took
+// 660 workgroups on 768 slots, and the CUs holding three of them set the
+// call's time (a 128-row call, 768 workgroups, took 49.4 us against 47.9 us
+// for 110 rows: 16 % more bytes in 3 % more time).  A balanced plan gives
+// target - rows * s rows one split more, so the grid fills the slots.
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile, int32_t target, bool balance) {
+  SplitPlan p{1, tile, 0, 1, tile};
   if (n_tokens <= 0 || bh <= 0) return p;
   const int32_t n_tiles = (n_tokens + tile - 1) / tile;
-  const int32_t splits = max_splits_bound(bh, n_tokens, tile, target);
-  const int32_t tiles_per = (n_tiles + splits - 1) / splits;
-  p.tokens_per_split = tiles_per * tile;
-  p.splits = (n_tokens + p.tokens_per_split - 1) / p.tokens_per_split;
+  auto even = [&](int32_t s, int32_t& splits, int32_t& tps) {
+    const int32_t tiles_per = (n_tiles + s - 1) / s;
+    tps = tiles_per * tile;
+    splits = (n_tokens + tps - 1) / tps;
+  };
+  const int32_t s = max_splits_bound(bh, n_tokens, tile, target);
+  even(s, p.splits, p.tokens_per_split);
+  if (balance && balances(bh, n_tokens, tile, target, s)) {
+    int32_t sh = 1, th = tile;
+    even(s + 1, sh, th);
+    if (sh > p.splits) {
+      // rows_hi * sh + rows_lo * splits_lo <= target, as sh <= s + 1 and
+      // splits_lo <= s
+      p.rows_lo = bh - (target - bh * s);
+      p.splits_lo = p.splits;
+      p.tokens_per_split_lo = p.tokens_per_split;
+      p.splits = sh;
+      p.tokens_per_split = th;
+    }
+  }
   return p;
 }
 
@@ -295,8 +336,8 @@ static uint64_t workspace_for(const rq_cache_desc* desc, int32_t rows, int32_t q
   if (check_desc(desc) != RQ_OK || q_heads <= 0 || rows <= 0) return 0;
   const int32_t bh = rows * q_heads;
   // four-wave tiles at the largest target bound the eight-wave plans too
-  int32_t s = rq::max_splits_bound(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim, 4),
-                                   desc->head_dim == 96 ? rq::kDecodeTarget96 : rq::kDecodeTarget);
+  int32_t s = rq::max_splits_hi(bh, max_n_tokens, rq::decode_tile_tokens(desc->head_dim, 4),
+                                desc->head_dim == 96 ? rq::kDecodeTarget96 : rq::kDecodeTarget, true);
   bool any_grouped = false;
   for (int32_t loop = 0; loop < desc->loops_per_group; ++loop)
     any_grouped = any_grouped || grouped(desc, loop, q_heads);
@@ -331,9 +372,10 @@ static rq::SplitPlan decode_plan(const rq_cache_desc* desc, int32_t rows, int32_
                          : two                    ? rq::kDecodeTargetTwo
                                                   : rq::kDecodeTargetOne;
   if (grouped(desc, loop, q_heads))
-    return rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget);
+    return rq::plan_splits(rows * desc->kv_heads, n_tokens, rq::gqa_tile_tokens(), rq::kGqaTarget,
+                           false);
   return rq::plan_splits(rows * q_heads, n_tokens, rq::decode_tile_tokens(desc->head_dim, *waves),
-                         target);
+                         target, target > rq::kOneRound);
 }
 
 int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads, int32_t n_tokens) {
@@ -387,6 +429,9 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   a.n_tokens = n_tokens;
   a.splits = plan.splits;
   a.tokens_per_split = plan.tokens_per_split;
+  a.rows_lo = plan.rows_lo;
+  a.splits_lo = plan.splits_lo;
+  a.tokens_per_split_lo = plan.tokens_per_split_lo;
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.waves = waves;
   return rq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? RQ_OK : RQ_ERR_LAUNCH;
@@ -525,7 +570,7 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
     return RQ_ERR_ALIGNMENT;
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
-  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens(), rq::kBf16Target);
+  const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens(), rq::kBf16Target, false);
   rq::Bf16DecodeArgs a{};
   a.batch = desc->batch;
   a.loops = desc->loops;

@@ -11,7 +11,7 @@
 // the saved memory traffic).
 //
 // gfx950 mapping.
-//   grid (splits, batch * q_heads), NWK = 4 or 8 waves per workgroup (8 for
+//   one workgroup per (batch * q_heads row, split), NWK = 4 or 8 waves per workgroup (8 for
 //   d = 128 calls reading at most one residual plane, paged anchor calls
 //   aside: decode_waves).  A wave takes its
 //   tokens in PAIRS (t, t+1); LPP lanes share a pair and each owns one
@@ -405,7 +405,23 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x, bh = blockIdx.y;
+  // workgroup -> (row, split): the first rows_lo rows take splits_lo splits
+  // each, the others a.splits (a balanced plan; rows_lo is 0 otherwise)
+  int split, bh;
+  {
+    const int wg = blockIdx.x, nlo = a.rows_lo * a.splits_lo;
+    if (wg < nlo) {
+      bh = wg / a.splits_lo;
+      split = wg - bh * a.splits_lo;
+    } else {
+      const int r = (wg - nlo) / a.splits;
+      bh = a.rows_lo + r;
+      split = wg - nlo - r * a.splits;
+    }
+  }
+  const bool lo_row = bh < a.rows_lo;
+  const int ns = lo_row ? a.splits_lo : a.splits;                       // this row's splits
+  const int tps = lo_row ? a.tokens_per_split_lo : a.tokens_per_split;
   const int b = bh / a.q_heads, hq = bh % a.q_heads, kvh = hq / a.group_ratio;
   const int pj = lane / LPP, e = lane % LPP;   // token pair, group
   const bool active = e < NG;
@@ -417,8 +433,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   // tokens of this batch row (per-row lengths come from device memory and are
   // clamped to the planned maximum)
   const int n_row = a.lengths ? min(max(a.lengths[b], 0), a.n_tokens) : a.n_tokens;
-  const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(n_row, t_begin + a.tokens_per_split);
+  const int t_begin = split * tps;
+  const int t_end = min(n_row, t_begin + tps);
 
   // ---- one buffer resource per slot (codes | sz | alpha of one stream); a
   // paged call rebuilds them per tile at its block's offset from block 0
@@ -931,7 +947,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     for (int ww = 0; ww < NWK; ++ww) s = fmaf(sm_acc[ww][i], fw[ww], s);
     return s;
   };
-  if (a.splits > 1) {
+  if (ns > 1) {
     // partial state (m, l, accA[D], accR[D]) of this split; the workgroup
     // that finishes the row last merges all of them
     float* mine = a.partials + ((uint64_t)bh * a.splits + split) * (2 + 2 * D);
@@ -943,8 +959,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
         store_dev(mine + 2 + i, (TWO || i < D) ? merged(i) : 0.f);
       }
     }
-    if (!arrive_last(a, bh, tid, &s_ticket) || w != 0) return;
-    merge_splits<D, TWO>(a, bh, lane);
+    if (!arrive_last(a, bh, ns, tid, &s_ticket) || w != 0) return;
+    merge_splits<D, TWO>(a, bh, ns, lane);
     return;
   }
   // ---- a single split: finish here (first wave, two elements per lane)
@@ -970,7 +986,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 
 template <int D, int B1, int B2, int NR = 1>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.splits, a.rows * a.q_heads);
+  const int bh = a.rows * a.q_heads;
+  const dim3 grid(a.rows_lo * a.splits_lo + (bh - a.rows_lo) * a.splits);
   if constexpr (D == 128 && NR == 1) {
     if (a.waves == 8) {
       if (a.paging.table)

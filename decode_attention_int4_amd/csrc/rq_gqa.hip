@@ -800,8 +800,8 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
     // the workgroup that finishes the KV head last merges its G rows (one
     // counter per KV head: that of its first query head)
     const int bh0 = b * a.q_heads + kvh * G;
-    if (!arrive_last(a, bh0, tid, &s_ticket)) return;
-    for (int n = w; n < G; n += NWG) merge_splits<D, TWO>(a, bh0 + n, lane);
+    if (!arrive_last(a, bh0, a.splits, tid, &s_ticket)) return;
+    for (int n = w; n < G; n += NWG) merge_splits<D, TWO>(a, bh0 + n, a.splits, lane);
     return;
   }
   // ---- a single split: finish here, one wave per head

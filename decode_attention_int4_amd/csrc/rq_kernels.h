@@ -57,6 +57,10 @@ struct DecodeArgs {
   Paging paging;
   int32_t loop, layer, q_heads, group_ratio, n_tokens;
   int32_t splits, tokens_per_split;
+  // per-head kernel: the first rows_lo rows take splits_lo splits of
+  // tokens_per_split_lo tokens, the others `splits` of tokens_per_split
+  // (partials keep the stride `splits`); the grouped kernel leaves rows_lo 0
+  int32_t rows_lo, splits_lo, tokens_per_split_lo;
   float qscale;           // softmax scale * log2(e)
   int32_t waves;          // per-head kernel: waves per workgroup (decode_waves)
 };
@@ -86,11 +90,19 @@ hipError_t launch_bf16_decode(const Bf16DecodeArgs& a, hipStream_t s);
 constexpr uint32_t kProbeBlocks = 1024;
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 
-// Split-K partition shared by workspace sizing and the launch.
+// Split-K partition shared by workspace sizing and the launch.  A balanced
+// plan gives the first rows_lo rows one split fewer (splits_lo of
+// tokens_per_split_lo tokens), so that the grid holds the target number of
+// workgroups exactly; otherwise rows_lo is 0.
 struct SplitPlan {
   int32_t splits;
   int32_t tokens_per_split;
+  int32_t rows_lo, splits_lo, tokens_per_split_lo;
+  int64_t workgroups(int32_t bh) const {
+    return (int64_t)rows_lo * splits_lo + (int64_t)(bh - rows_lo) * splits;
+  }
 };
-SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile_tokens, int32_t target_blocks);
+SplitPlan plan_splits(int32_t bh, int32_t n_tokens, int32_t tile_tokens, int32_t target_blocks,
+                      bool balance);
 
 }  // namespace rq

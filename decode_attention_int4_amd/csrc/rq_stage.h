@@ -246,13 +246,14 @@ __device__ __forceinline__ float load_dev(const float* p) {
 // then one thread takes a ticket from counter `ctr`; the workgroup that
 // arrives last sees every other partial already written, resets the counter
 // to zero for the next call and returns true.  `ticket` is a word of LDS.
-__device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int ctr, int tid, uint32_t* ticket) {
+__device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int ctr, int ns, int tid,
+                                            uint32_t* ticket) {
   wait_vm<0>();
   __syncthreads();
   if (tid == 0)
     *ticket = __hip_atomic_fetch_add(a.counters + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const bool last = *ticket == (uint32_t)a.splits - 1u;
+  const bool last = *ticket == (uint32_t)ns - 1u;
   if (last && tid == 0) __hip_atomic_store(a.counters + ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return last;
 }
@@ -264,11 +265,10 @@ __device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int ctr, int ti
 // once per R splits (merge_splits picks R for the split count, so a call
 // with four splits issues four splits' loads, not sixteen).
 template <int D, bool TWO, int R>
-__device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane) {
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int ns, int lane) {
   constexpr int W = 2 + 2 * D;
-  const int ns = a.splits;
   const bool v1ok = (D > 64) && (lane + 64 < D);
-  const float* all = a.partials + (uint64_t)bh * ns * W;
+  const float* all = a.partials + (uint64_t)bh * a.splits * W;   // row stride: a.splits states
   float M = kEmpty, L = 0.f, A0 = 0.f, A1 = 0.f, R0 = 0.f, R1 = 0.f;
   for (int s0 = 0; s0 < ns; s0 += R) {
     float ms[R], ls[R], a0[R], a1[R], r0[R], r1[R];
@@ -315,10 +315,10 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int bh, int lane)
 }
 
 template <int D, bool TWO>
-__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int bh, int lane) {
-  if (a.splits <= 4) merge_row<D, TWO, 4>(a, bh, lane);
-  else if (a.splits <= 8) merge_row<D, TWO, 8>(a, bh, lane);
-  else merge_row<D, TWO, 16>(a, bh, lane);
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int bh, int ns, int lane) {
+  if (ns <= 4) merge_row<D, TWO, 4>(a, bh, ns, lane);
+  else if (ns <= 8) merge_row<D, TWO, 8>(a, bh, ns, lane);
+  else merge_row<D, TWO, 16>(a, bh, ns, lane);
 }
 
 }  // namespace

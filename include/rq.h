@@ -224,7 +224,10 @@ uint64_t rq_decode_workspace_bytes(const rq_cache_desc* desc, int32_t q_heads,
  * `q_heads` query heads and n_tokens tokens of every batch row (host only;
  * 0 for invalid arguments).  Splits are counted per (batch row, query head),
  * or per (batch row, KV head) for grouped query heads served on matrix
- * cores; 1 means the call uses no workspace. */
+ * cores; 1 means the call uses no workspace.  Where the rows do not divide
+ * the planned number of workgroups, the first rows take one split fewer
+ * than the others, so that the grid fills it; the count returned is the
+ * larger one. */
 int32_t rq_decode_splits(const rq_cache_desc* desc, int32_t loop, int32_t q_heads,
                          int32_t n_tokens);
 

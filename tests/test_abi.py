@@ -257,14 +257,14 @@ def test_workspace_bound_is_monotone():
 
 
 def test_workspace_holds_one_round_of_splits():
-    """The split planner rounds the number of splits per (row, head) down, so
-    a grid of at most its target of four-wave workgroups runs in one round
-    (512 at d = 64 and 128, 768 at d = 96: 110 rows take 6 splits, 660
-    workgroups, not 7).  The workspace is the 256 KiB counter block plus one
-    partial state (m, l, accA[d], accR[d]) per row, head and split."""
+    """The split planner fills its target of four-wave workgroups exactly and
+    no more (512 at d = 64 and 128, 768 at d = 96): 110 rows at d = 96 take 6
+    splits each, and 768 - 660 = 108 of them a seventh.  The workspace is the
+    256 KiB counter block plus one partial state (m, l, accA[d], accR[d]) per
+    row, head and the largest split count."""
     counters = (1 << 16) * 4
     huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs
-    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 6 * (2 + 2 * 96) * 4
+    assert rq.decode_workspace_bytes(huginn, 55, 8192) == counters + 110 * 7 * (2 + 2 * 96) * 4
     ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs: 8 splits
     assert rq.decode_workspace_bytes(ouro, 16, 8192) == counters + 64 * 8 * (2 + 2 * 128) * 4
     # short contexts: at most half the 64-token tiles, and no workspace for one split
@@ -273,15 +273,19 @@ def test_workspace_holds_one_round_of_splits():
 
 
 def test_split_plan_fits_one_round():
-    """The split count the library reports for a call: eight-wave calls
-    (d = 128, at most one residual plane, paged anchors aside) aim at 256
-    workgroups, four-wave ones at 512 (d = 96 calls at 768; 110 rows: 6
-    splits, rounded down),
+    """The split count the library reports for a call (the largest of any
+    row): eight-wave calls (d = 128, at most one residual plane, paged anchors
+    aside) aim at 256 workgroups, four-wave ones at 512 (d = 96 calls at 768;
+    110 rows: 6 splits, 7 for the 108 rows that fill the target),
     grouped-query calls count (row, KV head) pairs, and no split is shorter
     than two tiles."""
     huginn = rq.make_desc(2, 4, 1, 55, 8192, 96)          # 110 (row, head) pairs, four waves
-    assert rq.decode_splits(huginn, 0, 55, 8192) == 6     # 768-workgroup target at d = 96
-    assert rq.decode_splits(huginn, 3, 55, 8192) == 6     # the anchor loop too
+    assert rq.decode_splits(huginn, 0, 55, 8192) == 7     # 768-workgroup target at d = 96
+    assert rq.decode_splits(huginn, 3, 55, 8192) == 7     # the anchor loop too
+    h64 = rq.make_desc(2, 4, 1, 64, 8192, 96)             # 128 rows divide 768: no seventh split
+    assert rq.decode_splits(h64, 0, 64, 8192) == 6
+    short = rq.make_desc(2, 4, 1, 55, 768, 96)            # 12 tiles of 64: at most 6 splits
+    assert rq.decode_splits(short, 0, 55, 768) == 6
     ouro = rq.make_desc(4, 4, 1, 16, 8192, 128)            # 64 pairs, eight waves
     assert rq.decode_splits(ouro, 0, 16, 8192) == 4
     assert rq.decode_splits(ouro, 3, 16, 8192) == 4       # the anchor loop

@@ -3,6 +3,8 @@ oracle on sampled slices (every loop of each slice):
 
   * split merges over more than 16 splits (merged in rounds of 16), at
     head_dim 64, 96 and 128 with few (batch row, head) pairs;
+  * balanced split plans, where some rows take one split fewer than the
+    others so that the grid fills its workgroup target;
   * 64k and 128k tokens with 8-16 splits per row, and single-split calls
     (a whole row per workgroup) at 32k and 128k tokens, in residual and
     direct mode: the longest accumulation per lane.
@@ -74,6 +76,27 @@ def test_many_splits(name):
     w = Workload(name, batch=batch, loops=4, layers=1, kv_heads=heads, q_heads=heads, head_dim=d,
                  n_tokens=n, seed=d + 1)
     _run(w, [(0, 0, heads - 1)], expect_splits=(lambda s, k: s > k, 16))
+
+
+BALANCED = {
+    # (d, batch, heads, tokens, rows_lo, splits): four-wave calls whose rows do
+    # not divide the workgroup target; the first rows_lo rows take one split
+    # fewer than the others
+    "balanced_d96": (96, 2, 55, 8192, 2, 7),    # 110 rows, 768 target: 2 x 6 + 108 x 7
+    "balanced_d64": (64, 4, 25, 8192, 88, 6),   # 100 rows, 512 target: 88 x 5 + 12 x 6
+}
+
+
+@pytest.mark.parametrize("name", list(BALANCED))
+def test_balanced_plan(name):
+    """Rows on both sides of the boundary between the two split counts, and
+    the last row, match the oracle in every loop."""
+    d, batch, heads, n, rows_lo, hi = BALANCED[name]
+    w = Workload(name, batch=batch, loops=4, layers=1, kv_heads=heads, q_heads=heads, head_dim=d,
+                 n_tokens=n, seed=d + 3)
+    rows = [rows_lo - 1, rows_lo, batch * heads - 1]
+    keep = [(r // heads, 0, r % heads) for r in rows]
+    _run(w, keep, expect_splits=(lambda s, k: s == k, hi))
 
 
 LONG = {
