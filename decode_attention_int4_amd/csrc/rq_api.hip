@@ -158,6 +158,10 @@ rq_status check_paged(const rq_cache_desc* pool, int32_t n_seqs, const int32_t* 
   if (st != RQ_OK) return st;
   const int sh = paged_block_shift(pool);
   if (sh < 0) return RQ_ERR_UNSUPPORTED;
+  // the decode kernels reach every plane of a block (all layers of its K or
+  // V half) through one buffer resource with 32-bit offsets
+  const Geometry g = rq::make_geometry(*pool);
+  if ((uint64_t)g.layers * g.layer_block >= (1ull << 32)) return RQ_ERR_UNSUPPORTED;
   if (n_seqs <= 0 || max_blocks <= 0 || !block_table) return RQ_ERR_INVALID_ARG;
   if (((int64_t)max_blocks << sh) > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   if (!aligned(block_table, 4)) return RQ_ERR_ALIGNMENT;
@@ -211,7 +215,8 @@ rq_status rq_cache_layout(const rq_cache_desc* desc, rq_layout* out) {
     out->sz_offset[k] = g.codes_bytes[k];
     out->code_row_bytes[k] = desc->head_dim * (k == 0 ? desc->anchor_bits : desc->residual_bits) / 8;
   }
-  out->alpha_offset = g.alpha_bytes ? g.codes_bytes[1] + g.sz_bytes : UINT64_MAX;
+  out->alpha_offset = g.alpha_row ? g.alpha_block : UINT64_MAX;
+  out->alpha_row_bytes = g.alpha_row;
   out->sz_row_bytes = 2 * desc->head_dim / 16;
   out->token_tile = rq::decode_wave_tokens(desc->head_dim);
   return RQ_OK;
@@ -229,7 +234,7 @@ rq_status rq_cache_slot(const rq_cache_desc* desc, int32_t kv, int32_t batch, in
   const uint64_t off = g.slot_offset(kv, batch, layer, loop, kv_head);
   out->codes_offset = off;
   out->sz_offset = off + g.sz_rel(loop);
-  out->alpha_offset = g.has_alpha(loop) ? off + g.alpha_rel(loop) : UINT64_MAX;
+  out->alpha_offset = g.has_alpha(loop) ? g.alpha_offset(kv, batch, layer, loop, kv_head) : UINT64_MAX;
   out->slot_bytes = g.slot_bytes[g.is_anchor(loop) ? 0 : 1];
   out->bits = g.bits_of(loop);
   out->code_bytes = desc->head_dim * out->bits / 8;

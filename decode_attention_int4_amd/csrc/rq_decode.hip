@@ -436,37 +436,65 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   const int t_begin = split * tps;
   const int t_end = min(n_row, t_begin + tps);
 
-  // ---- one buffer resource per slot (codes | sz | alpha of one stream); a
-  // paged call rebuilds them per tile at its block's offset from block 0
+  // ---- buffer resources.  Contiguous cache: one per plane (a slot, or a
+  // residual plane's alpha row), its pieces at offset 0.  Paged pool: one
+  // over the tile's pool block in the K half of the pool and one in the V
+  // half, rebuilt per tile, with every plane at its offset inside the block
+  // (the same for K and V), so the per-tile state stays small.
   const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
   const uint32_t sb1 = (uint32_t)g.slot_bytes[g.is_anchor(loop1) ? 0 : 1];
   const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
+  const uint32_t arow = (uint32_t)g.alpha_row;
   const int brow = PAGED ? 0 : b;
-  const uint8_t* bk1 = a.cache + g.slot_offset(0, brow, a.layer, loop1, kvh);
-  const uint8_t* bv1 = a.cache + g.slot_offset(1, brow, a.layer, loop1, kvh);
-  const uint8_t *bk2[NR], *bv2[NR];
+  // plane offsets in the K half (paged: inside pool block 0, under 4 GiB)
+  const uint64_t o1 = g.slot_offset(0, brow, a.layer, loop1, kvh);
+  uint64_t o2[NR], oa[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    bk2[r] = a.cache + g.slot_offset(0, brow, a.layer, a.loop + r, kvh);
-    bv2[r] = a.cache + g.slot_offset(1, brow, a.layer, a.loop + r, kvh);
+    o2[r] = g.slot_offset(0, brow, a.layer, a.loop + r, kvh);
+    oa[r] = TWO ? g.alpha_offset(0, brow, a.layer, a.loop + r, kvh) : 0;
   }
-  rsrc_t rk1, rv1, rk2[NR], rv2[NR];
-  auto point_at = [&](uint64_t delta) __attribute__((always_inline)) {
-    rk1 = make_rsrc(bk1 + delta, sb1);
-    rv1 = make_rsrc(bv1 + delta, sb1);
+  const uint64_t vhalf = (uint64_t)g.batch * g.layers * g.layer_block;  // K -> V
+  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;          // one pool block
+  rsrc_t rk1, rv1, rk2[NR], rv2[NR], rka[NR], rva[NR];
+  uint32_t po1 = 0, po2[NR], poa[NR];  // paged: plane offsets inside the block
+#pragma unroll
+  for (int r = 0; r < NR; ++r) po2[r] = poa[r] = 0;
+  if constexpr (!PAGED) {
+    rk1 = make_rsrc(a.cache + o1, sb1);
+    rv1 = make_rsrc(a.cache + vhalf + o1, sb1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      rk2[r] = make_rsrc(bk2[r] + delta, sb2);
-      rv2[r] = make_rsrc(bv2[r] + delta, sb2);
+      rk2[r] = make_rsrc(a.cache + o2[r], sb2);
+      rv2[r] = make_rsrc(a.cache + vhalf + o2[r], sb2);
+      if constexpr (TWO) {
+        rka[r] = make_rsrc(a.cache + oa[r], arow);
+        rva[r] = make_rsrc(a.cache + vhalf + oa[r], arow);
+      }
+    }
+  } else {
+    po1 = (uint32_t)o1;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      po2[r] = (uint32_t)o2[r];
+      poa[r] = (uint32_t)oa[r];
+    }
+  }
+  auto point_at = [&](uint64_t delta) __attribute__((always_inline)) {
+    const rsrc_t rk = make_rsrc(a.cache + delta, (uint32_t)bstride);
+    const rsrc_t rv = make_rsrc(a.cache + vhalf + delta, (uint32_t)bstride);
+    rk1 = rk;
+    rv1 = rv;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      rk2[r] = rka[r] = rk;
+      rv2[r] = rva[r] = rv;
     }
   };
-  if constexpr (!PAGED) point_at(0);
   // block-table row of this sequence, read through the scalar cache
   typedef const __attribute__((address_space(4))) int32_t c_i32;
   const c_i32* btab = (const c_i32*)(a.paging.table + (uint64_t)b * a.paging.max_blocks);
-  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;  // one pool block
-  const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
-  const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
+  const uint32_t s1rel = po1 + (uint32_t)g.sz_rel(loop1);
 
   // ---- stream the split's wave tiles (tile k: TPW tokens from t_begin +
   // k TPW) through each wave's LDS ring.  Waves start with tiles w and
@@ -484,20 +512,23 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   uint32_t claimed = 0;             // lane 0: the tile claimed for the one after
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
-    dma_piece<ST::C1, ST::R1, F>(rk1, tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
+    dma_piece<ST::C1, ST::R1, F>(rk1, po1 + tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
     dma_piece<ST::SZ, ST::RS, F>(rk1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
-    dma_piece<ST::C1, ST::R1, F>(rv1, tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
+    dma_piece<ST::C1, ST::R1, F>(rv1, po1 + tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
     dma_piece<ST::SZ, ST::RS, F>(rv1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
     if constexpr (TWO) {
+      const uint32_t s2rel = (uint32_t)g.sz_rel(a.loop);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         lds_u8* rs = st + ST::res(r);
-        dma_piece<ST::C2, ST::R2, F>(rk2[r], tb * ST::R2, vt * ST::R2, rs + ST::k2c, lane);
-        dma_piece<ST::SZ, ST::RS, F>(rk2[r], s2rel + tb * ST::RS, vt * ST::RS, rs + ST::k2s, lane);
-        dma_piece<ST::C2, ST::R2, F>(rv2[r], tb * ST::R2, vt * ST::R2, rs + ST::v2c, lane);
-        dma_piece<ST::SZ, ST::RS, F>(rv2[r], s2rel + tb * ST::RS, vt * ST::RS, rs + ST::v2s, lane);
-        dma_alpha(rk2[r], arel + tb * 2, F ? TPW : vt, rs + ST::ka, lane);
-        dma_alpha(rv2[r], arel + tb * 2, F ? TPW : vt, rs + ST::va, lane);
+        dma_piece<ST::C2, ST::R2, F>(rk2[r], po2[r] + tb * ST::R2, vt * ST::R2, rs + ST::k2c, lane);
+        dma_piece<ST::SZ, ST::RS, F>(rk2[r], po2[r] + s2rel + tb * ST::RS, vt * ST::RS, rs + ST::k2s,
+                                     lane);
+        dma_piece<ST::C2, ST::R2, F>(rv2[r], po2[r] + tb * ST::R2, vt * ST::R2, rs + ST::v2c, lane);
+        dma_piece<ST::SZ, ST::RS, F>(rv2[r], po2[r] + s2rel + tb * ST::RS, vt * ST::RS, rs + ST::v2s,
+                                     lane);
+        dma_alpha(rka[r], poa[r] + tb * 2, F ? TPW : vt, rs + ST::ka, lane);
+        dma_alpha(rva[r], poa[r] + tb * 2, F ? TPW : vt, rs + ST::va, lane);
       }
     }
   };

@@ -397,28 +397,43 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(n_row, t_begin + a.tokens_per_split);
 
-  // ---- buffer resources (paged: rebuilt per tile at the tile's block)
+  // ---- buffer resources.  Contiguous cache: one per plane (a slot, or the
+  // residual plane's alpha row).  Paged pool: one over the tile's pool block
+  // in the K half and one in the V half, rebuilt per tile, with every plane
+  // at its offset inside the block (the same for K and V).
   const int loop1 = (g.mode == RQ_MODE_DIRECT || !TWO) ? a.loop : (a.loop - a.loop % g.P + g.P - 1);
   const uint32_t sb1 = (uint32_t)g.slot_bytes[g.is_anchor(loop1) ? 0 : 1];
   const uint32_t sb2 = (uint32_t)g.slot_bytes[g.is_anchor(a.loop) ? 0 : 1];
+  const uint32_t arow = (uint32_t)g.alpha_row;
   const int brow = PAGED ? 0 : b;
-  const uint8_t* bk1 = a.cache + g.slot_offset(0, brow, a.layer, loop1, kvh);
-  const uint8_t* bv1 = a.cache + g.slot_offset(1, brow, a.layer, loop1, kvh);
-  const uint8_t* bk2 = a.cache + g.slot_offset(0, brow, a.layer, a.loop, kvh);
-  const uint8_t* bv2 = a.cache + g.slot_offset(1, brow, a.layer, a.loop, kvh);
-  rsrc_t rk1, rv1, rk2, rv2;
+  const uint64_t o1 = g.slot_offset(0, brow, a.layer, loop1, kvh);
+  const uint64_t o2 = g.slot_offset(0, brow, a.layer, a.loop, kvh);
+  const uint64_t oa = TWO ? g.alpha_offset(0, brow, a.layer, a.loop, kvh) : 0;
+  const uint64_t vhalf = (uint64_t)g.batch * g.layers * g.layer_block;  // K -> V
+  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;          // one pool block
+  rsrc_t rk1, rv1, rk2, rv2, rka, rva;
+  uint32_t po1 = 0, po2 = 0, poa = 0;  // paged: plane offsets inside the block
+  if constexpr (!PAGED) {
+    rk1 = make_rsrc(a.cache + o1, sb1);
+    rv1 = make_rsrc(a.cache + vhalf + o1, sb1);
+    rk2 = make_rsrc(a.cache + o2, sb2);
+    rv2 = make_rsrc(a.cache + vhalf + o2, sb2);
+    if constexpr (TWO) {
+      rka = make_rsrc(a.cache + oa, arow);
+      rva = make_rsrc(a.cache + vhalf + oa, arow);
+    }
+  } else {
+    po1 = (uint32_t)o1;
+    po2 = (uint32_t)o2;
+    poa = (uint32_t)oa;
+  }
   auto point_at = [&](uint64_t delta) __attribute__((always_inline)) {
-    rk1 = make_rsrc(bk1 + delta, sb1);
-    rv1 = make_rsrc(bv1 + delta, sb1);
-    rk2 = make_rsrc(bk2 + delta, sb2);
-    rv2 = make_rsrc(bv2 + delta, sb2);
+    rk1 = rk2 = rka = make_rsrc(a.cache + delta, (uint32_t)bstride);
+    rv1 = rv2 = rva = make_rsrc(a.cache + vhalf + delta, (uint32_t)bstride);
   };
-  if constexpr (!PAGED) point_at(0);
   typedef const __attribute__((address_space(4))) int32_t c_i32;
   const c_i32* btab = (const c_i32*)(a.paging.table + (uint64_t)b * a.paging.max_blocks);
-  const uint64_t bstride = (uint64_t)g.layers * g.layer_block;
-  const uint32_t s1rel = (uint32_t)g.sz_rel(loop1), s2rel = (uint32_t)g.sz_rel(a.loop);
-  const uint32_t arel = (uint32_t)g.alpha_rel(a.loop);
+  const uint32_t s1rel = po1 + (uint32_t)g.sz_rel(loop1), s2rel = po2 + (uint32_t)g.sz_rel(a.loop);
 
   // ---- this wave's tiles through its two-stage ring
   lds_u8* ring = (lds_u8*)smem + w * 2 * GS::BYTES;
@@ -426,17 +441,17 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   const int n_tiles = first < t_end ? (t_end - first + NWG * TT - 1) / (NWG * TT) : 0;
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
-    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rk1, tb * R1, vt, st + GS::k1c, lane);
+    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rk1, po1 + tb * R1, vt, st + GS::k1c, lane);
     dma_szrows<GS::WS, RS, F>(rk1, s1rel + tb * RS, vt, st + GS::k1s, lane);
-    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rv1, tb * R1, vt, st + GS::v1c, lane);
+    dma_blocks<typename GS::CB1, GS::W1, R1, F>(rv1, po1 + tb * R1, vt, st + GS::v1c, lane);
     dma_gather<GS::WS, RS, F>(rv1, s1rel + tb * RS, vt, st + GS::v1s, lane);
     if constexpr (TWO) {
-      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rk2, tb * R2, vt, st + GS::k2c, lane);
+      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rk2, po2 + tb * R2, vt, st + GS::k2c, lane);
       dma_szrows<GS::WS, RS, F>(rk2, s2rel + tb * RS, vt, st + GS::k2s, lane);
-      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rv2, tb * R2, vt, st + GS::v2c, lane);
+      dma_blocks<typename GS::CB2, GS::W2, R2, F>(rv2, po2 + tb * R2, vt, st + GS::v2c, lane);
       dma_gather<GS::WS, RS, F>(rv2, s2rel + tb * RS, vt, st + GS::v2s, lane);
-      dma_alpha(rk2, arel + tb * 2, F ? TT : vt, st + GS::ka, lane);
-      dma_alpha(rv2, arel + tb * 2, F ? TT : vt, st + GS::va, lane);
+      dma_alpha(rka, poa + tb * 2, F ? TT : vt, st + GS::ka, lane);
+      dma_alpha(rva, poa + tb * 2, F ? TT : vt, st + GS::va, lane);
     }
   };
   auto issue = [&](int tile) __attribute__((always_inline)) {

@@ -387,7 +387,9 @@ __global__ void __launch_bounds__(256) quant_append_kernel(QuantArgs a) {
           al = f64_to_bf16(sqrt(yy) / sqrt(den));
         else
           al = f64_to_bf16(num / den);
-        if (q == 0) reinterpret_cast<uint16_t*>(base + g.alpha_rel(loop))[pos] = (uint16_t)al;
+        if (q == 0)
+          reinterpret_cast<uint16_t*>(a.cache + g.alpha_offset(kv, slot_row, layer, loop, head))[pos] =
+              (uint16_t)al;
         if constexpr (CHAINED) {
           // alpha (8 significant bits) times yhat is exact, so the FMA is the
           // product-then-sum of the definition

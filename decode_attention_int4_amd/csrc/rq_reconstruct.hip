@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(256) reconstruct_kernel(ReconArgs a) {
       float y0 = 0.f, y1 = 0.f;
       for (int rl = last; rl >= loop; --rl) {
         const uint8_t* rs = a.cache + g.slot_offset(kv, b, layer, rl, head);
-        const float al = bf16_to_f32(reinterpret_cast<const uint16_t*>(rs + g.alpha_rel(rl))[t]);
+        const float al = bf16_to_f32(
+            reinterpret_cast<const uint16_t*>(a.cache + g.alpha_offset(kv, b, layer, rl, head))[t]);
         y0 = fmaf(al, deq_elem(rs, g.sz_rel(rl), g.residual_bits, D, t, lane), y0);
         if (v1ok) y1 = fmaf(al, deq_elem(rs, g.sz_rel(rl), g.residual_bits, D, t, lane + 64), y1);
       }

@@ -66,6 +66,7 @@ class Layout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_uint64), ("layer_bytes", ctypes.c_uint64),
                 ("group_bytes", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64 * 2),
                 ("sz_offset", ctypes.c_uint64 * 2), ("alpha_offset", ctypes.c_uint64),
+                ("alpha_row_bytes", ctypes.c_uint64),
                 ("code_row_bytes", ctypes.c_int32 * 2), ("sz_row_bytes", ctypes.c_int32),
                 ("token_tile", ctypes.c_int32)]
 

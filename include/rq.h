@@ -58,14 +58,15 @@
  * anchor when j == P-1.  Its bit width is anchor_bits for the anchor and
  * residual_bits otherwise (direct mode: the anchor-position loop is stored at
  * anchor_bits, the others at residual_bits, all as plain quantized states).
- * A slot is three sub-planes, each starting on a 256-byte boundary:
+ * A slot is two sub-planes, each starting on a 256-byte boundary:
  *     codes [max_tokens][d*bits/8]  element i of a token is in byte i*bits/8,
  *                                   at bit (i*bits) % 8 (low bits first)
  *     sz    [max_tokens][2*d/16]    byte 2g = FP8 e4m3fn scale of group g,
  *                                   byte 2g+1 = FP8 e4m3fn offset of group g
- *     alpha [max_tokens] uint16     BF16 coefficient (non-anchor loops of
- *                                   RESIDUAL and CHAINED modes; absent
- *                                   otherwise)
+ * In RESIDUAL and CHAINED modes each non-anchor (loop, kv head) also has an
+ * alpha row, [max_tokens] uint16 BF16 coefficients; the rows of one loop
+ * group follow the group's slots as one block, padded to 256 bytes as a
+ * whole (see rq_layout).
  * A dequantized group value is scale * code + offset.  Slot sizes and
  * offsets are given by rq_cache_slot(); the total by rq_cache_bytes().
  */
@@ -113,7 +114,7 @@ typedef struct rq_cache_desc {
 typedef struct rq_slot {
   uint64_t codes_offset; /* bytes from the start of the cache buffer */
   uint64_t sz_offset;
-  uint64_t alpha_offset; /* UINT64_MAX when the slot has no alpha plane */
+  uint64_t alpha_offset; /* the slot's alpha row; UINT64_MAX when it has none */
   uint64_t slot_bytes;   /* bytes from codes_offset to the next slot */
   int32_t bits;          /* code width of this slot */
   int32_t code_bytes;    /* bytes per token in the codes sub-plane */
@@ -122,26 +123,28 @@ typedef struct rq_slot {
 /* The whole byte layout of a cache for one descriptor, so a caller can
  * address any slot without further calls (host only).  With P =
  * loops_per_group, loop = k * P + j (group k, position j; j == P - 1 is the
- * anchor) and kind = (j == P - 1 ? 0 : 1), the slot of (kv, batch row b,
- * layer, loop, kv_head h) starts at
- *     ((kv * batch + b) * layers + layer) * layer_bytes
- *       + kv_heads * (k * group_bytes + j * slot_bytes[1])
- *       + h * slot_bytes[kind]
- * and its sub-planes at that offset + 0 (codes), + sz_offset[kind] (FP8
- * scale/offset pairs) and + alpha_offset (BF16 alpha; non-anchor slots of
- * RESIDUAL and CHAINED modes only).  Token t's rows are code_row_bytes[kind]
- * and sz_row_bytes long, at t times those sizes from their sub-plane.
- * total_bytes equals rq_cache_bytes().  token_tile is the decode kernels'
- * wave tile in tokens (16 at head_dim 96 and 128, 32 at 64): the smallest
- * block size a paged pool accepts.  (rq_cache_slot gives the same offsets
- * for one slot.) */
+ * anchor), kind = (j == P - 1 ? 0 : 1) and
+ *     base = ((kv * batch + b) * layers + layer) * layer_bytes + k * group_bytes,
+ * the slot of (kv, batch row b, layer, loop, kv_head h) starts at
+ *     base + j * kv_heads * slot_bytes[1] + h * slot_bytes[kind]
+ * and its sub-planes at that offset + 0 (codes) and + sz_offset[kind] (FP8
+ * scale/offset pairs).  In RESIDUAL and CHAINED modes the BF16 alpha row of
+ * a non-anchor (loop, h) starts at
+ *     base + alpha_offset + (j * kv_heads + h) * alpha_row_bytes
+ * (the loop group's slots come first, then its alpha block, padded to 256
+ * bytes).  Token t's rows are code_row_bytes[kind], sz_row_bytes and 2 bytes
+ * long, at t times those sizes from their sub-plane or row.  total_bytes
+ * equals rq_cache_bytes().  token_tile is the decode kernels' wave tile in
+ * tokens (16 at head_dim 96 and 128, 32 at 64): the smallest block size a
+ * paged pool accepts.  (rq_cache_slot gives the same offsets for one slot.) */
 typedef struct rq_layout {
   uint64_t total_bytes;
   uint64_t layer_bytes;       /* one (kv, batch row, layer) block */
-  uint64_t group_bytes;       /* one loop group of one kv head */
+  uint64_t group_bytes;       /* one loop group: all kv heads' slots, then the alpha block */
   uint64_t slot_bytes[2];     /* [0] anchor-position slots, [1] other slots */
   uint64_t sz_offset[2];      /* sz sub-plane offset inside a slot of each kind */
-  uint64_t alpha_offset;      /* alpha sub-plane offset in a kind-1 slot, or UINT64_MAX */
+  uint64_t alpha_offset;      /* alpha block offset inside a loop group, or UINT64_MAX */
+  uint64_t alpha_row_bytes;   /* 2 * max_tokens, or 0 without alpha */
   int32_t code_row_bytes[2];  /* d * bits / 8 of each kind */
   int32_t sz_row_bytes;       /* 2 * d / 16 */
   int32_t token_tile;
@@ -308,7 +311,8 @@ rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cach
  * of physical blocks described by an ordinary descriptor `pool` in which
  *   pool->batch       is the number of blocks in the pool, and
  *   pool->max_tokens  is the tokens per block: a power of two, at least 16
- *                     (head_dim 96, 128) or 32 (head_dim 64);
+ *                     (head_dim 96, 128) or 32 (head_dim 64), with one
+ *                     block's K (or V) bytes over all layers under 4 GiB;
  * the byte layout above then holds with "batch row" read as "block".  Sequence
  * s keeps logical token t in block block_table[s * max_blocks_per_seq +
  * t / block_tokens] at token t % block_tokens; the entries a call reads are

@@ -2,8 +2,9 @@
 
 Written from the header's description (slot order, sub-planes on 256-byte
 boundaries, codes low bits first, sz bytes = [scale, offset] per group, BF16
-alpha), independently of the library's own geometry code, so the tests can
-turn the GPU's planes into the oracle's logical arrays.
+alpha rows in one block after each loop group's slots), independently of the
+library's own geometry code, so the tests can turn the GPU's planes into the
+oracle's logical arrays.
 """
 from __future__ import annotations
 
@@ -49,25 +50,40 @@ class Geom:
         T = self.max_tokens
         codes = _align(T * self.d * self.bits(loop) // 8)
         sz = _align(T * 2 * (self.d // 16))
-        alpha = _align(T * 2) if self.mode != 1 else 0
-        return codes, sz, alpha
+        return codes, sz
 
     def slot_bytes(self, loop):
-        c, s, a = self.sub_sizes(loop)
-        return c + s + (a if self.has_alpha(loop) else 0)
+        return sum(self.sub_sizes(loop))
+
+    def alpha_row_bytes(self):
+        return 2 * self.max_tokens if self.mode != 1 else 0
+
+    def _group_slots(self):
+        # the slots of one loop group: P loops (anchor last) x kv heads
+        return sum(self.kv_heads * self.slot_bytes(j) for j in range(self.P))
+
+    def group_bytes(self):
+        return self._group_slots() + _align((self.P - 1) * self.kv_heads * self.alpha_row_bytes())
+
+    def _group_base(self, kv, b, layer, loop):
+        per_layer = (self.loops // self.P) * self.group_bytes()
+        return (((kv * self.batch + b) * self.layers + layer) * per_layer
+                + (loop // self.P) * self.group_bytes())
 
     def slot_offset(self, kv, b, layer, loop, head):
-        # order: kv, batch, layer, loop, head; loops of a group consecutive, anchor last
-        off = 0
-        per_layer = sum(self.kv_heads * self.slot_bytes(l) for l in range(self.loops))
-        off += ((kv * self.batch + b) * self.layers + layer) * per_layer
-        off += sum(self.kv_heads * self.slot_bytes(l) for l in range(loop))
-        off += head * self.slot_bytes(loop)
-        return off
+        # order: kv, batch, layer, loop group, loop (anchor last), head
+        j = loop % self.P
+        off = self._group_base(kv, b, layer, loop)
+        off += sum(self.kv_heads * self.slot_bytes(l) for l in range(j))
+        return off + head * self.slot_bytes(loop)
+
+    def alpha_offset(self, kv, b, layer, loop, head):
+        j = loop % self.P
+        return (self._group_base(kv, b, layer, loop) + self._group_slots()
+                + (j * self.kv_heads + head) * self.alpha_row_bytes())
 
     def total(self):
-        per_layer = sum(self.kv_heads * self.slot_bytes(l) for l in range(self.loops))
-        return 2 * self.batch * self.layers * per_layer
+        return 2 * self.batch * self.layers * (self.loops // self.P) * self.group_bytes()
 
 
 def unpack_codes(raw: np.ndarray, bits: int, d: int) -> np.ndarray:
@@ -104,12 +120,12 @@ def decode_slice(cache: torch.Tensor, geom: Geom, kv: int, b: int, layer: int, h
         off = geom.slot_offset(kv, b, layer, loop, head)
         bits = geom.bits(loop)
         cb = d * bits // 8
-        c_sz, s_sz, _ = geom.sub_sizes(loop)
+        c_sz, _ = geom.sub_sizes(loop)
         raw = _bytes(cache, off + t0 * cb, N * cb).reshape(N, cb)
         codes[loop] = unpack_codes(raw, bits, d)
         sz = _bytes(cache, off + c_sz + t0 * 2 * ng, N * 2 * ng).reshape(N, ng, 2)
         s8[loop], z8[loop] = sz[:, :, 0], sz[:, :, 1]
         if geom.has_alpha(loop):
-            a = _bytes(cache, off + c_sz + s_sz + 2 * t0, 2 * N)
+            a = _bytes(cache, geom.alpha_offset(kv, b, layer, loop, head) + 2 * t0, 2 * N)
             alpha[loop] = a.view(np.uint16)
     return Planes(codes, s8, z8, alpha)

@@ -59,10 +59,11 @@ def test_geometry_matches_documented_layout(desc):
         head = int(rng.integers(0, desc.kv_heads))
         s = rq.cache_slot(desc, kv, b, layer, loop, head)
         off = g.slot_offset(kv, b, layer, loop, head)
-        c, z, a = g.sub_sizes(loop)
+        c, z = g.sub_sizes(loop)
         assert s.codes_offset == off and s.codes_offset % 256 == 0
         assert s.sz_offset == off + c
-        assert s.alpha_offset == (off + c + z if g.has_alpha(loop) else 2 ** 64 - 1)
+        assert s.alpha_offset == (g.alpha_offset(kv, b, layer, loop, head) if g.has_alpha(loop)
+                                  else 2 ** 64 - 1)
         assert s.bits == g.bits(loop)
         assert s.code_bytes == desc.head_dim * s.bits // 8
         assert s.slot_bytes == g.slot_bytes(loop)
@@ -84,17 +85,49 @@ def test_cache_layout_addresses_every_slot(desc):
                     for h in range(desc.kv_heads):
                         k, j = divmod(loop, P)
                         kind = 0 if j == P - 1 else 1
-                        off = (((kv * desc.batch + b) * desc.layers + layer) * lay.layer_bytes
-                               + desc.kv_heads * (k * lay.group_bytes + j * lay.slot_bytes[1])
-                               + h * lay.slot_bytes[kind])
+                        base = (((kv * desc.batch + b) * desc.layers + layer) * lay.layer_bytes
+                                + k * lay.group_bytes)
+                        off = base + j * desc.kv_heads * lay.slot_bytes[1] + h * lay.slot_bytes[kind]
                         s = rq.cache_slot(desc, kv, b, layer, loop, h)
                         assert s.codes_offset == off
                         assert s.sz_offset == off + lay.sz_offset[kind]
-                        want_alpha = off + lay.alpha_offset if (kind == 1 and lay.alpha_offset
-                                                                != 2 ** 64 - 1) else 2 ** 64 - 1
+                        want_alpha = (base + lay.alpha_offset + (j * desc.kv_heads + h)
+                                      * lay.alpha_row_bytes) if (kind == 1 and lay.alpha_offset
+                                                                 != 2 ** 64 - 1) else 2 ** 64 - 1
                         assert s.alpha_offset == want_alpha
                         assert s.slot_bytes == lay.slot_bytes[kind]
                         assert s.code_bytes == lay.code_row_bytes[kind]
+
+
+@pytest.mark.parametrize("desc", [DESCS[0], DESCS[3], DESCS[4], DESCS[5],
+                                  rq.make_desc(2, 8, 2, 3, 16, 128),
+                                  rq.make_desc(1, 4, 1, 16, 16, 96, mode=rq.MODE_CHAINED)],
+                         ids=lambda d: f"{d.head_dim}-{d.max_tokens}-{d.mode}-{d.kv_heads}")
+def test_cache_planes_tile_the_buffer(desc):
+    """Every codes, sz and alpha range of every slot lies inside the buffer
+    and no two overlap; alpha rows are only 2 * max_tokens bytes apart, so a
+    16-token paged block carries no per-row padding."""
+    total = rq.cache_bytes(desc)
+    lay = rq.cache_layout(desc)
+    n = desc.max_tokens
+    ranges = []
+    for kv in range(2):
+        for b in range(desc.batch):
+            for layer in range(desc.layers):
+                for loop in range(desc.loops):
+                    for h in range(desc.kv_heads):
+                        s = rq.cache_slot(desc, kv, b, layer, loop, h)
+                        ranges.append((s.codes_offset, s.codes_offset + n * s.code_bytes))
+                        ranges.append((s.sz_offset, s.sz_offset + n * lay.sz_row_bytes))
+                        if s.alpha_offset != 2 ** 64 - 1:
+                            assert s.alpha_offset % 2 == 0
+                            ranges.append((s.alpha_offset, s.alpha_offset + 2 * n))
+    ranges.sort()
+    assert ranges[0][0] >= 0 and ranges[-1][1] <= total
+    for (a0, a1), (b0, _) in zip(ranges, ranges[1:]):
+        assert a1 <= b0
+    if desc.mode != rq.MODE_DIRECT:
+        assert lay.alpha_row_bytes == 2 * n
 
 
 def test_cache_layout_rejects_bad_arguments():
@@ -208,6 +241,14 @@ def test_paged_entry_points_reject_bad_arguments_before_launch():
         st = L.rq_paged_quantize_append(ctypes.byref(p), FAKE, FAKE, 3, FAKE, 8, FAKE,
                                         8 * bt + 1, FAKE, None)
         assert st == (3 if ok else 2), (bt, d)
+    # one block's K bytes over all layers must stay under 4 GiB (131072-token
+    # blocks of 24 layers: about 11 GB)
+    huge = rq.make_desc(2, 4, 24, 16, 1 << 17, 128)
+    st = L.rq_paged_decode_attention(ctypes.byref(huge), FAKE, FAKE, 0, 0, FAKE, 16, 1, FAKE, 1,
+                                     FAKE, 1 << 17, f, FAKE, 1 << 40, FAKE, None)
+    assert st == 2
+    assert L.rq_paged_quantize_append(ctypes.byref(huge), FAKE, FAKE, 1, FAKE, 1, FAKE, 1,
+                                      FAKE, None) == 2
     pool = rq.make_desc(40, 4, 1, 2, 32, 64)
     P = ctypes.byref(pool)
     ws = rq.paged_decode_workspace_bytes(pool, 2, 3, 256)
