@@ -382,6 +382,7 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   __shared__ float spq[16], spu[16];             // per-head prescales
   __shared__ float sm_m[NWG][16], sm_l[NWG][16];
   __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_claim;   // next unclaimed wave tile of this split
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -437,8 +438,15 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
 
   // ---- this wave's tiles through its two-stage ring
   lds_u8* ring = (lds_u8*)smem + w * 2 * GS::BYTES;
-  const int first = t_begin + w * TT;
-  const int n_tiles = first < t_end ? (t_end - first + NWG * TT - 1) / (NWG * TT) : 0;
+  // Tile k of the split holds tokens [t_begin + k TT, + TT).  Waves start
+  // with tiles w and NWG + w; after that each wave claims the next unclaimed
+  // tile from an LDS counter, one tile ahead, so no wave idles while another
+  // still holds an equal share of the split (the second wave of a SIMD loses
+  // issue arbitration to the first).  Tiles are summed in a different order
+  // from call to call: results agree to fp32 summation order.
+  const int n_tot = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
+  int kcur = w, knext = NWG + w;   // tile being computed, tile after it
+  uint32_t claimed = 0;             // lane 0: the tile claimed for the one after
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
     dma_blocks<typename GS::CB1, GS::W1, R1, F>(rk1, po1 + tb * R1, vt, st + GS::k1c, lane);
@@ -454,9 +462,9 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
       dma_alpha(rva, poa + tb * 2, F ? TT : vt, st + GS::va, lane);
     }
   };
-  auto issue = [&](int tile) __attribute__((always_inline)) {
-    uint32_t tb = (uint32_t)(first + tile * NWG * TT);
-    lds_u8* st = ring + (tile & 1) * GS::BYTES;
+  auto issue = [&](int k, int slot) __attribute__((always_inline)) {
+    uint32_t tb = (uint32_t)(t_begin + k * TT);
+    lds_u8* st = ring + slot * GS::BYTES;
     const int vt = t_end - (int)tb;
     if constexpr (PAGED) {
       const int blk = min(max(btab[tb >> a.paging.block_shift], 0), g.batch - 1);
@@ -480,8 +488,9 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   if (rotated && w == 0)
     dma1<4>(make_rsrc((const uint8_t*)(a.signs + (uint64_t)a.layer * D), D), stage + 16 * 256,
             min(4 * lane, D - 4), 0u);
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 0) wait_vm<GS::N_DMA>();
+  if (kcur < n_tot) issue(kcur, 0);
+  if (tid == 0) s_claim = 2 * NWG;
+  if (kcur < n_tot) wait_vm<GS::N_DMA>();
   else wait_vm<0>();
   __syncthreads();   // every wave's rows and the signs are in LDS
   constexpr int kHw = 16 / NWG;   // operand columns per wave
@@ -618,13 +627,21 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
   float m = kEmpty, l = 0.f;
   const uint32_t vm1 = v_mask<B1>(r), vm2 = v_mask<B2E>(r);   // this lane's element row
 
-  for (int it = 0; it < n_tiles; ++it) {
-    // tile it + 1 goes into the slot tile it - 1 has left
-    if (it + 1 < n_tiles) issue(it + 1);
-    if (it + 1 < n_tiles) wait_vm<GS::N_DMA>();
+  auto claim = [&]() __attribute__((always_inline)) {
+    if (lane == 0)
+      claimed = __hip_atomic_fetch_add(&s_claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  claim();
+  // Tiles are claimed in increasing order, so once knext is past the split
+  // every later claim is too.
+  for (int it = 0; kcur < n_tot; ++it) {
+    // slot (it & 1) holds kcur; knext goes into the slot the tile before left
+    if (knext < n_tot) issue(knext, (it + 1) & 1);
+    if (it > 0) claim();
+    if (knext < n_tot) wait_vm<GS::N_DMA>();
     else wait_vm<0>();
     const lds_u8* st = ring + (it & 1) * GS::BYTES;
-    const int vt = t_end - (first + it * NWG * TT);  // in-range tokens of this tile
+    const int vt = t_end - (t_begin + kcur * TT);  // in-range tokens of this tile
 
     // ---- logits S^T (lane: head r, tokens 4c + j)
     f4 SA = {0.f, 0.f, 0.f, 0.f};
@@ -725,6 +742,8 @@ __global__ void __launch_bounds__(NWG * 64, 2) gqa_kernel(DecodeArgs a) {
       OZR = mfma16(z, Qh, OZR);
       OZR = mfma16(z, Ql, OZR);
     }
+    kcur = knext;
+    knext = (int)__builtin_amdgcn_readfirstlane(claimed);
   }
 
   // ---- merge the waves: running max per head, then the G heads' sums of

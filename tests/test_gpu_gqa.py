@@ -79,8 +79,10 @@ def test_grouped_query_ragged_and_lengths():
 
 
 def test_grouped_query_paged_equals_contiguous():
-    """The grouped kernel over a paged pool gives bit-identical outputs to the
-    contiguous cache holding the same tokens."""
+    """The grouped kernel over a paged pool gives the outputs of the
+    contiguous cache holding the same tokens, up to fp32 summation order (the
+    waves claim their tiles dynamically, so the order in which a wave sums
+    its tiles varies from call to call)."""
     base = Workload("gqa_paged", batch=2, loops=4, layers=1, kv_heads=2, q_heads=8, head_dim=128,
                     n_tokens=300, seed=4)
     run = RQDecode(base, chunk_tokens=300)
@@ -88,7 +90,10 @@ def test_grouped_query_paged_equals_contiguous():
     run.step()
     paged.step()
     torch.cuda.synchronize()
-    assert torch.equal(run.out, paged.out)
+    a, b = run.out.double(), paged.out.double()
+    rel = ((a - b).norm() / a.norm()).item()
+    assert rel < 1e-6, rel
+    assert (a - b).abs().max().item() < 1e-5
 
 
 @pytest.mark.parametrize("hq", [2, 8])
