@@ -315,6 +315,29 @@ def capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode):
         b *= 2
 
 
+def pages_sweep(args, torch, rq, WORKLOADS, RQDecode):
+    """The configured shapes on a contiguous cache and in paged pools of the
+    given block sizes (blocks in random pool order): step time, dominant call
+    and pool bytes, one JSON line per cache."""
+    base = WORKLOADS[args.config]
+    for pt in [0] + [int(x) for x in args.pages.split(",") if x]:
+        w = base.with_(page_tokens=pt, name=f"{base.name}_pages{pt}" if pt else base.name)
+        run = RQDecode(w)
+        run.step()
+        g = graphed(run.step, torch)
+        for _ in range(args.warmup):
+            g.replay()
+        ms, _ = time_steps(g.replay, args.steps, torch)
+        roof = dominant_roofline(run, args.steps, torch, True)
+        rec = {"sweep": "pages", "workload": base.name, "block_tokens": pt or None,
+               "ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+               "dominant_call_us": roof["avg_launch_us"], "kernel": roof["kernel"],
+               "pool_gb": round(rq.cache_bytes(run.desc) / 1e9, 3)}
+        print(json.dumps(rec), flush=True)
+        del g, run
+        torch.cuda.empty_cache()
+
+
 def measure_variant(w, keep, args, torch, rq, RQDecode):
     """Cache size, step bytes and throughput of one workload's packed cache, the
     relative L2 error of its K and V reconstructions (first 128 tokens) against
@@ -478,6 +501,10 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="batch-capacity sweep (batch 1, 2, 4, ... while caches fit) instead of the "
                          "single benchmark line")
+    ap.add_argument("--pages", default="",
+                    help="comma-separated paged block sizes: time the configured shapes on a "
+                         "contiguous cache and in pools of these blocks (JSON lines) instead of "
+                         "the single benchmark line")
     ap.add_argument("--variants", action="store_true",
                     help="accuracy and cost of the method's variants on the configured shapes "
                          "(one JSON line per variant) instead of the single benchmark line")
@@ -518,6 +545,9 @@ def main():
         return
     if args.sweep:
         capacity_sweep(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
+        return
+    if args.pages:
+        pages_sweep(args, torch, rq, WORKLOADS, RQDecode)
         return
     if args.variants:
         variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
