@@ -717,6 +717,19 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     if (knext < n_tot) wait_vm<ST::N_DMA>();
     else wait_vm<0>();
     const lds_u8* st = ring + (it & 1) * ST::BYTES;
+    if constexpr (NWK == 4) {
+      // Four-wave workgroups share a CU with two or three others, and the
+      // oldest waves win issue arbitration: with equal priorities the first
+      // workgroup on a CU finished its split early and the last ran on alone
+      // at a third of the CU's waves (Huginn-like shapes: loop times 17-40 us
+      // for equal splits).  A wave's issue priority follows the share of
+      // its split still unclaimed, so workgroups that lag catch up.
+      const int left4 = 4 * (n_tot - kcur);
+      if (left4 > 3 * n_tot) __builtin_amdgcn_s_setprio(3);
+      else if (left4 > 2 * n_tot) __builtin_amdgcn_s_setprio(2);
+      else if (left4 > n_tot) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     const int tt = t_begin + kcur * TPW + t0;
     const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
 
