@@ -14,7 +14,7 @@
 //   one workgroup per (batch * q_heads row, split), NWK = 4 or 8 waves per workgroup (8 for
 //   d = 128 calls reading at most one residual plane, paged anchor calls
 //   aside: decode_waves).  A wave takes its
-//   tokens in PAIRS (t, t+1); LPP lanes share a pair and each owns one
+//   tokens in PAIRS (t, t + TPW/2 of its tile); LPP lanes share a pair and each owns one
 //   quantization group (16 head_dim elements) of both tokens, so a lane's
 //   accumulators cover just 16 elements.
 //   Codes are never converted element by element: one v_and_or_b32 drops two
@@ -181,15 +181,39 @@ struct Stage {
 // past the piece, and in a partial tile lanes past `valid` (the bytes of the
 // in-range tokens), re-read the last granule in range, so nothing outside the
 // range is read and every staged value stays finite.
-template <int BYTES, int ROW, bool FULL>
+// Key code planes read by the matrix-core logits at head_dim 128 land
+// swizzled inside each token row, so that those reads hit distinct LDS banks:
+// lane (token n, block kb) reads 16 bytes (4-bit codes) or 8 bytes (2-bit) of
+// row n, and the sixteen rows of a read are 64 or 32 bytes apart, which put
+// rows n and n + 4 (n + 8) on the same banks.  Row t's chunk c (16 or 8
+// bytes) is stored at chunk (c + rot(t)) mod 4, rot(t) = t / 4 (4-bit rows of
+// 64 bytes) or 2 (t / 8) (2-bit rows of 32 bytes).  Only the DMA's per-lane
+// global offsets change: slot s of the staged tile takes the byte the
+// permutation sends there.
+template <int ROW>
+struct KSwz {
+  static constexpr int CH = ROW / 4;  // chunk bytes
+  __host__ __device__ static constexpr int rot(int t) { return ROW == 64 ? t / 4 : 2 * (t / 8); }
+  // byte offset, in the tile, of the global byte staged at tile byte `slot`
+  __host__ __device__ static constexpr int src(int slot) {
+    return (slot / ROW) * ROW + (((slot % ROW) / CH - rot(slot / ROW)) & 3) * CH + slot % CH;
+  }
+  // tile byte where chunk c of row t is staged
+  __host__ __device__ static constexpr int dst(int t, int c) { return t * ROW + ((c + rot(t)) & 3) * CH; }
+};
+
+template <int BYTES, int ROW, bool FULL, bool SWZ = false>
 __device__ __forceinline__ void dma_piece(rsrc_t r, uint32_t so, int valid, lds_u8* dst, int lane) {
   constexpr int G = gran_of(BYTES, ROW), STEP = 64 * G, N = span_of(BYTES, ROW) / STEP;
+  static_assert(!SWZ || ((ROW == 64 && G == 16) || (ROW == 32 && G == 4)) && BYTES % STEP == 0,
+                "swizzled planes: whole rows per instruction, granules inside one chunk");
 #pragma unroll
   for (int c = 0; c < N; ++c) {
-    const int o = c * STEP + lane * G;
+    const int s = c * STEP + lane * G;                // staged byte of this lane
+    const int o = SWZ ? KSwz<ROW>::src(s) : s;        // tile byte it takes
     if constexpr (FULL) {
       // the c * STEP part rides in the scalar offset
-      const int vo = (c * STEP + STEP <= BYTES) ? lane * G : min(o, BYTES - G) - c * STEP;
+      const int vo = (SWZ || c * STEP + STEP <= BYTES) ? o - c * STEP : min(o, BYTES - G) - c * STEP;
       dma1<G, true>(r, dst + c * STEP, vo, so + c * STEP);
     } else {
       dma1<G, true>(r, dst + c * STEP, min(o, valid - G), so);
@@ -267,11 +291,10 @@ __device__ __forceinline__ h8 kslab(const uint32_t* c, uint32_t magic) {
 }
 
 // The lane's code dwords of one plane of token n: 16 bytes (4-bit codes) or
-// 8 bytes (2-bit codes), block kb of the token's row.
+// 8 bytes (2-bit codes), block kb of the token's row, staged at p.
 template <int BITS>
-__device__ __forceinline__ void kcodes(const lds_u8* row, int kb, uint32_t* c) {
-  constexpr int W = BITS;  // dwords per lane at head_dim 128: 4 or 2
-  const lds_u8* p = row + kb * 4 * W;
+__device__ __forceinline__ void kcodes(const lds_u8* p, uint32_t* c) {
+  constexpr int W = BITS;  // dwords per lane: 4 or 2
   if constexpr (W == 4) {
     typedef __attribute__((address_space(3))) const u32x4 l4;
     const u32x4 v = *reinterpret_cast<l4*>(p);
@@ -382,6 +405,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   // slab of lane block 3 reads the next bytes of the staged tile (finite
   // codes that meet only zero query entries)
   constexpr bool KM = (D == 128 || D == 96) && NR == 1;
+  constexpr bool SWK = KM && D == 128;   // key code planes staged swizzled (KSwz)
   const Geometry& g = a.g;
 
   using ST = Stage<D, B1, B2, NR>;
@@ -512,7 +536,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   uint32_t claimed = 0;             // lane 0: the tile claimed for the one after
   auto issue_t = [&](auto full, uint32_t tb, lds_u8* st, int vt) __attribute__((always_inline)) {
     constexpr bool F = decltype(full)::value;
-    dma_piece<ST::C1, ST::R1, F>(rk1, po1 + tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
+    dma_piece<ST::C1, ST::R1, F, SWK>(rk1, po1 + tb * ST::R1, vt * ST::R1, st + ST::k1c, lane);
     dma_piece<ST::SZ, ST::RS, F>(rk1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::k1s, lane);
     dma_piece<ST::C1, ST::R1, F>(rv1, po1 + tb * ST::R1, vt * ST::R1, st + ST::v1c, lane);
     dma_piece<ST::SZ, ST::RS, F>(rv1, s1rel + tb * ST::RS, vt * ST::RS, st + ST::v1s, lane);
@@ -521,7 +545,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         lds_u8* rs = st + ST::res(r);
-        dma_piece<ST::C2, ST::R2, F>(rk2[r], po2[r] + tb * ST::R2, vt * ST::R2, rs + ST::k2c, lane);
+        dma_piece<ST::C2, ST::R2, F, SWK>(rk2[r], po2[r] + tb * ST::R2, vt * ST::R2, rs + ST::k2c,
+                                          lane);
         dma_piece<ST::SZ, ST::RS, F>(rk2[r], po2[r] + s2rel + tb * ST::RS, vt * ST::RS, rs + ST::k2s,
                                      lane);
         dma_piece<ST::C2, ST::R2, F>(rv2[r], po2[r] + tb * ST::R2, vt * ST::R2, rs + ST::v2c, lane);
@@ -657,6 +682,9 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   // anchor, residual high part, residual low part) and, for the lane's rows,
   // the groups' magic constants and plain query sums
   const int kn = lane & 15, kb = lane >> 4;
+  // where the lane's code chunks sit in a staged tile (swizzled at d = 128)
+  const int kofs1 = SWK ? KSwz<ST::R1>::dst(kn, kb) : kn * ST::R1 + kb * 4 * B1;
+  const int kofs2 = SWK ? KSwz<ST::R2>::dst(kn, kb) : kn * ST::R2 + kb * 4 * B2E;
   h8 Aq[4], Auh[4], Aul[4];
   float koff[4], ksum[4];
   const bool kres = TWO && kb >= 2;   // lane's rows are residual rows
@@ -694,8 +722,12 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
   float WA = 0.f, WR = 0.f, zA = 0.f, zR = 0.f;  // fp16 weight sums, offset sums
   float m = kEmpty, l = 0.f;
 
-  // lane-constant LDS offsets inside a tile buffer (token 2 pj of the tile)
-  const int t0 = 2 * pj;
+  // lane-constant LDS offsets inside a tile buffer: the lane's tokens are
+  // pj and pj + TS of the tile.  (Tokens 2 pj and 2 pj + 1 put the rows read
+  // by one half-wave 2 rows apart, so rows 4 apart met in the same LDS banks;
+  // with pj the rows read together are consecutive.)
+  constexpr int TS = LY::PAIRS;
+  const int t0 = pj;
   const int o1c = t0 * ST::R1 + eg * CB1, o2c = t0 * ST::R2 + eg * CB2;
   const int osz = t0 * ST::RS + eg * 2, oal = t0 * 4;
 
@@ -731,7 +763,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       else __builtin_amdgcn_s_setprio(0);
     }
     const int tt = t_begin + kcur * TPW + t0;
-    const bool ok0 = tt < t_end, ok1 = tt + 1 < t_end;
+    const bool ok0 = tt < t_end, ok1 = tt + TS < t_end;
 
     float lg0, lg1;
     if constexpr (KM) {
@@ -742,13 +774,13 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       // 2-bit planes), and that op's sums came out wrong
       f4 dk = {0.f, 0.f, 0.f, 0.f};
       uint32_t c1[B1];
-      kcodes<B1>(st + ST::k1c + kn * ST::R1, kb, c1);
+      kcodes<B1>(st + ST::k1c + kofs1, c1);
       h8 kb1[4], kb2[4];
       static_for<4>([&](auto J) { kb1[decltype(J)::value] = kslab<B1, decltype(J)::value>(c1, magic); });
       const lds_u8* rs = st + ST::res(0);
       if constexpr (TWO) {
         uint32_t c2[B2E];
-        kcodes<B2E>(rs + ST::k2c + kn * ST::R2, kb, c2);
+        kcodes<B2E>(rs + ST::k2c + kofs2, c2);
         static_for<4>([&](auto J) { kb2[decltype(J)::value] = kslab<B2E, decltype(J)::value>(c2, magic); });
       }
       static_for<4>([&](auto J) {
@@ -786,17 +818,17 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       kp = pair_add<32>(pair_add<16>(kp)) * qs;   // logit of token kn
       asm volatile("" :: "v"(kb1[0]), "v"(kb1[1]), "v"(kb1[2]), "v"(kb1[3]));
       if constexpr (TWO) asm volatile("" :: "v"(kb2[0]), "v"(kb2[1]), "v"(kb2[2]), "v"(kb2[3]));
-      // to the value side's layout: lane (pair pj, group e) takes tokens 2 pj, 2 pj + 1
+      // to the value side's layout: lane (pair pj, group e) takes tokens pj, pj + TS
       const int kbits = __builtin_bit_cast(int, kp);
-      const float lk0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(8 * pj, kbits));
-      const float lk1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(8 * pj + 4, kbits));
+      const float lk0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * t0, kbits));
+      const float lk1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (t0 + TS), kbits));
       lg0 = ok0 ? lk0 : kEmpty;
       lg1 = ok1 ? lk1 : kEmpty;
     } else {
       // keys now; the value planes are read after the softmax update, so their
       // registers are not live across the logit computation
       PairPlane<B1> k1;
-      lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, ST::R1, ST::RS);
+      lds_pair<B1>(k1, st + ST::k1c + o1c, st + ST::k1s + osz, TS * ST::R1, TS * ST::RS);
 
       // ---- logits of the pair
       asm volatile("" ::: "memory");  // keep the pair reads inside the loop
@@ -839,8 +871,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
         for (int r = 0; r < NR; ++r) {
           const lds_u8* rs = st + ST::res(r);
           PairPlane<B2E> k2;
-          lds_pair<B2E>(k2, rs + ST::k2c + o2c, rs + ST::k2s + osz, ST::R2, ST::RS);
-          const uint32_t ka0 = lds_u16(rs + ST::ka + oal), ka1 = lds_u16(rs + ST::ka + oal + 4);
+          lds_pair<B2E>(k2, rs + ST::k2c + o2c, rs + ST::k2s + osz, TS * ST::R2, TS * ST::RS);
+          const uint32_t ka0 = lds_u16(rs + ST::ka + oal), ka1 = lds_u16(rs + ST::ka + oal + 4 * TS);
           f2 s0 = sz_pair(k2.sz0), s1 = sz_pair(k2.sz1);
           if (!active) s0 = s1 = (f2){0.f, 0.f};
           const float r0 = fmaf(s0.x * key_dot2<B2E>(k2.c0, uh, ul, magic), ipu, s0.y * usum);
@@ -876,7 +908,7 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
 
     // ---- values
     PairPlane<B1> v1;
-    lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, ST::R1, ST::RS);
+    lds_pair<B1>(v1, st + ST::v1c + o1c, st + ST::v1s + osz, TS * ST::R1, TS * ST::RS);
     {
       // first plane: fp16 high + low weights, so the weights are exact to ~2^-22
       f2 s0 = sz_pair(v1.sz0), s1 = sz_pair(v1.sz1);
@@ -898,8 +930,8 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       for (int r = 0; r < NR; ++r) {
         const lds_u8* rs = st + ST::res(r);
         PairPlane<B2E> v2;
-        lds_pair<B2E>(v2, rs + ST::v2c + o2c, rs + ST::v2s + osz, ST::R2, ST::RS);
-        const uint32_t va0 = lds_u16(rs + ST::va + oal), va1 = lds_u16(rs + ST::va + oal + 4);
+        lds_pair<B2E>(v2, rs + ST::v2c + o2c, rs + ST::v2s + osz, TS * ST::R2, TS * ST::RS);
+        const uint32_t va0 = lds_u16(rs + ST::va + oal), va1 = lds_u16(rs + ST::va + oal + 4 * TS);
         f2 s0 = sz_pair(v2.sz0), s1 = sz_pair(v2.sz1);
         if (!active) s0 = s1 = (f2){0.f, 0.f};
         const float pa0 = p0 * bf16_to_f32(va0), pa1 = p1 * bf16_to_f32(va1);
