@@ -339,6 +339,22 @@ def pages_sweep(args, torch, rq, WORKLOADS, RQDecode):
         torch.cuda.empty_cache()
 
 
+def launch_gap(args, torch):
+    """Per-launch time of 72 back-to-back trivial kernels (one 256 x 512
+    element add each) replayed from a HIP graph: the floor that the graph's
+    launch sequencing puts under every decode call's event-timed duration."""
+    y = torch.zeros(256 * 512, device="cuda")
+
+    def once():
+        for _ in range(72):
+            y.add_(1.0)
+    g = graphed(once, torch)
+    for _ in range(args.warmup):
+        g.replay()
+    ms, _ = time_steps(g.replay, args.steps, torch)
+    print(json.dumps({"launch_gap_us": round(ms * 1e3 / 72, 3), "launches": 72 * args.steps}), flush=True)
+
+
 def measure_variant(w, keep, args, torch, rq, RQDecode):
     """Cache size, step bytes and throughput of one workload's packed cache, the
     relative L2 error of its K and V reconstructions (first 128 tokens) against
@@ -506,6 +522,9 @@ def main():
                     help="comma-separated paged block sizes: time the configured shapes on a "
                          "contiguous cache and in pools of these blocks (JSON lines) instead of "
                          "the single benchmark line")
+    ap.add_argument("--launch-gap", action="store_true",
+                    help="only time back-to-back trivial kernels replayed from a HIP graph "
+                         "(the per-launch floor under every event-timed call)")
     ap.add_argument("--variants", action="store_true",
                     help="accuracy and cost of the method's variants on the configured shapes "
                          "(one JSON line per variant) instead of the single benchmark line")
@@ -549,6 +568,9 @@ def main():
         return
     if args.pages:
         pages_sweep(args, torch, rq, WORKLOADS, RQDecode)
+        return
+    if args.launch_gap:
+        launch_gap(args, torch)
         return
     if args.variants:
         variants_study(args, torch, rq, WORKLOADS, RQDecode, BF16Decode)
