@@ -510,7 +510,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
-    ap.add_argument("--also", default="ouro16k_b4",
+    ap.add_argument("--also", default="ouro16k_b4,huginn8k_b2",
                     help="comma-separated workloads whose dominant decode call is also timed "
                          "(roofline only; empty to skip)")
     ap.add_argument("--eager", action="store_true",
