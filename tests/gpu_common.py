@@ -77,8 +77,10 @@ def check_slice_planes(w, run, key, t0=0, n=None):
         gpu = decode_slice(run.cache, geom, kv, b, layer, head, n, t0)
 
         def dump(g, e, kv=kv, H=H):
-            os.makedirs("gpurun_out", exist_ok=True)
-            path = f"gpurun_out/mismatch_{w.name}_kv{kv}_{b}_{layer}_{head}.npz"
+            # inputs and both encodings of a mismatching slice, for offline study
+            out_dir = os.environ.get("RQ_MISMATCH_DIR", "mismatch_dumps")
+            os.makedirs(out_dir, exist_ok=True)
+            path = f"{out_dir}/mismatch_{w.name}_kv{kv}_{b}_{layer}_{head}.npz"
             np.savez_compressed(path, x=bits16(run.kept[key][kv]), H=H,
                                 gpu_codes=g.codes, gpu_s8=g.s8, gpu_z8=g.z8, gpu_alpha=g.alpha,
                                 o_codes=e.codes, o_s8=e.s8, o_z8=e.z8, o_alpha=e.alpha)
