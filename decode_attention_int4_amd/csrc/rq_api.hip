@@ -416,6 +416,12 @@ static rq_status decode_attention_impl(const rq_cache_desc* desc, const void* ca
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   int waves = 4;
   const rq::SplitPlan plan = decode_plan(desc, rows, loop, q_heads, n_tokens, pg.table != nullptr, &waves);
+  // workspace_for bounds every plan; a plan past it would write partials
+  // beyond the caller's buffer, so refuse rather than launch
+  const uint64_t used = plan.splits > 1 ? kCounterBytes + (uint64_t)rows * q_heads * plan.splits *
+                                                             (2 + 2 * desc->head_dim) * 4ull
+                                        : 0;
+  if (used > workspace_bytes) return RQ_ERR_WORKSPACE;
   rq::DecodeArgs a{};
   a.g = rq::make_geometry(*desc);
   a.cache = static_cast<const uint8_t*>(cache);
@@ -576,6 +582,8 @@ rq_status rq_bf16_decode_attention(const rq_cache_desc* desc, const uint16_t* k_
   if (workspace_bytes < need) return RQ_ERR_WORKSPACE;
   const int32_t bh = desc->batch * q_heads;
   const rq::SplitPlan plan = rq::plan_splits(bh, n_tokens, rq::bf16_tile_tokens(), rq::kBf16Target, false);
+  if (plan.splits > 1 && (uint64_t)bh * plan.splits * (2 + desc->head_dim) * 4ull > workspace_bytes)
+    return RQ_ERR_WORKSPACE;
   rq::Bf16DecodeArgs a{};
   a.batch = desc->batch;
   a.loops = desc->loops;
