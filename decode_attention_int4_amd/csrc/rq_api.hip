@@ -163,7 +163,9 @@ rq_status check_paged(const rq_cache_desc* pool, int32_t n_seqs, const int32_t* 
   const Geometry g = rq::make_geometry(*pool);
   if ((uint64_t)g.layers * g.layer_block >= (1ull << 32)) return RQ_ERR_UNSUPPORTED;
   if (n_seqs <= 0 || max_blocks <= 0 || !block_table) return RQ_ERR_INVALID_ARG;
-  if (((int64_t)max_blocks << sh) > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  // at most 2^30 tokens per sequence, so token counts rounded up to whole
+  // tiles and splits stay far inside int32
+  if (((int64_t)max_blocks << sh) > (int64_t)1 << 30) return RQ_ERR_UNSUPPORTED;
   if (!aligned(block_table, 4)) return RQ_ERR_ALIGNMENT;
   pg.table = block_table;
   pg.max_blocks = max_blocks;

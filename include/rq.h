@@ -321,7 +321,8 @@ rq_status rq_decode_attention_ragged(const rq_cache_desc* desc, const void* cach
  * logical tokens.
  *   block_table  device int32 [n_seqs][max_blocks_per_seq], 4-byte aligned,
  *                read on the device.  Capacity per sequence is
- *                max_blocks_per_seq * block_tokens (at most 2^31 - 1).
+ *                max_blocks_per_seq * block_tokens (at most 2^30; larger
+ *                tables return RQ_ERR_UNSUPPORTED).
  */
 
 /* Workspace for rq_paged_decode_attention: as rq_decode_workspace_bytes with

@@ -264,9 +264,11 @@ def test_paged_entry_points_reject_bad_arguments_before_launch():
     assert dec(table=ODD) == 5
     assert dec(max_n=257) == 3           # 8 blocks of 32 tokens
     assert dec(max_blocks=1 << 27) == 2  # capacity beyond 2^31 - 1 tokens
+    assert dec(max_blocks=(1 << 25) + 1) == 2  # 32-token blocks: 2^30 + 32 tokens
     need = rq.paged_decode_workspace_bytes(pool, 2, 3, 8192)
     assert need > 0
     assert dec(max_blocks=256, max_n=8192, wsb=need - 4) == 4
+    assert dec(max_blocks=1 << 25, max_n=8192, wsb=need - 4) == 4  # 2^30 tokens pass capacity
     assert dec(max_blocks=256, max_n=8192, wsb=need, work=None) == 1
     # the workspace is sized by the sequences, not by the pool's block count
     assert rq.paged_decode_workspace_bytes(pool, 2, 3, 8192) == \
