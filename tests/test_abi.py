@@ -315,6 +315,27 @@ def test_workspace_holds_one_round_of_splits():
     assert rq.decode_workspace_bytes(ouro, 16, 127) == 0
 
 
+def test_workspace_covers_every_split_plan():
+    """For every call a descriptor admits, the workspace bound holds the
+    partial states of the split plan the call runs (the entry points refuse
+    a plan past it rather than write beyond the buffer)."""
+    counters = (1 << 16) * 4
+    for d in (64, 96, 128):
+        for batch, kvh, ratio in ((1, 1, 1), (1, 4, 1), (2, 55, 1), (3, 16, 1), (4, 16, 1),
+                                  (16, 4, 4), (1, 2, 8), (9, 7, 2), (64, 16, 1)):
+            for mode in (rq.MODE_RESIDUAL, rq.MODE_DIRECT, rq.MODE_CHAINED):
+                desc = rq.make_desc(batch, 4, 1, kvh, 65536, d, mode=mode)
+                hq = kvh * ratio
+                for n in (0, 1, 100, 257, 1000, 4097, 8192, 30000, 65536):
+                    ws = rq.decode_workspace_bytes(desc, hq, n)
+                    for loop in range(4):
+                        s = rq.decode_splits(desc, loop, hq, n)
+                        assert s >= 1
+                        if s > 1:
+                            assert ws >= counters + batch * hq * s * (2 + 2 * d) * 4, \
+                                (d, batch, kvh, ratio, mode, n, loop, s, ws)
+
+
 def test_split_plan_fits_one_round():
     """The split count the library reports for a call (the largest of any
     row): eight-wave calls (d = 128, at most one residual plane, paged anchors
