@@ -193,7 +193,7 @@ def read_peak(torch, rq, call_bytes: int, nbytes=8 << 30, reps=5):
 
 def cpu_threads():
     """Host cores this process may run on, and the threads the oracle uses:
-    all of them, up to 16 (the CPU share a one-GPU machine gives a job)."""
+    all of them, up to 16 (the host share of a one-GPU machine)."""
     try:
         usable = len(os.sched_getaffinity(0))
     except AttributeError:
