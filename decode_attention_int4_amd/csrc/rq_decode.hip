@@ -20,19 +20,25 @@
 //   Codes are never converted element by element: one v_and_or_b32 drops two
 //   codes into the mantissas of an fp16 pair whose exponent encodes 1024 (the
 //   "magic number" conversion), giving 1024 + m*c.
-//   * Keys: the pair holds two elements of ONE token and meets
-//     (q_a, q_b)/m in v_dot2_f32_f16; the constant 1024*sum(q)/m is
-//     subtracted once per group.  The query is exact in fp16 after a
-//     power-of-two prescale (BF16 fits fp16's mantissa); H q is not, so it is
-//     split into fp16 high and low parts and each meets the codes in a dot2.
+//   * Keys at d = 128 and 96 (at most one residual plane): one
+//     v_mfma_f32_16x16x32_f16 chain per 16-token tile, the codes in
+//     magic-number form against a block-diagonal query operand (one row per
+//     group and plane), so the code-times-query sums leave the VALU.
+//     Elsewhere (d = 64, chained loops) the pair holds two elements of ONE
+//     token and meets (q_a, q_b)/m in v_dot2_f32_f16.  Either way the
+//     constant 1024*sum(q)/m is subtracted once per group.  The query is
+//     exact in fp16 after a power-of-two prescale (BF16 fits fp16's
+//     mantissa); H q is not, so it is split into fp16 high and low parts and
+//     each meets the codes.
 //   * Values: v_perm_b32 first interleaves the same 16-bit unit of the two
 //     tokens, so the pair holds ONE element of BOTH tokens and meets the fp16
 //     weight pair (p_t s_t, p_t' s_t') in v_dot2_f32_f16 -- one instruction
 //     per two multiply-adds.  The first plane's weights go in as an fp16 high
 //     and low part (two dot2s); the residual plane, a smaller term, uses one
 //     fp16 weight against codes centred on the middle code.  The magic
-//     constant is taken out per lane at the end from the running sum of the
-//     fp16 weights.
+//     constant is folded out of a lane's sums every eight tiles (and at the
+//     end) from the running sum of the fp16 weights, so the fp32 rounding of
+//     the code term does not grow with the context.
 //   FP8 scale/offset bytes are decoded by v_cvt_pk_f32_fp8 (OCP e4m3fn on
 //   gfx950).  Each wave streams its tiles through a private ring in LDS filled
 //   by buffer_load ... lds DMA with scalar offsets, so issuing a tile costs no
