@@ -28,10 +28,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 PROFILES = os.path.join(ROOT, "profiles")
-# the sources the dominant kernel's code and launch depend on
+# the sources the dominant kernel's code and launch depend on, and the build
+# script that sets its compiler flags
 DECODE_SRCS = [os.path.join(ROOT, "decode_attention_int4_amd", "csrc", f)
                for f in ("rq_decode.hip", "rq_stage.h", "rq_api.hip", "rq_layout.h", "rq_kernels.h",
-                         "rq_device.h")]
+                         "rq_device.h")] + [os.path.join(ROOT, "decode_attention_int4_amd", "build.py")]
 
 
 def log(*a):

@@ -40,6 +40,12 @@ ARCH = os.environ.get("RQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # one-lane atomics stay single instructions.  The compiler's
+    # wave-aggregating rewrite of an atomic (ballot, bit count, then a
+    # read-first-lane of the result) waits for the result right after the
+    # atomic; the decode kernels' tile claims (an LDS counter, one lane) are
+    # read an iteration later, so the plain atomic hides its latency
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
@@ -84,6 +90,7 @@ def is_stale() -> bool:
     t = os.path.getmtime(LIB)
     srcs = [os.path.join(CSRC, s) for s in SOURCES + HEADERS]
     srcs.append(os.path.join(os.path.dirname(PKG), "include", "rq.h"))
+    srcs.append(os.path.abspath(__file__))   # compiler flags
     return any(os.path.getmtime(s) > t for s in srcs)
 
 
