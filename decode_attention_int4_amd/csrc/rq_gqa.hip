@@ -311,10 +311,9 @@ template <int BITS>
 __device__ __forceinline__ f4 v_unshift() {
   return BITS == 4 ? (f4){1.f, 1.f / 16.f, 1.f, 1.f / 16.f} : (f4){1.f, 1.f / 4.f, 1.f / 16.f, 1.f / 64.f};
 }
+// (plain C, selected as one v_and_or_b32 with the mask in a VGPR; see and_or)
 __device__ __forceinline__ uint32_t and_or_v(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
-  return r;
+  return (x & mask) | magic;
 }
 
 // V-side A operand for group g: element e (lane row) of tokens 4c..4c+3,

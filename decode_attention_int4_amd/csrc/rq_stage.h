@@ -28,11 +28,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef u32x4 rsrc_t;
 
 // fp16 pair of two codes: v_and_or_b32 keeps the masked code bits and ORs in
-// the exponent of 1024, so each half reads 1024 + 2^p * code.
+// the exponent of 1024, so each half reads 1024 + 2^p * code.  Plain C, which
+// the compiler selects as that one instruction: as inline asm its writes were
+// invisible to the compiler's hazard checks, so a code operand rebuilt right
+// after the matrix op reading it could change under that op, and every use
+// paid a conservative wait state.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return r;
+  return (x & mask) | magic;
 }
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
