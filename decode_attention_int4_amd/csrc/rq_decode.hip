@@ -774,10 +774,6 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
     float lg0, lg1;
     if constexpr (KM) {
       // ---- logits on matrix cores: D[group row][token] for the 16 tokens
-      // Every code operand gets registers of its own that stay live until the
-      // logits are formed: with operands rebuilt in place, a register was
-      // rewritten one instruction after the matrix op reading it (head_dim 96,
-      // 2-bit planes), and that op's sums came out wrong
       f4 dk = {0.f, 0.f, 0.f, 0.f};
       uint32_t c1[B1];
       kcodes<B1>(st + ST::k1c + kofs1, c1);
@@ -822,8 +818,6 @@ __global__ void __launch_bounds__(NWK * 64, NWK == 8 ? 2 : 3) decode_kernel(Deco
       if constexpr (TWO) kmul = kres ? ipu * bf16_to_f32(lds_u16(rs + ST::ka + 4 * kn)) : ipq;
       kp = (TWO || kb < 2) ? kp * kmul : 0.f;
       kp = pair_add<32>(pair_add<16>(kp)) * qs;   // logit of token kn
-      asm volatile("" :: "v"(kb1[0]), "v"(kb1[1]), "v"(kb1[2]), "v"(kb1[3]));
-      if constexpr (TWO) asm volatile("" :: "v"(kb2[0]), "v"(kb2[1]), "v"(kb2[2]), "v"(kb2[3]));
       // to the value side's layout: lane (pair pj, group e) takes tokens pj, pj + TS
       const int kbits = __builtin_bit_cast(int, kp);
       const float lk0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * t0, kbits));
