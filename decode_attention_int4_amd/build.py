@@ -4,9 +4,7 @@
     python -m decode_attention_int4_amd.build --sanitize
 
 Each translation unit is compiled separately (in parallel) and linked with
-hipcc.  Packed-FP32 instruction selection is disabled for all device code,
-one-lane atomics are left as single instructions, and the decode sources are
-scheduled by LLVM's iterative ILP scheduler (see FLAGS and SOURCE_FLAGS).
+hipcc.  Packed-FP32 instruction selection is disabled for all device code.
 
 --sanitize builds librq_san.so instead: the host side (argument checking,
 layout arithmetic, launch setup) under AddressSanitizer and
